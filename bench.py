@@ -1,0 +1,231 @@
+"""Throughput of the WKV7 forward + backward on one MI355X.
+
+One step = the whole hot path over one batch: wkv7_fwd (y, checkpoints, final
+state), then the backward (state-gradient pass, then the per-token input
+gradients) for a loss gradient dy.  Inputs are seeded synthetic tensors of the
+workload's shape, resident in HBM before timing starts.
+
+Prints one JSON line.  Default workload: B12 T1024 H6 D64, bf16 inputs
+(the 36M "debug" training layer).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "WKV7 fwd+bwd tokens/s and % HBM peak, B12 T1024 H6 D64 (1 MI355X)"
+HBM_PEAK_GBS = 8000.0
+D = 64
+CSRC = os.path.join(ROOT, "linear_rnn_lm_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_bytes(wl, in_bytes: int) -> dict:
+    """Bytes each kernel must move per launch (inputs read once, outputs
+    written once); see the design doc for the per-head-token figures."""
+    ht = wl.B * wl.T * wl.H          # head-tokens
+    heads = wl.B * wl.H
+    nc = (wl.T + 31) // 32
+    tok_in = ht * D * in_bytes
+    tok32 = ht * D * 4
+    st = heads * D * D * 4
+    ck = heads * nc * D * D * 4
+    h0 = st if wl.with_h0 else 0
+    return {
+        "fwd": 6 * tok_in + tok32 + ck + h0 + st,
+        "bwd_state": 5 * tok_in + tok32 + tok32 + ck + st,
+        "bwd_inputs": 6 * tok_in + tok32 + 2 * ck + 5 * tok32,
+        # whole path, algorithmic: fwd 1536 B and bwd 3072 B per head-token (bf16 inputs)
+        "path": (6 * tok_in + tok32 + ck + h0 + st) + (6 * tok_in + tok32 + ck + 6 * tok32 + st),
+    }
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The oracle, as it stands, on the host cores: whole fwd+bwd passes of the
+    workload (a subset of heads if one pass would exceed the budget)."""
+    import oracle
+    from linear_rnn_lm_amd.inputs import make_inputs
+    threads = min(oracle.default_threads(), 16)
+    # probe with a few heads to size the sample
+    probe_heads = min(wl.heads, threads)
+    xb = make_inputs(1, wl.T, probe_heads, wl.dtype, seed=wl.seed, with_h0=wl.with_h0)
+    t0 = time.perf_counter()
+    oracle.fwd(*xb.tensors(), xb.h0, threads=threads)
+    oracle.bwd(*xb.tensors(), xb.dy, xb.h0, None, threads=threads)
+    per_head = (time.perf_counter() - t0) / probe_heads
+    heads = max(probe_heads, min(wl.heads, int(budget_s / max(per_head, 1e-9))))
+    B = max(1, heads // wl.H) if heads >= wl.H else 1
+    H = wl.H if heads >= wl.H else heads
+    x = make_inputs(B, wl.T, H, wl.dtype, seed=wl.seed, with_h0=wl.with_h0)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.fwd(*x.tensors(), x.h0, threads=threads)
+        oracle.bwd(*x.tensors(), x.dy, x.h0, None, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s * 0.5 or reps >= 1000:
+            break
+    tokens = B * wl.T * reps * (H / wl.H)    # tokens of the full-width layer
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd on B{B} T{wl.T} H{H} ({B * H} of {wl.heads} heads), "
+                      f"{reps} pass(es) in {el:.1f} s; tokens scaled by {H}/{wl.H} heads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="debug_36m")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported. "
+              "The WKV7 op shards over heads with no exchange, so N GPUs each run this same "
+              "single-GPU step on their share.", file=sys.stderr)
+        return 2
+
+    import torch
+    import linear_rnn_lm_amd as L
+    from linear_rnn_lm_amd.inputs import WORKLOADS, workload_inputs
+
+    wl = WORKLOADS[args.workload]
+    if wl.T == 1:
+        print("bench.py: the one-token recurrent-step workload is measured by its own benchmark "
+              "(forward only); pick a training workload", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = workload_inputs(wl)
+    ins = [t.to(dev) for t in x.tensors()]
+    h0 = None if x.h0 is None else x.h0.to(dev)
+    dy = x.dy.to(dev)
+    B, T, H = wl.B, wl.T, wl.H
+    nc = L.num_chunks(T)
+    f32 = dict(device=dev, dtype=torch.float32)
+    y = torch.empty(B, T, H, D, **f32)
+    ck = torch.empty(B, H, nc, D, D, **f32)
+    hT = torch.empty(B, H, D, D, **f32)
+    dck = torch.empty(B, H, nc, D, D, **f32)
+    dv = torch.empty(B, T, H, D, **f32)
+    dh0 = torch.empty(B, H, D, D, **f32)
+    grads = [torch.empty(B, T, H, D, **f32) for _ in range(5)]
+    lib = L.lib()
+    code = 1 if wl.dtype == torch.bfloat16 else 0
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    p = [t.data_ptr() for t in ins]
+    ph0 = None if h0 is None else h0.data_ptr()
+
+    def k_fwd():
+        st = lib.wkv7_fwd(B, T, H, D, code, *p, ph0, y.data_ptr(), ck.data_ptr(), hT.data_ptr(), sh)
+        assert st == 0, lib.wkv7_status_str(st)
+
+    def k_state():
+        st = lib.wkv7_bwd_state(B, T, H, D, code, dy.data_ptr(), None, p[0], p[1], p[2], p[4], p[5],
+                                dck.data_ptr(), dv.data_ptr(), dh0.data_ptr(), sh)
+        assert st == 0, lib.wkv7_status_str(st)
+
+    def k_inputs():
+        st = lib.wkv7_bwd_inputs(B, T, H, D, code, dy.data_ptr(), None, *p, ck.data_ptr(), dck.data_ptr(),
+                                 *[g.data_ptr() for g in grads], sh)
+        assert st == 0, lib.wkv7_status_str(st)
+
+    kernels = [("fwd", k_fwd), ("bwd_state", k_state), ("bwd_inputs", k_inputs)]
+
+    def step():
+        for _, fn in kernels:
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps between two events on the launch stream
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel durations: events between the launches of every step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        for i, (_, fn) in enumerate(kernels):
+            fn()
+            evs[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_kernel_ms = {name: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
+                     for i, (name, _) in enumerate(kernels)}
+
+    in_bytes = 2 if wl.dtype == torch.bfloat16 else 4
+    kb = kernel_bytes(wl, in_bytes)
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
+    achieved = kb[dom] / (per_kernel_ms[dom] * 1e-3) / 1e9
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(args.workload, {}).get(dom)
+        if ent and ent.get("source_digest") == source_digest():
+            traffic = ent["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+
+    tokens = B * T
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: WKV7 fwd+bwd {wl.description}, chunk 32",
+                   "B": B, "T": T, "H": H, "D": D,
+                   "in_dtype": "bf16" if in_bytes == 2 else "f32", "state_dtype": "f32"},
+        "fwd_tokens_per_s": tokens / (per_kernel_ms["fwd"] * 1e-3),
+        "kernel_ms": per_kernel_ms,
+        "path_hbm": {"algorithmic_bytes": kb["path"],
+                     "achieved_GBs": kb["path"] / (ms_per_step * 1e-3) / 1e9,
+                     "frac_of_peak": kb["path"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,194 @@
+/*
+ * wkv7.h -- C ABI of libwkv7: the RWKV-7 WKV7 time-mix recurrence, forward
+ * and backward, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (rwkv-mlx page, section "Metal kernel architecture",
+ * forward block, in its per-element reading): every head (b, h) carries a
+ * D x D fp32 state S, rows i paired with v and y, columns j paired with r, w,
+ * k, a and b.  Per token t:
+ *
+ *     sa[i]   = sum_j S[i][j] a_t[j]                 (state before the update)
+ *     S[i][j] = w_t[j] S[i][j] + v_t[i] k_t[j] + sa[i] b_t[j]
+ *     y_t[i]  = sum_j S[i][j] r_t[j]                 (state after the update)
+ *
+ * The backward walks the sequence in reverse from per-chunk state
+ * checkpoints (same section, backward block, and the paragraph after it on
+ * why checkpoints are kept every 32 tokens).  Unlike the page's design, this
+ * library never reconstructs an earlier state by dividing by w: it re-runs
+ * each chunk forward from its checkpoint.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - D must be 64.  B, T, H must be >= 1.  CHUNK = 32; NC = ceil(T / 32).
+ * - Token tensors (r, w, k, v, a, b, y, dy and the six input gradients) are
+ *   dense row-major (B, T, H, D): element (b,t,h,d) at ((b*T + t)*H + h)*D + d.
+ * - State tensors (h0, hT, dhT, dh0) are dense row-major (B, H, D, D) with
+ *   S[i][j] at i*D + j.  Checkpoints are (B, H, NC, D, D); checkpoint c is the
+ *   state ENTERING chunk c, i.e. after 32*c tokens (checkpoint 0 is h0).
+ * - r, w, k, v, a, b share one storage type, `in_dtype` (fp32 or bf16).
+ *   Everything else is fp32.  All arithmetic is fp32 (fp32 accumulation;
+ *   with bf16 inputs the matrix-core products use a two-term bf16 split of
+ *   every fp32 operand, good to about 2^-17 relative per product).
+ * - Decay w must lie in [1/8, 1].  (RWKV-7's decay exp(-e^-0.5 * sigmoid(x))
+ *   lies in (0.545, 1).)  Within a chunk, running products of up to 32 decays
+ *   and their reciprocals are used as scale factors; at w >= 1/8 they stay
+ *   within 2^-96 .. 2^96.  Values outside the range are not detected and give
+ *   unspecified (possibly non-finite) results.  NaN/Inf inputs propagate.
+ * - Every pointer must be a device pointer (hipMalloc'd or equivalent) aligned
+ *   to 16 bytes.  Optional pointers may be NULL where stated.
+ * - The library allocates nothing, frees nothing and keeps no pointer after a
+ *   call returns.  It holds no mutable global state; calls on different
+ *   streams may run concurrently if their outputs do not overlap.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every entry point is
+ *   asynchronous: it only enqueues kernels and never synchronises.
+ * - Argument, shape, alignment, workspace and aliasing errors are detected on
+ *   the host BEFORE anything is enqueued; no output is touched then.  A
+ *   failed launch returns WKV7_ERR_HIP.  Faults during execution surface at
+ *   the caller's next synchronisation.
+ * - Outputs must not overlap each other or any input, except where an entry
+ *   point allows it explicitly (hT may equal h0).
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WKV7_OK = 0,
+    WKV7_ERR_ARG = 1,       /* NULL where a pointer is required, bad enum   */
+    WKV7_ERR_SHAPE = 2,     /* D != 64, B/T/H < 1, sizes overflowing int64  */
+    WKV7_ERR_DTYPE = 3,     /* in_dtype not a wkv7_dtype                    */
+    WKV7_ERR_ALIGN = 4,     /* a pointer not 16-byte aligned                */
+    WKV7_ERR_ALIAS = 5,     /* an output overlaps an input or another output */
+    WKV7_ERR_HIP = 6,       /* kernel launch failed                         */
+    WKV7_ERR_WORKSPACE = 7  /* workspace NULL or smaller than required      */
+} wkv7_status;
+
+typedef enum {
+    WKV7_F32 = 0,
+    WKV7_BF16 = 1
+} wkv7_dtype;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int wkv7_version(void);
+
+/* Chunk length used for checkpoints (32). */
+int wkv7_chunk_len(void);
+
+/* NC = ceil(T / 32) for T >= 1; 0 for T < 1. */
+int64_t wkv7_num_chunks(int64_t T);
+
+/* Static string naming a status code (never NULL). */
+const char *wkv7_status_str(int status);
+
+/* Bytes of device workspace wkv7_bwd needs: B*H*NC*D*D*4 (one fp32 state
+ * gradient per chunk boundary).  0 for invalid shapes. */
+size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int D);
+
+/*
+ * Forward (rwkv-mlx page, "Metal kernel architecture", forward block).
+ *
+ *   r, w, k, v, a, b : (B,T,H,D), in_dtype, required.
+ *   h0               : (B,H,D,D) fp32 initial state, or NULL for zero.
+ *   y                : (B,T,H,D) fp32 output, or NULL if not wanted.
+ *   h_ckpt           : (B,H,NC,D,D) fp32 checkpoints, or NULL (inference:
+ *                      nothing kept for a backward).
+ *   hT               : (B,H,D,D) fp32 final state, or NULL.  hT may be the
+ *                      same pointer as h0 (state updated in place), but must
+ *                      not otherwise overlap h0.
+ * At least one of y, h_ckpt, hT must be non-NULL.
+ */
+wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                     const void *r, const void *w, const void *k,
+                     const void *v, const void *a, const void *b,
+                     const float *h0, float *y, float *h_ckpt, float *hT,
+                     void *stream);
+
+/*
+ * Backward (rwkv-mlx page, "Metal kernel architecture", backward block:
+ * chunks in reverse from the checkpoints, producing dr, dw, dk, dv, da, db).
+ *
+ *   dy               : (B,T,H,D) fp32 gradient of the loss w.r.t. y, required.
+ *   dhT              : (B,H,D,D) fp32 gradient w.r.t. the final state, or NULL
+ *                      for zero.
+ *   r..b             : the forward's inputs, in_dtype, required.
+ *   h_ckpt           : (B,H,NC,D,D) checkpoints written by wkv7_fwd for the
+ *                      same inputs and h0, required.
+ *   dr,dw,dk,dv,da,db: (B,T,H,D) fp32 outputs, required.
+ *   dh0              : (B,H,D,D) fp32 gradient w.r.t. h0, or NULL.
+ *   workspace        : device scratch of at least
+ *                      wkv7_bwd_workspace_bytes(B,T,H,D) bytes, required; its
+ *                      contents on entry do not matter and are clobbered.
+ * Equivalent to wkv7_bwd_state (with the workspace as dh_ckpt) followed by
+ * wkv7_bwd_inputs.
+ */
+wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                     const float *dy, const float *dhT,
+                     const void *r, const void *w, const void *k,
+                     const void *v, const void *a, const void *b,
+                     const float *h_ckpt,
+                     float *dr, float *dw, float *dk, float *dv,
+                     float *da, float *db, float *dh0,
+                     void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * Backward, first stage: the gradient of the loss w.r.t. the state at every
+ * chunk boundary, walking the chunks in reverse (rwkv-mlx page, "Metal kernel
+ * architecture", backward block).  Needs neither v nor the checkpoints: the
+ * state gradient obeys its own recurrence, driven by dy, r, w, a, b.
+ *
+ *   dy, dhT, r, w, k, a, b : as for wkv7_bwd.
+ *   dh_ckpt  : (B,H,NC,D,D) fp32 output, required: dh_ckpt[c] is the gradient
+ *              w.r.t. checkpoint c (the state entering chunk c).
+ *   dv       : (B,T,H,D) fp32 output (the gradient w.r.t. v), or NULL.
+ *   dh0      : (B,H,D,D) fp32 output (equals dh_ckpt[0]), or NULL.
+ */
+wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                           const float *dy, const float *dhT,
+                           const void *r, const void *w, const void *k,
+                           const void *a, const void *b,
+                           float *dh_ckpt, float *dv, float *dh0,
+                           void *stream);
+
+/*
+ * Backward, second stage: dr, dw, dk, da, db for every token, all chunks in
+ * parallel, each chunk recomputed forward from its checkpoint (never by
+ * dividing by w).
+ *
+ *   dy, dhT, r..b, h_ckpt : as for wkv7_bwd.
+ *   dh_ckpt  : (B,H,NC,D,D) written by wkv7_bwd_state for the same inputs.
+ *   dr, dw, dk, da, db : (B,T,H,D) fp32 outputs, required.
+ */
+wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                            const float *dy, const float *dhT,
+                            const void *r, const void *w, const void *k,
+                            const void *v, const void *a, const void *b,
+                            const float *h_ckpt, const float *dh_ckpt,
+                            float *dr, float *dw, float *dk, float *da, float *db,
+                            void *stream);
+
+/*
+ * Token-by-token forward (same definition as wkv7_fwd, same arguments and
+ * rules), evaluated one token after another on the vector units instead of
+ * in chunks on the matrix cores.  This is the path wkv7_fwd itself takes for
+ * very short sequences (the one-token recurrent step of RNN-mode inference,
+ * RWKV-LM README page, the pip-package usage that hands the state from call
+ * to call).  Exposed so that callers can pick it explicitly.
+ */
+wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                                const void *r, const void *w, const void *k,
+                                const void *v, const void *a, const void *b,
+                                const float *h0, float *y, float *h_ckpt, float *hT,
+                                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV7_H */

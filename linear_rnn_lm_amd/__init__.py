@@ -1,0 +1,234 @@
+"""linear_rnn_lm_amd -- the RWKV-7 WKV7 recurrence on AMD Instinct MI355X.
+
+Thin Python binding of ``libwkv7.so`` (C ABI in ``include/wkv7.h``).  It only
+marshals arguments: torch supplies device memory and the current HIP stream,
+every step of the computation runs in the library's HIP kernels.  There is no
+CPU fallback; if the library is missing, calls raise.
+
+    y, ckpt, hT = fwd(r, w, k, v, a, b, h0)            # (B,T,H,64) inputs
+    dr, dw, dk, dv, da, db, dh0 = bwd(dy, r, w, k, v, a, b, ckpt, dhT)
+    WKV7.apply(r, w, k, v, a, b, h0)                   # autograd op -> (y, hT)
+
+The recurrence (rwkv-mlx page, section "Metal kernel architecture"): per
+head a 64x64 fp32 state S; per token sa = S a, S = S diag(w) + v k^T + sa b^T,
+y = S r.  Inputs r, w, k, v, a, b are fp32 or bf16; all outputs are fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["lib", "fwd", "fwd_sequential", "bwd", "bwd_state", "bwd_inputs", "step", "WKV7", "Wkv7Error",
+           "num_chunks", "workspace_bytes", "CHUNK", "HEAD_SIZE"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwkv7.so")
+CHUNK = 32
+HEAD_SIZE = 64
+F32, BF16 = 0, 1
+
+_lib = None
+
+
+class Wkv7Error(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+def lib():
+    """Load libwkv7.so (built by ``python -m linear_rnn_lm_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m linear_rnn_lm_amd.build` "
+                               "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.wkv7_version.restype = i
+        L.wkv7_chunk_len.restype = i
+        L.wkv7_num_chunks.argtypes = [i64]
+        L.wkv7_num_chunks.restype = i64
+        L.wkv7_status_str.argtypes = [i]
+        L.wkv7_status_str.restype = ctypes.c_char_p
+        L.wkv7_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.wkv7_bwd_workspace_bytes.restype = sz
+        L.wkv7_fwd.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 4 + [vp]
+        L.wkv7_fwd.restype = i
+        L.wkv7_fwd_sequential.argtypes = L.wkv7_fwd.argtypes
+        L.wkv7_fwd_sequential.restype = i
+        L.wkv7_bwd.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] + [vp] * 7 + [vp, sz, vp]
+        L.wkv7_bwd.restype = i
+        L.wkv7_bwd_state.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 5 + [vp] * 3 + [vp]
+        L.wkv7_bwd_state.restype = i
+        L.wkv7_bwd_inputs.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] * 2 + [vp] * 5 + [vp]
+        L.wkv7_bwd_inputs.restype = i
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Wkv7Error(fn, status, lib().wkv7_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"inputs must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _shape(r):
+    if r.dim() != 4:
+        raise ValueError("inputs must be (B, T, H, D)")
+    return tuple(r.shape)
+
+
+def num_chunks(T: int) -> int:
+    return int(lib().wkv7_num_chunks(T))
+
+
+def workspace_bytes(B: int, T: int, H: int, D: int = HEAD_SIZE) -> int:
+    return int(lib().wkv7_bwd_workspace_bytes(B, T, H, D))
+
+
+def _fwd_call(cfn, name, r, w, k, v, a, b, h0, want_y, want_ckpt, want_hT, y, ckpt, hT):
+    import torch
+    B, T, H, D = _shape(r)
+    dev = r.device
+    f32 = dict(device=dev, dtype=torch.float32)
+    if want_y and y is None:
+        y = torch.empty((B, T, H, D), **f32)
+    if want_ckpt and ckpt is None:
+        ckpt = torch.empty((B, H, num_chunks(T), D, D), **f32)
+    if want_hT and hT is None:
+        hT = torch.empty((B, H, D, D), **f32)
+    st = cfn(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, v, a, b)), _ptr(h0),
+             _ptr(y), _ptr(ckpt), _ptr(hT), _stream(dev))
+    _check(name, st)
+    return y, ckpt, hT
+
+
+def fwd(r, w, k, v, a, b, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
+        y=None, ckpt=None, hT=None):
+    """Forward.  Returns (y, ckpt, hT); entries not wanted are None.
+    Pre-allocated outputs may be passed; hT may be h0 (in-place update)."""
+    return _fwd_call(lib().wkv7_fwd, "wkv7_fwd", r, w, k, v, a, b, h0,
+                     want_y, want_ckpt, want_hT, y, ckpt, hT)
+
+
+def fwd_sequential(r, w, k, v, a, b, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
+                   y=None, ckpt=None, hT=None):
+    """Token-by-token forward (same results as ``fwd``)."""
+    return _fwd_call(lib().wkv7_fwd_sequential, "wkv7_fwd_sequential", r, w, k, v, a, b, h0,
+                     want_y, want_ckpt, want_hT, y, ckpt, hT)
+
+
+def step(r, w, k, v, a, b, state, y=None):
+    """One recurrent call updating ``state`` (B,H,64,64) in place; returns y."""
+    y, _, _ = fwd(r, w, k, v, a, b, state, want_ckpt=False, y=y, hT=state)
+    return y
+
+
+def bwd(dy, r, w, k, v, a, b, ckpt, dhT=None, *, want_dh0=True, workspace=None, out=None):
+    """Backward.  Returns (dr, dw, dk, dv, da, db, dh0) as fp32 tensors."""
+    import torch
+    B, T, H, D = _shape(r)
+    dev = r.device
+    f32 = dict(device=dev, dtype=torch.float32)
+    if out is None:
+        out = [torch.empty((B, T, H, D), **f32) for _ in range(6)]
+    dh0 = torch.empty((B, H, D, D), **f32) if want_dh0 else None
+    need = workspace_bytes(B, T, H, D)
+    if workspace is None:
+        workspace = torch.empty(need // 4, **f32)
+    st = lib().wkv7_bwd(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
+                        *map(_ptr, (r, w, k, v, a, b)), _ptr(ckpt), *map(_ptr, out), _ptr(dh0),
+                        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("wkv7_bwd", st)
+    return (*out, dh0)
+
+
+def bwd_state(dy, r, w, k, a, b, dhT=None, *, want_dv=True, want_dh0=True, dh_ckpt=None):
+    """First backward stage: returns (dh_ckpt, dv, dh0); dh_ckpt[:, :, c] is the
+    gradient w.r.t. checkpoint c."""
+    import torch
+    B, T, H, D = _shape(r)
+    f32 = dict(device=r.device, dtype=torch.float32)
+    if dh_ckpt is None:
+        dh_ckpt = torch.empty((B, H, num_chunks(T), D, D), **f32)
+    dv = torch.empty((B, T, H, D), **f32) if want_dv else None
+    dh0 = torch.empty((B, H, D, D), **f32) if want_dh0 else None
+    st = lib().wkv7_bwd_state(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
+                              *map(_ptr, (r, w, k, a, b)), _ptr(dh_ckpt), _ptr(dv), _ptr(dh0),
+                              _stream(r.device))
+    _check("wkv7_bwd_state", st)
+    return dh_ckpt, dv, dh0
+
+
+def bwd_inputs(dy, r, w, k, v, a, b, ckpt, dh_ckpt, dhT=None, *, out=None):
+    """Second backward stage: returns (dr, dw, dk, da, db)."""
+    import torch
+    B, T, H, D = _shape(r)
+    if out is None:
+        out = [torch.empty((B, T, H, D), device=r.device, dtype=torch.float32) for _ in range(5)]
+    st = lib().wkv7_bwd_inputs(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
+                               *map(_ptr, (r, w, k, v, a, b)), _ptr(ckpt), _ptr(dh_ckpt),
+                               *map(_ptr, out), _stream(r.device))
+    _check("wkv7_bwd_inputs", st)
+    return tuple(out)
+
+
+def _make_autograd():
+    import torch
+
+    class WKV7(torch.autograd.Function):
+        """Differentiable op: (r, w, k, v, a, b, h0) -> (y, hT), gradients by wkv7_bwd."""
+
+        @staticmethod
+        def forward(ctx, r, w, k, v, a, b, h0=None):
+            ins = [x.contiguous() for x in (r, w, k, v, a, b)]
+            h0c = None if h0 is None else h0.contiguous().float()
+            y, ckpt, hT = fwd(*ins, h0c)
+            ctx.save_for_backward(*ins, ckpt)
+            ctx.has_h0 = h0 is not None
+            return y, hT
+
+        @staticmethod
+        def backward(ctx, dy, dhT):
+            *ins, ckpt = ctx.saved_tensors
+            if dy is None:
+                dy = torch.zeros(ins[0].shape, dtype=torch.float32, device=ins[0].device)
+            else:
+                dy = dy.contiguous().float()
+            dhT = None if dhT is None else dhT.contiguous().float()
+            dr, dw, dk, dv, da, db, dh0 = bwd(dy, *ins, ckpt, dhT)
+            cast = lambda g, x: g.to(x.dtype)
+            grads = [cast(g, x) for g, x in zip((dr, dw, dk, dv, da, db), ins)]
+            return (*grads, dh0 if ctx.has_h0 else None)
+
+    return WKV7
+
+
+class _LazyWKV7:
+    _cls = None
+
+    def __getattr__(self, name):
+        if _LazyWKV7._cls is None:
+            _LazyWKV7._cls = _make_autograd()
+        return getattr(_LazyWKV7._cls, name)
+
+
+WKV7 = _LazyWKV7()

@@ -1,0 +1,275 @@
+// wkv7_api.hip -- the C ABI of libwkv7 (declared in include/wkv7.h):
+// argument checks on the host, then kernel launches on the caller's stream.
+#include <stdint.h>
+
+#include "wkv7.h"
+#include "wkv7_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kD = 64;
+constexpr int kChunk = 32;
+// wkv7_fwd evaluates sequences of at most this many tokens token by token.
+constexpr int kSequentialMaxT = 1;
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi); empty if lo == hi
+};
+
+Span span(const void* p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, p ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlaps(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Sizes {
+    int64_t heads, nc, tok_elems, state_elems, ckpt_elems;
+};
+
+wkv7_status check_shape(int B, int T, int H, int D, Sizes* sz) {
+    if (D != kD || B < 1 || T < 1 || H < 1) return WKV7_ERR_SHAPE;
+    const int64_t heads = (int64_t)B * H;
+    const int64_t nc = ((int64_t)T + kChunk - 1) / kChunk;
+    // Grid sizes (heads * NC workgroups at most) must fit a 32-bit launch.
+    if (heads * nc * 4 > INT32_MAX || heads * 4 > INT32_MAX) return WKV7_ERR_SHAPE;
+    const int64_t tok = heads * (int64_t)T * kD;
+    if (tok / T != heads * kD) return WKV7_ERR_SHAPE;
+    if (tok > (INT64_MAX / 8)) return WKV7_ERR_SHAPE;
+    sz->heads = heads;
+    sz->nc = nc;
+    sz->tok_elems = tok;
+    sz->state_elems = heads * kD * kD;
+    sz->ckpt_elems = heads * nc * kD * kD;
+    if (sz->ckpt_elems > (INT64_MAX / 8)) return WKV7_ERR_SHAPE;
+    return WKV7_OK;
+}
+
+int elem_size(wkv7_dtype dt) { return dt == WKV7_BF16 ? 2 : 4; }
+
+wkv7_status check_dtype(int dt) { return (dt == WKV7_F32 || dt == WKV7_BF16) ? WKV7_OK : WKV7_ERR_DTYPE; }
+
+// One buffer argument of an entry point.
+struct Buf {
+    const void* p;
+    int64_t bytes;
+    bool required;
+    bool output;
+};
+
+// NULL and alignment checks over all buffers of a call.
+wkv7_status check_bufs(const Buf* bufs, int n) {
+    for (int i = 0; i < n; ++i)
+        if (bufs[i].required && !bufs[i].p) return WKV7_ERR_ARG;
+    for (int i = 0; i < n; ++i)
+        if (bufs[i].p && !aligned16(bufs[i].p)) return WKV7_ERR_ALIGN;
+    return WKV7_OK;
+}
+
+// Outputs may not overlap any other buffer; the one exception is
+// `same_ok_a` == `same_ok_b` (the in-place state update): those two buffers
+// may be the very same pointer.
+wkv7_status check_alias(const Buf* bufs, int n, const void* same_ok_a = nullptr,
+                        const void* same_ok_b = nullptr) {
+    for (int i = 0; i < n; ++i) {
+        if (!bufs[i].output || !bufs[i].p) continue;
+        const Span si = span(bufs[i].p, bufs[i].bytes);
+        for (int j = 0; j < n; ++j) {
+            if (j == i || !bufs[j].p) continue;
+            if (bufs[j].output && j < i) continue;  // pair already checked
+            const bool exempt = same_ok_a && same_ok_a == same_ok_b &&
+                                ((bufs[i].p == same_ok_a && bufs[j].p == same_ok_b) ||
+                                 (bufs[j].p == same_ok_a && bufs[i].p == same_ok_b));
+            if (exempt) continue;
+            if (overlaps(si, span(bufs[j].p, bufs[j].bytes))) return WKV7_ERR_ALIAS;
+        }
+    }
+    return WKV7_OK;
+}
+
+// Shared checks of the forward entry points.
+wkv7_status check_fwd(int B, int T, int H, int D, wkv7_dtype dt, const void* r, const void* w,
+                      const void* k, const void* v, const void* a, const void* b, const float* h0,
+                      const float* y, const float* ckpt, const float* hT, Sizes* sz) {
+    wkv7_status st = check_dtype(dt);
+    if (st != WKV7_OK) return st;
+    st = check_shape(B, T, H, D, sz);
+    if (st != WKV7_OK) return st;
+    const int64_t tin = sz->tok_elems * elem_size(dt), t32 = sz->tok_elems * 4, s32 = sz->state_elems * 4;
+    const Buf bufs[10] = {{r, tin, true, false},  {w, tin, true, false},  {k, tin, true, false},
+                          {v, tin, true, false},  {a, tin, true, false},  {b, tin, true, false},
+                          {h0, s32, false, false}, {y, t32, false, true}, {ckpt, sz->ckpt_elems * 4, false, true},
+                          {hT, s32, false, true}};
+    st = check_bufs(bufs, 10);
+    if (st != WKV7_OK) return st;
+    if (!y && !ckpt && !hT) return WKV7_ERR_ARG;
+    return check_alias(bufs, 10, h0, hT);
+}
+
+wkv7::FwdArgs fwd_args(int B, int T, int H, const Sizes& sz, const void* r, const void* w,
+                       const void* k, const void* v, const void* a, const void* b, const float* h0,
+                       float* y, float* ckpt, float* hT) {
+    wkv7::FwdArgs fa;
+    fa.r = r; fa.w = w; fa.k = k; fa.v = v; fa.a = a; fa.b = b;
+    fa.h0 = h0; fa.y = y; fa.ckpt = ckpt; fa.hT = hT;
+    fa.B = B; fa.T = T; fa.H = H; fa.NC = (int)sz.nc;
+    return fa;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv7_version(void) { return kVersion; }
+
+int wkv7_chunk_len(void) { return kChunk; }
+
+int64_t wkv7_num_chunks(int64_t T) { return T < 1 ? 0 : (T + kChunk - 1) / kChunk; }
+
+const char* wkv7_status_str(int status) {
+    switch (status) {
+        case WKV7_OK: return "WKV7_OK";
+        case WKV7_ERR_ARG: return "WKV7_ERR_ARG: a required pointer is NULL or an argument is invalid";
+        case WKV7_ERR_SHAPE: return "WKV7_ERR_SHAPE: D must be 64 and B, T, H at least 1 (and sizes must fit)";
+        case WKV7_ERR_DTYPE: return "WKV7_ERR_DTYPE: in_dtype must be WKV7_F32 or WKV7_BF16";
+        case WKV7_ERR_ALIGN: return "WKV7_ERR_ALIGN: every pointer must be 16-byte aligned";
+        case WKV7_ERR_ALIAS: return "WKV7_ERR_ALIAS: an output overlaps an input or another output";
+        case WKV7_ERR_HIP: return "WKV7_ERR_HIP: kernel launch failed";
+        case WKV7_ERR_WORKSPACE: return "WKV7_ERR_WORKSPACE: workspace missing or too small";
+        default: return "WKV7: unknown status";
+    }
+}
+
+size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int D) {
+    Sizes sz;
+    if (check_shape(B, T, H, D, &sz) != WKV7_OK) return 0;
+    return (size_t)sz.ckpt_elems * sizeof(float);
+}
+
+wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
+                     const void* k, const void* v, const void* a, const void* b, const float* h0,
+                     float* y, float* h_ckpt, float* hT, void* stream) {
+    Sizes sz;
+    wkv7_status st = check_fwd(B, T, H, D, in_dtype, r, w, k, v, a, b, h0, y, h_ckpt, hT, &sz);
+    if (st != WKV7_OK) return st;
+    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, h0, y, h_ckpt, hT);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = in_dtype == WKV7_BF16;
+    const hipError_t e = T <= kSequentialMaxT ? wkv7::launch_fwd_sequential(fa, bf16, s)
+                                              : wkv7::launch_fwd_chunked(fa, bf16, s);
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r,
+                                const void* w, const void* k, const void* v, const void* a,
+                                const void* b, const float* h0, float* y, float* h_ckpt, float* hT,
+                                void* stream) {
+    Sizes sz;
+    wkv7_status st = check_fwd(B, T, H, D, in_dtype, r, w, k, v, a, b, h0, y, h_ckpt, hT, &sz);
+    if (st != WKV7_OK) return st;
+    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, h0, y, h_ckpt, hT);
+    const hipError_t e = wkv7::launch_fwd_sequential(fa, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+namespace {
+
+wkv7::BwdArgs bwd_args(int B, int T, int H, const Sizes& sz, const float* dy, const float* dhT,
+                       const void* r, const void* w, const void* k, const void* v, const void* a,
+                       const void* b, const float* h_ckpt, float* dh_ckpt) {
+    wkv7::BwdArgs ba = {};
+    ba.r = r; ba.w = w; ba.k = k; ba.v = v; ba.a = a; ba.b = b;
+    ba.dy = dy; ba.dhT = dhT; ba.ckpt = h_ckpt; ba.gbuf = dh_ckpt;
+    ba.B = B; ba.T = T; ba.H = H; ba.NC = (int)sz.nc;
+    return ba;
+}
+
+wkv7_status status_of(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP; }
+
+}  // namespace
+
+wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy,
+                           const float* dhT, const void* r, const void* w, const void* k, const void* a,
+                           const void* b, float* dh_ckpt, float* dv, float* dh0, void* stream) {
+    wkv7_status st = check_dtype(in_dtype);
+    if (st != WKV7_OK) return st;
+    Sizes sz;
+    st = check_shape(B, T, H, D, &sz);
+    if (st != WKV7_OK) return st;
+    const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
+    const Buf bufs[10] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
+                          {w, tin, true, false},  {k, tin, true, false},    {a, tin, true, false},
+                          {b, tin, true, false},  {dh_ckpt, sz.ckpt_elems * 4, true, true},
+                          {dv, t32, false, true}, {dh0, s32, false, true}};
+    st = check_bufs(bufs, 10);
+    if (st != WKV7_OK) return st;
+    st = check_alias(bufs, 10);
+    if (st != WKV7_OK) return st;
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, nullptr, a, b, nullptr, dh_ckpt);
+    ba.dv = dv;
+    ba.dh0 = dh0;
+    return status_of(wkv7::launch_bwd_state(ba, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
+}
+
+wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy,
+                            const float* dhT, const void* r, const void* w, const void* k, const void* v,
+                            const void* a, const void* b, const float* h_ckpt, const float* dh_ckpt,
+                            float* dr, float* dw, float* dk, float* da, float* db, void* stream) {
+    wkv7_status st = check_dtype(in_dtype);
+    if (st != WKV7_OK) return st;
+    Sizes sz;
+    st = check_shape(B, T, H, D, &sz);
+    if (st != WKV7_OK) return st;
+    const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
+    const int64_t c32 = sz.ckpt_elems * 4;
+    const Buf bufs[15] = {{dy, t32, true, false},  {dhT, s32, false, false}, {r, tin, true, false},
+                          {w, tin, true, false},   {k, tin, true, false},    {v, tin, true, false},
+                          {a, tin, true, false},   {b, tin, true, false},    {h_ckpt, c32, true, false},
+                          {dh_ckpt, c32, true, false}, {dr, t32, true, true}, {dw, t32, true, true},
+                          {dk, t32, true, true},   {da, t32, true, true},    {db, t32, true, true}};
+    st = check_bufs(bufs, 15);
+    if (st != WKV7_OK) return st;
+    st = check_alias(bufs, 15);
+    if (st != WKV7_OK) return st;
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, h_ckpt, const_cast<float*>(dh_ckpt));
+    ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.da = da; ba.db = db;
+    return status_of(wkv7::launch_bwd_inputs(ba, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
+}
+
+wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy, const float* dhT,
+                     const void* r, const void* w, const void* k, const void* v, const void* a,
+                     const void* b, const float* h_ckpt, float* dr, float* dw, float* dk, float* dv,
+                     float* da, float* db, float* dh0, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    wkv7_status st = check_dtype(in_dtype);
+    if (st != WKV7_OK) return st;
+    Sizes sz;
+    st = check_shape(B, T, H, D, &sz);
+    if (st != WKV7_OK) return st;
+    const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
+    const int64_t c32 = sz.ckpt_elems * 4;
+    const Buf bufs[17] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
+                          {w, tin, true, false},  {k, tin, true, false},    {v, tin, true, false},
+                          {a, tin, true, false},  {b, tin, true, false},    {h_ckpt, c32, true, false},
+                          {dr, t32, true, true},  {dw, t32, true, true},    {dk, t32, true, true},
+                          {dv, t32, true, true},  {da, t32, true, true},    {db, t32, true, true},
+                          {dh0, s32, false, true}, {workspace, c32, false, true}};
+    st = check_bufs(bufs, 17);
+    if (st != WKV7_OK) return st;
+    if (!workspace || workspace_bytes < (size_t)c32) return WKV7_ERR_WORKSPACE;
+    st = check_alias(bufs, 17);
+    if (st != WKV7_OK) return st;
+    float* gbuf = static_cast<float*>(workspace);
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, h_ckpt, gbuf);
+    ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.dv = dv; ba.da = da; ba.db = db; ba.dh0 = dh0;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = in_dtype == WKV7_BF16;
+    hipError_t e = wkv7::launch_bwd_state(ba, bf16, s);
+    if (e == hipSuccess) e = wkv7::launch_bwd_inputs(ba, bf16, s);
+    return status_of(e);
+}
+
+}  // extern "C"

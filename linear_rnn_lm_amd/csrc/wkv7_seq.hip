@@ -1,0 +1,100 @@
+// wkv7_seq.hip -- token-by-token WKV7 forward on the vector units (gfx950).
+//
+// The per-token update exactly as the rwkv-mlx page states it ("Metal kernel
+// architecture", forward block): sa = S a, S = S diag(w) + v k^T + sa b^T,
+// y = S r.  One workgroup per head; thread (i = tid/4, part = tid%4) keeps
+// the 16 state values S[i][16*part .. 16*part+15] in registers, so the row
+// dot products need a 4-lane reduction only.  This is the streaming path
+// for very short sequences -- above all the one-token recurrent step, where
+// the state is read from and written back to HBM once (in place if
+// hT == h0) and the kernel is bound by HBM bandwidth.
+#include "wkv7_device.h"
+#include "wkv7_internal.h"
+
+namespace wkv7 {
+namespace {
+
+constexpr int SEQ_NT = 256;
+
+template <typename InT>
+__device__ __forceinline__ float load1(const InT* p);
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) {
+    return __uint_as_float((uint32_t)(*p) << 16);
+}
+
+template <typename InT>
+__global__ __launch_bounds__(SEQ_NT) void fwd_sequential_kernel(FwdArgs p) {
+    __shared__ float vec[6][D];  // w, k, a, b, r, v of the current token
+    const int tid = threadIdx.x;
+    const int i = tid >> 2, part = tid & 3, j0 = part * 16;
+    const int head = blockIdx.x;
+    const int bb = head / p.H, hh = head % p.H;
+    const int64_t tstride = (int64_t)p.H * D;
+    const int64_t soff = (int64_t)head * D * D + (int64_t)i * D + j0;
+
+    float s[16];
+    if (p.h0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(p.h0 + soff + 4 * q);
+            s[4 * q] = v.x; s[4 * q + 1] = v.y; s[4 * q + 2] = v.z; s[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s[q] = 0.f;
+    }
+
+    const InT* srcs[6] = {static_cast<const InT*>(p.w), static_cast<const InT*>(p.k),
+                          static_cast<const InT*>(p.a), static_cast<const InT*>(p.b),
+                          static_cast<const InT*>(p.r), static_cast<const InT*>(p.v)};
+
+    for (int t = 0; t < p.T; ++t) {
+        const int64_t base = ((int64_t)bb * p.T + t) * tstride + (int64_t)hh * D;
+        if (p.ckpt && (t % C) == 0) {
+            float* dst = p.ckpt + ((int64_t)head * p.NC + t / C) * D * D + (int64_t)i * D + j0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(dst + 4 * q) = make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+        }
+        __syncthreads();  // previous token's reads of vec are done
+        for (int e = tid; e < 6 * D; e += SEQ_NT) vec[e / D][e % D] = load1<InT>(srcs[e / D] + base + (e % D));
+        __syncthreads();
+
+        float sa = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) sa = fmaf(s[q], vec[2][j0 + q], sa);
+        sa += __shfl_xor(sa, 1);
+        sa += __shfl_xor(sa, 2);
+        const float vi = vec[5][i];
+        float y = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int j = j0 + q;
+            s[q] = fmaf(vec[0][j], s[q], fmaf(vi, vec[1][j], sa * vec[3][j]));
+            y = fmaf(s[q], vec[4][j], y);
+        }
+        y += __shfl_xor(y, 1);
+        y += __shfl_xor(y, 2);
+        if (p.y && part == 0) p.y[base + i] = y;
+    }
+    if (p.hT) {
+        float* dst = p.hT + soff;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(dst + 4 * q) = make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, hipStream_t s) {
+    const int heads = a.B * a.H;
+    if (bf16) hipLaunchKernelGGL(fwd_sequential_kernel<uint16_t>, dim3(heads), dim3(SEQ_NT), 0, s, a);
+    else hipLaunchKernelGGL(fwd_sequential_kernel<float>, dim3(heads), dim3(SEQ_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace wkv7

@@ -1,0 +1,99 @@
+"""Shared helpers of the GPU parity tests: run the HIP path and the oracle on
+the same seeded inputs and compare tensor by tensor (relative L2 in fp64)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import linear_rnn_lm_amd as L
+import oracle
+
+# Tolerances on rel-L2 (|x - ref|_2 / |ref|_2 over a whole tensor, in fp64):
+# fp32 inputs 1e-5 on forward outputs and 1e-4 on gradients; bf16 inputs
+# (the oracle receives the same rounded values) 2e-3 on everything.
+TOL = {
+    torch.float32: {"fwd": 1e-5, "bwd": 1e-4},
+    torch.bfloat16: {"fwd": 2e-3, "bwd": 2e-3},
+}
+FWD_NAMES = ("y", "ckpt", "hT")
+BWD_NAMES = ("dr", "dw", "dk", "dv", "da", "db", "dh0")
+
+
+def note(msg):
+    """Name the case before a GPU step, flushed, so a crash log says what ran."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def rel(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / den) if den > 0 else float(np.linalg.norm(x))
+
+
+def _np(t):
+    return None if t is None else t.detach().double().cpu().numpy()
+
+
+def run_gpu(x, dhT=None, sequential=False, bwd=True):
+    dev = torch.device("cuda:0")
+    ins = [t.to(dev) for t in x.tensors()]
+    h0 = None if x.h0 is None else x.h0.to(dev)
+    f = L.fwd_sequential if sequential else L.fwd
+    y, ck, hT = f(*ins, h0)
+    out = {"y": y, "ckpt": ck, "hT": hT}
+    if bwd:
+        dy = x.dy.to(dev)
+        dh = None if dhT is None else dhT.to(dev)
+        g = L.bwd(dy, *ins, ck, dh)
+        out.update(dict(zip(BWD_NAMES, g)))
+    torch.cuda.synchronize()
+    return {k: _np(v) for k, v in out.items()}
+
+
+def run_oracle(x, dhT=None, bwd=True):
+    y, ck, hT = oracle.fwd(*x.tensors(), x.h0)
+    out = {"y": y, "ckpt": ck, "hT": hT}
+    if bwd:
+        g = oracle.bwd(*x.tensors(), x.dy, x.h0, dhT)
+        out.update(dict(zip(BWD_NAMES, g)))
+    return out
+
+
+def compare(gpu, ref, dtype, names=None):
+    """Return {name: rel-L2} and the list of names over tolerance."""
+    names = names or [n for n in FWD_NAMES + BWD_NAMES if n in gpu and n in ref]
+    errs, bad = {}, []
+    for n in names:
+        e = rel(gpu[n], ref[n])
+        errs[n] = e
+        tol = TOL[dtype]["fwd" if n in FWD_NAMES else "bwd"]
+        if not (e <= tol):
+            bad.append(n)
+    return errs, bad
+
+
+def slice_heads(x, bsel, hsel):
+    """Sub-workload of heads (b, h) for b in bsel, h in hsel (index lists)."""
+    from linear_rnn_lm_amd.inputs import Inputs
+    bi = torch.tensor(bsel)
+    hi = torch.tensor(hsel)
+    tok = lambda t: t.index_select(0, bi).index_select(2, hi).contiguous()
+    st = lambda t: None if t is None else t.index_select(0, bi).index_select(1, hi).contiguous()
+    return Inputs(*(tok(t) for t in x.tensors()), st(x.h0), tok(x.dy))
+
+
+def select_heads(out, bsel, hsel):
+    bi, hi = np.asarray(bsel), np.asarray(hsel)
+    res = {}
+    for n, v in out.items():
+        if v is None:
+            continue
+        if n in ("ckpt", "hT", "dh0"):
+            res[n] = v[bi][:, hi]
+        else:
+            res[n] = v[bi][:, :, hi]
+    return res

@@ -1,0 +1,144 @@
+"""The C ABI of libwkv7 on the host: it loads, exports every declared symbol,
+and rejects bad arguments before anything reaches the GPU (CPU only).
+
+The rejection tests pass made-up device addresses; every case is built to
+fail a host-side check, so no kernel is ever launched.  They are skipped
+where a GPU is present (the GPU suite repeats them with real allocations).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_rnn_lm_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wkv7.h")
+
+OK, ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_ALIAS, ERR_HIP, ERR_WS = range(8)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wkv7_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    names = declared_functions()
+    assert {"wkv7_fwd", "wkv7_bwd", "wkv7_fwd_sequential", "wkv7_bwd_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in wkv7.h but not exported"
+
+
+def test_library_has_no_unexpected_exports():
+    out = os.popen(f"nm -D --defined-only {L.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (wkv7_[a-z0-9_]+)\b", out))
+    assert exported == set(declared_functions())
+
+
+def test_queries():
+    lib = L.lib()
+    assert lib.wkv7_version() >= 100
+    assert lib.wkv7_chunk_len() == 32
+    assert [L.num_chunks(t) for t in (0, 1, 31, 32, 33, 64, 1024)] == [0, 1, 1, 1, 2, 2, 32]
+    assert L.workspace_bytes(12, 1024, 6) == 12 * 6 * 32 * 64 * 64 * 4
+    assert L.workspace_bytes(1, 1, 1) == 64 * 64 * 4
+    assert L.workspace_bytes(1, 0, 1) == 0
+    assert L.workspace_bytes(1, 10, 1, 32) == 0
+    for s in range(8):
+        assert lib.wkv7_status_str(s).startswith(b"WKV7")
+    assert b"unknown" in lib.wkv7_status_str(99)
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+needs_no_gpu = pytest.mark.skipif(_gpu_present(), reason="made-up device pointers are only used without a GPU")
+
+BASE = 1 << 40          # a made-up, 16-byte-aligned device address
+MB = 1 << 20
+
+
+def fake(n):            # distinct non-overlapping fake buffers, 64 MiB apart
+    return BASE + n * 64 * MB
+
+
+def fwd_args(**over):
+    a = dict(B=1, T=64, H=1, D=64, dt=1, r=fake(0), w=fake(1), k=fake(2), v=fake(3), a=fake(4),
+             b=fake(5), h0=None, y=fake(6), ck=fake(7), hT=fake(8))
+    a.update(over)
+    return a
+
+
+def call_fwd(fn="wkv7_fwd", **over):
+    a = fwd_args(**over)
+    f = getattr(L.lib(), fn)
+    return f(a["B"], a["T"], a["H"], a["D"], a["dt"], a["r"], a["w"], a["k"], a["v"], a["a"], a["b"],
+             a["h0"], a["y"], a["ck"], a["hT"], None)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("fn", ["wkv7_fwd", "wkv7_fwd_sequential"])
+def test_fwd_rejects_bad_arguments(fn):
+    c = lambda **o: call_fwd(fn, **o)
+    assert c(D=32) == ERR_SHAPE
+    assert c(T=0) == ERR_SHAPE
+    assert c(B=0) == ERR_SHAPE
+    assert c(H=-1) == ERR_SHAPE
+    assert c(dt=7) == ERR_DTYPE
+    assert c(r=None) == ERR_ARG
+    assert c(b=None) == ERR_ARG
+    assert c(y=None, ck=None, hT=None) == ERR_ARG
+    assert c(w=fake(1) + 4) == ERR_ALIGN
+    assert c(h0=fake(9) + 8) == ERR_ALIGN
+    assert c(y=fake(0)) == ERR_ALIAS                 # y on top of r
+    assert c(y=fake(5) + 4096) == ERR_ALIAS          # y overlapping the tail of b
+    assert c(hT=fake(6)) == ERR_ALIAS                # hT inside y
+    assert c(ck=fake(6) + 16) == ERR_ALIAS           # ckpt overlapping y
+    assert c(h0=fake(9), hT=fake(9) + 64) == ERR_ALIAS  # hT overlapping h0 but not equal
+
+
+@needs_no_gpu
+def test_bwd_rejects_bad_arguments():
+    lib = L.lib()
+    B, T, H, D = 1, 64, 1, 64
+    ws = L.workspace_bytes(B, T, H)
+
+    def c(**o):
+        a = dict(B=B, T=T, H=H, D=D, dt=1, dy=fake(0), dhT=None, r=fake(1), w=fake(2), k=fake(3),
+                 v=fake(4), a=fake(5), b=fake(6), ck=fake(7), dr=fake(8), dw=fake(9), dk=fake(10),
+                 dv=fake(11), da=fake(12), db=fake(13), dh0=fake(14), ws=fake(15), wsb=ws)
+        a.update(o)
+        return lib.wkv7_bwd(a["B"], a["T"], a["H"], a["D"], a["dt"], a["dy"], a["dhT"], a["r"], a["w"],
+                            a["k"], a["v"], a["a"], a["b"], a["ck"], a["dr"], a["dw"], a["dk"], a["dv"],
+                            a["da"], a["db"], a["dh0"], a["ws"], a["wsb"], None)
+
+    assert c(D=16) == ERR_SHAPE
+    assert c(T=0) == ERR_SHAPE
+    assert c(dt=2) == ERR_DTYPE
+    assert c(dy=None) == ERR_ARG
+    assert c(ck=None) == ERR_ARG
+    assert c(db=None) == ERR_ARG
+    assert c(ws=None) == ERR_WS
+    assert c(wsb=ws - 4) == ERR_WS
+    assert c(dv=fake(11) + 2) == ERR_ALIGN
+    assert c(ws=fake(15) + 8) == ERR_ALIGN
+    assert c(dr=fake(0)) == ERR_ALIAS                # dr on dy
+    assert c(dw=fake(8) + 64) == ERR_ALIAS           # dw overlapping dr
+    assert c(ws=fake(7)) == ERR_ALIAS                # workspace on the checkpoints
+    assert c(dh0=fake(16), dhT=fake(16)) == ERR_ALIAS
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        L.lib()
