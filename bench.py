@@ -46,11 +46,13 @@ def kernel_bytes(wl, in_bytes: int) -> dict:
     tok32 = ht * D * 4
     st = heads * D * D * 4
     ck = heads * nc * D * D * 4
+    inv = heads * nc * 32 * 32 * 4
     h0 = st if wl.with_h0 else 0
     return {
-        "fwd": 6 * tok_in + tok32 + ck + h0 + st,
-        "bwd_state": 5 * tok_in + tok32 + tok32 + ck + st,
-        "bwd_inputs": 6 * tok_in + tok32 + 2 * ck + 5 * tok32,
+        "chunk_inverse": 3 * tok_in + inv,
+        "fwd": 6 * tok_in + inv + tok32 + ck + h0 + st,
+        "bwd_state": 5 * tok_in + inv + tok32 + tok32 + ck + st,
+        "bwd_inputs": 6 * tok_in + inv + tok32 + 2 * ck + 5 * tok32,
         # whole path, algorithmic: fwd 1536 B and bwd 3072 B per head-token (bf16 inputs)
         "path": (6 * tok_in + tok32 + ck + h0 + st) + (6 * tok_in + tok32 + ck + 6 * tok32 + st),
     }
@@ -126,6 +128,7 @@ def main() -> int:
     ck = torch.empty(B, H, nc, D, D, **f32)
     hT = torch.empty(B, H, D, D, **f32)
     dck = torch.empty(B, H, nc, D, D, **f32)
+    inv = torch.empty(B, H, nc, 32, 32, **f32)
     dv = torch.empty(B, T, H, D, **f32)
     dh0 = torch.empty(B, H, D, D, **f32)
     grads = [torch.empty(B, T, H, D, **f32) for _ in range(5)]
@@ -136,21 +139,29 @@ def main() -> int:
     p = [t.data_ptr() for t in ins]
     ph0 = None if h0 is None else h0.data_ptr()
 
+    pinv = inv.data_ptr()
+
+    def k_inv():
+        st = lib.wkv7_chunk_inverse(B, T, H, D, code, p[1], p[4], p[5], pinv, sh)
+        assert st == 0, lib.wkv7_status_str(st)
+
     def k_fwd():
-        st = lib.wkv7_fwd(B, T, H, D, code, *p, ph0, y.data_ptr(), ck.data_ptr(), hT.data_ptr(), sh)
+        st = lib.wkv7_fwd_chunks(B, T, H, D, code, *p, pinv, ph0, y.data_ptr(), ck.data_ptr(), hT.data_ptr(), sh)
         assert st == 0, lib.wkv7_status_str(st)
 
     def k_state():
-        st = lib.wkv7_bwd_state(B, T, H, D, code, dy.data_ptr(), None, p[0], p[1], p[2], p[4], p[5],
+        st = lib.wkv7_bwd_state(B, T, H, D, code, dy.data_ptr(), None, p[0], p[1], p[2], p[4], p[5], pinv,
                                 dck.data_ptr(), dv.data_ptr(), dh0.data_ptr(), sh)
         assert st == 0, lib.wkv7_status_str(st)
 
     def k_inputs():
-        st = lib.wkv7_bwd_inputs(B, T, H, D, code, dy.data_ptr(), None, *p, ck.data_ptr(), dck.data_ptr(),
+        st = lib.wkv7_bwd_inputs(B, T, H, D, code, dy.data_ptr(), None, *p, pinv, ck.data_ptr(), dck.data_ptr(),
                                  *[g.data_ptr() for g in grads], sh)
         assert st == 0, lib.wkv7_status_str(st)
 
-    kernels = [("fwd", k_fwd), ("bwd_state", k_state), ("bwd_inputs", k_inputs)]
+    # one training step: the chunk inverses (shared by forward and backward), the
+    # forward, the state-gradient pass, the input gradients
+    kernels = [("chunk_inverse", k_inv), ("fwd", k_fwd), ("bwd_state", k_state), ("bwd_inputs", k_inputs)]
 
     def step():
         for _, fn in kernels:
@@ -213,7 +224,7 @@ def main() -> int:
         "config": {"workload": f"{wl.name}: WKV7 fwd+bwd {wl.description}, chunk 32",
                    "B": B, "T": T, "H": H, "D": D,
                    "in_dtype": "bf16" if in_bytes == 2 else "f32", "state_dtype": "f32"},
-        "fwd_tokens_per_s": tokens / (per_kernel_ms["fwd"] * 1e-3),
+        "fwd_tokens_per_s": tokens / ((per_kernel_ms["fwd"] + per_kernel_ms["chunk_inverse"]) * 1e-3),
         "kernel_ms": per_kernel_ms,
         "path_hbm": {"algorithmic_bytes": kb["path"],
                      "achieved_GBs": kb["path"] / (ms_per_step * 1e-3) / 1e9,

@@ -86,9 +86,34 @@ int64_t wkv7_num_chunks(int64_t T);
 /* Static string naming a status code (never NULL). */
 const char *wkv7_status_str(int status);
 
-/* Bytes of device workspace wkv7_bwd needs: B*H*NC*D*D*4 (one fp32 state
- * gradient per chunk boundary).  0 for invalid shapes. */
+/* Bytes of the per-chunk inverses: B*H*NC*32*32*4.  0 for invalid shapes. */
+size_t wkv7_chunk_inv_bytes(int B, int T, int H, int D);
+
+/* Bytes of device workspace wkv7_fwd needs: wkv7_chunk_inv_bytes(...) when
+ * T > 1, else 0.  0 for invalid shapes. */
+size_t wkv7_fwd_workspace_bytes(int B, int T, int H, int D);
+
+/* Bytes of device workspace wkv7_bwd needs: one fp32 D x D state gradient per
+ * chunk (B*H*NC*D*D*4) plus wkv7_chunk_inv_bytes(...).  0 for invalid shapes. */
 size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int D);
+
+/*
+ * Per-chunk factor of the chunked evaluation.  Within chunk c (tokens
+ * 32c .. 32c+31; a shorter last chunk is padded with w = 1, a = b = 0) let
+ * g_t be the running product of w over the chunk's tokens up to t, and
+ *     L[t][s] = sum_j a_t[j] g_{t-1}[j] b_s[j] / g_s[j]   for s < t, else 0
+ * (the coupling of token s's b into token t's sa through the decays in
+ * between; rwkv-mlx page, "Metal kernel architecture", forward block, unrolled
+ * over one chunk).  Writes chunk_inv[b][h][c] = (I - L)^-1, 32 x 32 fp32,
+ * row-major: (B, H, NC, 32, 32).  It depends on w, a, b only, so the forward
+ * and the backward of one step may share it.
+ *
+ *   w, a, b   : (B,T,H,D), in_dtype, required.
+ *   chunk_inv : output, required, wkv7_chunk_inv_bytes(...) bytes.
+ */
+wkv7_status wkv7_chunk_inverse(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                               const void *w, const void *a, const void *b,
+                               float *chunk_inv, void *stream);
 
 /*
  * Forward (rwkv-mlx page, "Metal kernel architecture", forward block).
@@ -101,13 +126,27 @@ size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int D);
  *   hT               : (B,H,D,D) fp32 final state, or NULL.  hT may be the
  *                      same pointer as h0 (state updated in place), but must
  *                      not otherwise overlap h0.
+ *   workspace        : device scratch of wkv7_fwd_workspace_bytes(...) bytes;
+ *                      may be NULL when that is 0 (T == 1).  Clobbered; on
+ *                      return it holds the chunk inverses (wkv7_chunk_inverse).
  * At least one of y, h_ckpt, hT must be non-NULL.
+ * Equivalent to wkv7_chunk_inverse into the workspace, then wkv7_fwd_chunks.
  */
 wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
                      const void *r, const void *w, const void *k,
                      const void *v, const void *a, const void *b,
                      const float *h0, float *y, float *h_ckpt, float *hT,
-                     void *stream);
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward given the chunk inverses (from wkv7_chunk_inverse for the same w,
+ * a, b).  Arguments as wkv7_fwd; chunk_inv is required.
+ */
+wkv7_status wkv7_fwd_chunks(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                            const void *r, const void *w, const void *k,
+                            const void *v, const void *a, const void *b,
+                            const float *chunk_inv, const float *h0,
+                            float *y, float *h_ckpt, float *hT, void *stream);
 
 /*
  * Backward (rwkv-mlx page, "Metal kernel architecture", backward block:
@@ -124,8 +163,8 @@ wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
  *   workspace        : device scratch of at least
  *                      wkv7_bwd_workspace_bytes(B,T,H,D) bytes, required; its
  *                      contents on entry do not matter and are clobbered.
- * Equivalent to wkv7_bwd_state (with the workspace as dh_ckpt) followed by
- * wkv7_bwd_inputs.
+ * Equivalent to wkv7_chunk_inverse, wkv7_bwd_state (the workspace's first
+ * part as dh_ckpt), then wkv7_bwd_inputs.
  */
 wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
                      const float *dy, const float *dhT,
@@ -144,6 +183,7 @@ wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
  * state gradient obeys its own recurrence, driven by dy, r, w, a, b.
  *
  *   dy, dhT, r, w, k, a, b : as for wkv7_bwd.
+ *   chunk_inv: from wkv7_chunk_inverse for the same w, a, b, required.
  *   dh_ckpt  : (B,H,NC,D,D) fp32 output, required: dh_ckpt[c] is the gradient
  *              w.r.t. checkpoint c (the state entering chunk c).
  *   dv       : (B,T,H,D) fp32 output (the gradient w.r.t. v), or NULL.
@@ -152,7 +192,7 @@ wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
 wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype,
                            const float *dy, const float *dhT,
                            const void *r, const void *w, const void *k,
-                           const void *a, const void *b,
+                           const void *a, const void *b, const float *chunk_inv,
                            float *dh_ckpt, float *dv, float *dh0,
                            void *stream);
 
@@ -162,6 +202,7 @@ wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype,
  * dividing by w).
  *
  *   dy, dhT, r..b, h_ckpt : as for wkv7_bwd.
+ *   chunk_inv: from wkv7_chunk_inverse for the same w, a, b, required.
  *   dh_ckpt  : (B,H,NC,D,D) written by wkv7_bwd_state for the same inputs.
  *   dr, dw, dk, da, db : (B,T,H,D) fp32 outputs, required.
  */
@@ -169,17 +210,18 @@ wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype,
                             const float *dy, const float *dhT,
                             const void *r, const void *w, const void *k,
                             const void *v, const void *a, const void *b,
-                            const float *h_ckpt, const float *dh_ckpt,
+                            const float *chunk_inv, const float *h_ckpt,
+                            const float *dh_ckpt,
                             float *dr, float *dw, float *dk, float *da, float *db,
                             void *stream);
 
 /*
- * Token-by-token forward (same definition as wkv7_fwd, same arguments and
- * rules), evaluated one token after another on the vector units instead of
- * in chunks on the matrix cores.  This is the path wkv7_fwd itself takes for
- * very short sequences (the one-token recurrent step of RNN-mode inference,
- * RWKV-LM README page, the pip-package usage that hands the state from call
- * to call).  Exposed so that callers can pick it explicitly.
+ * Token-by-token forward (same definition as wkv7_fwd, same rules, no
+ * workspace), evaluated one token after another on the vector units instead
+ * of in chunks on the matrix cores.  This is the path wkv7_fwd itself takes
+ * for one-token calls (the recurrent step of RNN-mode inference, RWKV-LM
+ * README page, the pip-package usage that hands the state from call to
+ * call).  Exposed so that callers can pick it explicitly.
  */
 wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype,
                                 const void *r, const void *w, const void *k,

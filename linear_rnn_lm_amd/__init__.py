@@ -18,7 +18,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["lib", "fwd", "fwd_sequential", "bwd", "bwd_state", "bwd_inputs", "step", "WKV7", "Wkv7Error",
+__all__ = ["lib", "fwd", "fwd_sequential", "fwd_chunks", "chunk_inverse", "bwd", "bwd_state",
+           "bwd_inputs", "step", "WKV7", "Wkv7Error",
            "num_chunks", "workspace_bytes", "CHUNK", "HEAD_SIZE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,17 +52,22 @@ def lib():
         L.wkv7_num_chunks.restype = i64
         L.wkv7_status_str.argtypes = [i]
         L.wkv7_status_str.restype = ctypes.c_char_p
-        L.wkv7_bwd_workspace_bytes.argtypes = [i, i, i, i]
-        L.wkv7_bwd_workspace_bytes.restype = sz
-        L.wkv7_fwd.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 4 + [vp]
+        for q in ("wkv7_bwd_workspace_bytes", "wkv7_fwd_workspace_bytes", "wkv7_chunk_inv_bytes"):
+            getattr(L, q).argtypes = [i, i, i, i]
+            getattr(L, q).restype = sz
+        L.wkv7_chunk_inverse.argtypes = [i, i, i, i, i] + [vp] * 3 + [vp] + [vp]
+        L.wkv7_chunk_inverse.restype = i
+        L.wkv7_fwd.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 4 + [vp, sz] + [vp]
         L.wkv7_fwd.restype = i
-        L.wkv7_fwd_sequential.argtypes = L.wkv7_fwd.argtypes
+        L.wkv7_fwd_chunks.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 5 + [vp]
+        L.wkv7_fwd_chunks.restype = i
+        L.wkv7_fwd_sequential.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 4 + [vp]
         L.wkv7_fwd_sequential.restype = i
         L.wkv7_bwd.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] + [vp] * 7 + [vp, sz, vp]
         L.wkv7_bwd.restype = i
-        L.wkv7_bwd_state.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 5 + [vp] * 3 + [vp]
+        L.wkv7_bwd_state.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 5 + [vp] + [vp] * 3 + [vp]
         L.wkv7_bwd_state.restype = i
-        L.wkv7_bwd_inputs.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] * 2 + [vp] * 5 + [vp]
+        L.wkv7_bwd_inputs.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] * 3 + [vp] * 5 + [vp]
         L.wkv7_bwd_inputs.restype = i
         _lib = L
     return _lib
@@ -101,39 +107,84 @@ def num_chunks(T: int) -> int:
 
 
 def workspace_bytes(B: int, T: int, H: int, D: int = HEAD_SIZE) -> int:
+    """Workspace bytes of wkv7_bwd."""
     return int(lib().wkv7_bwd_workspace_bytes(B, T, H, D))
 
 
-def _fwd_call(cfn, name, r, w, k, v, a, b, h0, want_y, want_ckpt, want_hT, y, ckpt, hT):
+def fwd_workspace_bytes(B: int, T: int, H: int, D: int = HEAD_SIZE) -> int:
+    return int(lib().wkv7_fwd_workspace_bytes(B, T, H, D))
+
+
+def chunk_inv_bytes(B: int, T: int, H: int, D: int = HEAD_SIZE) -> int:
+    return int(lib().wkv7_chunk_inv_bytes(B, T, H, D))
+
+
+def _f32_bytes(nbytes, device):
+    import torch
+    return torch.empty(max(nbytes, 16) // 4, device=device, dtype=torch.float32)
+
+
+def _fwd_outputs(r, want_y, want_ckpt, want_hT, y, ckpt, hT):
     import torch
     B, T, H, D = _shape(r)
-    dev = r.device
-    f32 = dict(device=dev, dtype=torch.float32)
+    f32 = dict(device=r.device, dtype=torch.float32)
     if want_y and y is None:
         y = torch.empty((B, T, H, D), **f32)
     if want_ckpt and ckpt is None:
         ckpt = torch.empty((B, H, num_chunks(T), D, D), **f32)
     if want_hT and hT is None:
         hT = torch.empty((B, H, D, D), **f32)
-    st = cfn(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, v, a, b)), _ptr(h0),
-             _ptr(y), _ptr(ckpt), _ptr(hT), _stream(dev))
-    _check(name, st)
     return y, ckpt, hT
 
 
 def fwd(r, w, k, v, a, b, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
-        y=None, ckpt=None, hT=None):
+        y=None, ckpt=None, hT=None, workspace=None):
     """Forward.  Returns (y, ckpt, hT); entries not wanted are None.
     Pre-allocated outputs may be passed; hT may be h0 (in-place update)."""
-    return _fwd_call(lib().wkv7_fwd, "wkv7_fwd", r, w, k, v, a, b, h0,
-                     want_y, want_ckpt, want_hT, y, ckpt, hT)
+    B, T, H, D = _shape(r)
+    y, ckpt, hT = _fwd_outputs(r, want_y, want_ckpt, want_hT, y, ckpt, hT)
+    need = fwd_workspace_bytes(B, T, H, D)
+    if workspace is None and need:
+        workspace = _f32_bytes(need, r.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().wkv7_fwd(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, v, a, b)), _ptr(h0),
+                        _ptr(y), _ptr(ckpt), _ptr(hT), _ptr(workspace), wsb, _stream(r.device))
+    _check("wkv7_fwd", st)
+    return y, ckpt, hT
+
+
+def chunk_inverse(w, a, b, out=None):
+    """(I - L)^-1 of every chunk, (B, H, NC, 32, 32) fp32 (see include/wkv7.h)."""
+    import torch
+    B, T, H, D = _shape(w)
+    if out is None:
+        out = torch.empty((B, H, num_chunks(T), CHUNK, CHUNK), device=w.device, dtype=torch.float32)
+    st = lib().wkv7_chunk_inverse(B, T, H, D, _dtype_code(w), _ptr(w), _ptr(a), _ptr(b), _ptr(out),
+                                  _stream(w.device))
+    _check("wkv7_chunk_inverse", st)
+    return out
+
+
+def fwd_chunks(r, w, k, v, a, b, chunk_inv, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
+               y=None, ckpt=None, hT=None):
+    """Forward given the chunk inverses of the same w, a, b."""
+    B, T, H, D = _shape(r)
+    y, ckpt, hT = _fwd_outputs(r, want_y, want_ckpt, want_hT, y, ckpt, hT)
+    st = lib().wkv7_fwd_chunks(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, v, a, b)), _ptr(chunk_inv),
+                               _ptr(h0), _ptr(y), _ptr(ckpt), _ptr(hT), _stream(r.device))
+    _check("wkv7_fwd_chunks", st)
+    return y, ckpt, hT
 
 
 def fwd_sequential(r, w, k, v, a, b, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
                    y=None, ckpt=None, hT=None):
     """Token-by-token forward (same results as ``fwd``)."""
-    return _fwd_call(lib().wkv7_fwd_sequential, "wkv7_fwd_sequential", r, w, k, v, a, b, h0,
-                     want_y, want_ckpt, want_hT, y, ckpt, hT)
+    B, T, H, D = _shape(r)
+    y, ckpt, hT = _fwd_outputs(r, want_y, want_ckpt, want_hT, y, ckpt, hT)
+    st = lib().wkv7_fwd_sequential(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, v, a, b)), _ptr(h0),
+                                   _ptr(y), _ptr(ckpt), _ptr(hT), _stream(r.device))
+    _check("wkv7_fwd_sequential", st)
+    return y, ckpt, hT
 
 
 def step(r, w, k, v, a, b, state, y=None):
@@ -161,7 +212,7 @@ def bwd(dy, r, w, k, v, a, b, ckpt, dhT=None, *, want_dh0=True, workspace=None, 
     return (*out, dh0)
 
 
-def bwd_state(dy, r, w, k, a, b, dhT=None, *, want_dv=True, want_dh0=True, dh_ckpt=None):
+def bwd_state(dy, r, w, k, a, b, chunk_inv, dhT=None, *, want_dv=True, want_dh0=True, dh_ckpt=None):
     """First backward stage: returns (dh_ckpt, dv, dh0); dh_ckpt[:, :, c] is the
     gradient w.r.t. checkpoint c."""
     import torch
@@ -172,20 +223,20 @@ def bwd_state(dy, r, w, k, a, b, dhT=None, *, want_dv=True, want_dh0=True, dh_ck
     dv = torch.empty((B, T, H, D), **f32) if want_dv else None
     dh0 = torch.empty((B, H, D, D), **f32) if want_dh0 else None
     st = lib().wkv7_bwd_state(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
-                              *map(_ptr, (r, w, k, a, b)), _ptr(dh_ckpt), _ptr(dv), _ptr(dh0),
+                              *map(_ptr, (r, w, k, a, b)), _ptr(chunk_inv), _ptr(dh_ckpt), _ptr(dv), _ptr(dh0),
                               _stream(r.device))
     _check("wkv7_bwd_state", st)
     return dh_ckpt, dv, dh0
 
 
-def bwd_inputs(dy, r, w, k, v, a, b, ckpt, dh_ckpt, dhT=None, *, out=None):
+def bwd_inputs(dy, r, w, k, v, a, b, chunk_inv, ckpt, dh_ckpt, dhT=None, *, out=None):
     """Second backward stage: returns (dr, dw, dk, da, db)."""
     import torch
     B, T, H, D = _shape(r)
     if out is None:
         out = [torch.empty((B, T, H, D), device=r.device, dtype=torch.float32) for _ in range(5)]
     st = lib().wkv7_bwd_inputs(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
-                               *map(_ptr, (r, w, k, v, a, b)), _ptr(ckpt), _ptr(dh_ckpt),
+                               *map(_ptr, (r, w, k, v, a, b)), _ptr(chunk_inv), _ptr(ckpt), _ptr(dh_ckpt),
                                *map(_ptr, out), _stream(r.device))
     _check("wkv7_bwd_inputs", st)
     return tuple(out)
@@ -201,20 +252,31 @@ def _make_autograd():
         def forward(ctx, r, w, k, v, a, b, h0=None):
             ins = [x.contiguous() for x in (r, w, k, v, a, b)]
             h0c = None if h0 is None else h0.contiguous().float()
-            y, ckpt, hT = fwd(*ins, h0c)
-            ctx.save_for_backward(*ins, ckpt)
+            T = ins[0].shape[1]
+            if T > 1:   # chunked path: one chunk inverse serves forward and backward
+                inv = chunk_inverse(ins[1], ins[4], ins[5])
+                y, ckpt, hT = fwd_chunks(*ins, inv, h0c)
+            else:
+                inv = None
+                y, ckpt, hT = fwd(*ins, h0c)
+            ctx.save_for_backward(*ins, ckpt, inv)
             ctx.has_h0 = h0 is not None
             return y, hT
 
         @staticmethod
         def backward(ctx, dy, dhT):
-            *ins, ckpt = ctx.saved_tensors
+            *ins, ckpt, inv = ctx.saved_tensors
             if dy is None:
                 dy = torch.zeros(ins[0].shape, dtype=torch.float32, device=ins[0].device)
             else:
                 dy = dy.contiguous().float()
             dhT = None if dhT is None else dhT.contiguous().float()
-            dr, dw, dk, dv, da, db, dh0 = bwd(dy, *ins, ckpt, dhT)
+            if inv is None:
+                dr, dw, dk, dv, da, db, dh0 = bwd(dy, *ins, ckpt, dhT)
+            else:
+                r, w, k, v, a, b = ins
+                dh_ck, dv, dh0 = bwd_state(dy, r, w, k, a, b, inv, dhT)
+                dr, dw, dk, da, db = bwd_inputs(dy, r, w, k, v, a, b, inv, ckpt, dh_ck, dhT)
             cast = lambda g, x: g.to(x.dtype)
             grads = [cast(g, x) for g, x in zip((dr, dw, dk, dv, da, db), ins)]
             return (*grads, dh0 if ctx.has_h0 else None)

@@ -110,13 +110,35 @@ wkv7_status check_fwd(int B, int T, int H, int D, wkv7_dtype dt, const void* r, 
 }
 
 wkv7::FwdArgs fwd_args(int B, int T, int H, const Sizes& sz, const void* r, const void* w,
-                       const void* k, const void* v, const void* a, const void* b, const float* h0,
-                       float* y, float* ckpt, float* hT) {
+                       const void* k, const void* v, const void* a, const void* b, const float* inv,
+                       const float* h0, float* y, float* ckpt, float* hT) {
     wkv7::FwdArgs fa;
     fa.r = r; fa.w = w; fa.k = k; fa.v = v; fa.a = a; fa.b = b;
-    fa.h0 = h0; fa.y = y; fa.ckpt = ckpt; fa.hT = hT;
+    fa.inv = inv; fa.h0 = h0; fa.y = y; fa.ckpt = ckpt; fa.hT = hT;
     fa.B = B; fa.T = T; fa.H = H; fa.NC = (int)sz.nc;
     return fa;
+}
+
+wkv7::BwdArgs bwd_args(int B, int T, int H, const Sizes& sz, const float* dy, const float* dhT,
+                       const void* r, const void* w, const void* k, const void* v, const void* a,
+                       const void* b, const float* inv, const float* h_ckpt, float* dh_ckpt) {
+    wkv7::BwdArgs ba = {};
+    ba.r = r; ba.w = w; ba.k = k; ba.v = v; ba.a = a; ba.b = b; ba.inv = inv;
+    ba.dy = dy; ba.dhT = dhT; ba.ckpt = h_ckpt; ba.gbuf = dh_ckpt;
+    ba.B = B; ba.T = T; ba.H = H; ba.NC = (int)sz.nc;
+    return ba;
+}
+
+wkv7_status status_of(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP; }
+
+int64_t inv_bytes(const Sizes& sz) { return sz.heads * sz.nc * kChunk * kChunk * 4; }
+
+wkv7_status launch_inverse(int B, int T, int H, const Sizes& sz, bool bf16, const void* w, const void* a,
+                           const void* b, float* inv, hipStream_t s) {
+    wkv7::InvArgs ia;
+    ia.w = w; ia.a = a; ia.b = b; ia.inv = inv;
+    ia.B = B; ia.T = T; ia.H = H; ia.NC = (int)sz.nc;
+    return status_of(wkv7::launch_chunk_inv(ia, bf16, s));
 }
 
 }  // namespace
@@ -143,24 +165,85 @@ const char* wkv7_status_str(int status) {
     }
 }
 
+size_t wkv7_chunk_inv_bytes(int B, int T, int H, int D) {
+    Sizes sz;
+    if (check_shape(B, T, H, D, &sz) != WKV7_OK) return 0;
+    return (size_t)inv_bytes(sz);
+}
+
+size_t wkv7_fwd_workspace_bytes(int B, int T, int H, int D) {
+    Sizes sz;
+    if (check_shape(B, T, H, D, &sz) != WKV7_OK) return 0;
+    return T <= kSequentialMaxT ? 0 : (size_t)inv_bytes(sz);
+}
+
 size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int D) {
     Sizes sz;
     if (check_shape(B, T, H, D, &sz) != WKV7_OK) return 0;
-    return (size_t)sz.ckpt_elems * sizeof(float);
+    return (size_t)(sz.ckpt_elems * 4 + inv_bytes(sz));
+}
+
+wkv7_status wkv7_chunk_inverse(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* w, const void* a,
+                               const void* b, float* chunk_inv, void* stream) {
+    wkv7_status st = check_dtype(in_dtype);
+    if (st != WKV7_OK) return st;
+    Sizes sz;
+    st = check_shape(B, T, H, D, &sz);
+    if (st != WKV7_OK) return st;
+    const int64_t tin = sz.tok_elems * elem_size(in_dtype);
+    const Buf bufs[4] = {{w, tin, true, false}, {a, tin, true, false}, {b, tin, true, false},
+                         {chunk_inv, inv_bytes(sz), true, true}};
+    st = check_bufs(bufs, 4);
+    if (st != WKV7_OK) return st;
+    st = check_alias(bufs, 4);
+    if (st != WKV7_OK) return st;
+    return launch_inverse(B, T, H, sz, in_dtype == WKV7_BF16, w, a, b, chunk_inv, static_cast<hipStream_t>(stream));
+}
+
+wkv7_status wkv7_fwd_chunks(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
+                            const void* k, const void* v, const void* a, const void* b, const float* chunk_inv,
+                            const float* h0, float* y, float* h_ckpt, float* hT, void* stream) {
+    Sizes sz;
+    wkv7_status st = check_fwd(B, T, H, D, in_dtype, r, w, k, v, a, b, h0, y, h_ckpt, hT, &sz);
+    if (st != WKV7_OK) return st;
+    const Buf bufs[4] = {{chunk_inv, inv_bytes(sz), true, false}, {y, sz.tok_elems * 4, false, true},
+                         {h_ckpt, sz.ckpt_elems * 4, false, true}, {hT, sz.state_elems * 4, false, true}};
+    st = check_bufs(bufs, 4);
+    if (st != WKV7_OK) return st;
+    st = check_alias(bufs, 4);
+    if (st != WKV7_OK) return st;
+    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, chunk_inv, h0, y, h_ckpt, hT);
+    return status_of(wkv7::launch_fwd_chunked(fa, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
 }
 
 wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
                      const void* k, const void* v, const void* a, const void* b, const float* h0,
-                     float* y, float* h_ckpt, float* hT, void* stream) {
+                     float* y, float* h_ckpt, float* hT, void* workspace, size_t workspace_bytes,
+                     void* stream) {
     Sizes sz;
     wkv7_status st = check_fwd(B, T, H, D, in_dtype, r, w, k, v, a, b, h0, y, h_ckpt, hT, &sz);
     if (st != WKV7_OK) return st;
-    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, h0, y, h_ckpt, hT);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = in_dtype == WKV7_BF16;
-    const hipError_t e = T <= kSequentialMaxT ? wkv7::launch_fwd_sequential(fa, bf16, s)
-                                              : wkv7::launch_fwd_chunked(fa, bf16, s);
-    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+    if (T <= kSequentialMaxT) {
+        const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, nullptr, h0, y, h_ckpt, hT);
+        return status_of(wkv7::launch_fwd_sequential(fa, bf16, s));
+    }
+    if (workspace && !aligned16(workspace)) return WKV7_ERR_ALIGN;
+    if (!workspace || workspace_bytes < (size_t)inv_bytes(sz)) return WKV7_ERR_WORKSPACE;
+    const int64_t tin = sz.tok_elems * elem_size(in_dtype);
+    const Buf bufs[11] = {{r, tin, true, false},   {w, tin, true, false},  {k, tin, true, false},
+                          {v, tin, true, false},   {a, tin, true, false},  {b, tin, true, false},
+                          {h0, sz.state_elems * 4, false, false},
+                          {y, sz.tok_elems * 4, false, true}, {h_ckpt, sz.ckpt_elems * 4, false, true},
+                          {hT, sz.state_elems * 4, false, true}, {workspace, inv_bytes(sz), true, true}};
+    st = check_alias(bufs, 11, h0, hT);
+    if (st != WKV7_OK) return st;
+    float* inv = static_cast<float*>(workspace);
+    st = launch_inverse(B, T, H, sz, bf16, w, a, b, inv, s);
+    if (st != WKV7_OK) return st;
+    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, inv, h0, y, h_ckpt, hT);
+    return status_of(wkv7::launch_fwd_chunked(fa, bf16, s));
 }
 
 wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r,
@@ -170,45 +253,30 @@ wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype,
     Sizes sz;
     wkv7_status st = check_fwd(B, T, H, D, in_dtype, r, w, k, v, a, b, h0, y, h_ckpt, hT, &sz);
     if (st != WKV7_OK) return st;
-    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, h0, y, h_ckpt, hT);
-    const hipError_t e = wkv7::launch_fwd_sequential(fa, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, nullptr, h0, y, h_ckpt, hT);
+    return status_of(wkv7::launch_fwd_sequential(fa, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
 }
-
-namespace {
-
-wkv7::BwdArgs bwd_args(int B, int T, int H, const Sizes& sz, const float* dy, const float* dhT,
-                       const void* r, const void* w, const void* k, const void* v, const void* a,
-                       const void* b, const float* h_ckpt, float* dh_ckpt) {
-    wkv7::BwdArgs ba = {};
-    ba.r = r; ba.w = w; ba.k = k; ba.v = v; ba.a = a; ba.b = b;
-    ba.dy = dy; ba.dhT = dhT; ba.ckpt = h_ckpt; ba.gbuf = dh_ckpt;
-    ba.B = B; ba.T = T; ba.H = H; ba.NC = (int)sz.nc;
-    return ba;
-}
-
-wkv7_status status_of(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP; }
-
-}  // namespace
 
 wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy,
                            const float* dhT, const void* r, const void* w, const void* k, const void* a,
-                           const void* b, float* dh_ckpt, float* dv, float* dh0, void* stream) {
+                           const void* b, const float* chunk_inv, float* dh_ckpt, float* dv, float* dh0,
+                           void* stream) {
     wkv7_status st = check_dtype(in_dtype);
     if (st != WKV7_OK) return st;
     Sizes sz;
     st = check_shape(B, T, H, D, &sz);
     if (st != WKV7_OK) return st;
     const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
-    const Buf bufs[10] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
+    const Buf bufs[11] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
                           {w, tin, true, false},  {k, tin, true, false},    {a, tin, true, false},
-                          {b, tin, true, false},  {dh_ckpt, sz.ckpt_elems * 4, true, true},
-                          {dv, t32, false, true}, {dh0, s32, false, true}};
-    st = check_bufs(bufs, 10);
+                          {b, tin, true, false},  {chunk_inv, inv_bytes(sz), true, false},
+                          {dh_ckpt, sz.ckpt_elems * 4, true, true}, {dv, t32, false, true},
+                          {dh0, s32, false, true}};
+    st = check_bufs(bufs, 11);
     if (st != WKV7_OK) return st;
-    st = check_alias(bufs, 10);
+    st = check_alias(bufs, 11);
     if (st != WKV7_OK) return st;
-    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, nullptr, a, b, nullptr, dh_ckpt);
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, nullptr, a, b, chunk_inv, nullptr, dh_ckpt);
     ba.dv = dv;
     ba.dh0 = dh0;
     return status_of(wkv7::launch_bwd_state(ba, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
@@ -216,8 +284,9 @@ wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype, cons
 
 wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy,
                             const float* dhT, const void* r, const void* w, const void* k, const void* v,
-                            const void* a, const void* b, const float* h_ckpt, const float* dh_ckpt,
-                            float* dr, float* dw, float* dk, float* da, float* db, void* stream) {
+                            const void* a, const void* b, const float* chunk_inv, const float* h_ckpt,
+                            const float* dh_ckpt, float* dr, float* dw, float* dk, float* da, float* db,
+                            void* stream) {
     wkv7_status st = check_dtype(in_dtype);
     if (st != WKV7_OK) return st;
     Sizes sz;
@@ -225,16 +294,18 @@ wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype, con
     if (st != WKV7_OK) return st;
     const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
     const int64_t c32 = sz.ckpt_elems * 4;
-    const Buf bufs[15] = {{dy, t32, true, false},  {dhT, s32, false, false}, {r, tin, true, false},
+    const Buf bufs[16] = {{dy, t32, true, false},  {dhT, s32, false, false}, {r, tin, true, false},
                           {w, tin, true, false},   {k, tin, true, false},    {v, tin, true, false},
-                          {a, tin, true, false},   {b, tin, true, false},    {h_ckpt, c32, true, false},
-                          {dh_ckpt, c32, true, false}, {dr, t32, true, true}, {dw, t32, true, true},
-                          {dk, t32, true, true},   {da, t32, true, true},    {db, t32, true, true}};
-    st = check_bufs(bufs, 15);
+                          {a, tin, true, false},   {b, tin, true, false},    {chunk_inv, inv_bytes(sz), true, false},
+                          {h_ckpt, c32, true, false}, {dh_ckpt, c32, true, false}, {dr, t32, true, true},
+                          {dw, t32, true, true},   {dk, t32, true, true},    {da, t32, true, true},
+                          {db, t32, true, true}};
+    st = check_bufs(bufs, 16);
     if (st != WKV7_OK) return st;
-    st = check_alias(bufs, 15);
+    st = check_alias(bufs, 16);
     if (st != WKV7_OK) return st;
-    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, h_ckpt, const_cast<float*>(dh_ckpt));
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, chunk_inv, h_ckpt,
+                                const_cast<float*>(dh_ckpt));
     ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.da = da; ba.db = db;
     return status_of(wkv7::launch_bwd_inputs(ba, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
 }
@@ -251,22 +322,26 @@ wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const floa
     if (st != WKV7_OK) return st;
     const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
     const int64_t c32 = sz.ckpt_elems * 4;
+    const int64_t need = c32 + inv_bytes(sz);
     const Buf bufs[17] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
                           {w, tin, true, false},  {k, tin, true, false},    {v, tin, true, false},
                           {a, tin, true, false},  {b, tin, true, false},    {h_ckpt, c32, true, false},
                           {dr, t32, true, true},  {dw, t32, true, true},    {dk, t32, true, true},
                           {dv, t32, true, true},  {da, t32, true, true},    {db, t32, true, true},
-                          {dh0, s32, false, true}, {workspace, c32, false, true}};
+                          {dh0, s32, false, true}, {workspace, need, false, true}};
     st = check_bufs(bufs, 17);
     if (st != WKV7_OK) return st;
-    if (!workspace || workspace_bytes < (size_t)c32) return WKV7_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < (size_t)need) return WKV7_ERR_WORKSPACE;
     st = check_alias(bufs, 17);
     if (st != WKV7_OK) return st;
     float* gbuf = static_cast<float*>(workspace);
-    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, h_ckpt, gbuf);
-    ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.dv = dv; ba.da = da; ba.db = db; ba.dh0 = dh0;
+    float* inv = gbuf + sz.ckpt_elems;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = in_dtype == WKV7_BF16;
+    st = launch_inverse(B, T, H, sz, bf16, w, a, b, inv, s);
+    if (st != WKV7_OK) return st;
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, inv, h_ckpt, gbuf);
+    ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.dv = dv; ba.da = da; ba.db = db; ba.dh0 = dh0;
     hipError_t e = wkv7::launch_bwd_state(ba, bf16, s);
     if (e == hipSuccess) e = wkv7::launch_bwd_inputs(ba, bf16, s);
     return status_of(e);

@@ -8,23 +8,24 @@
 // does not involve the forward state, so it is a pass of its own:
 //
 // Kernel 1 (state gradient, one workgroup per head row block, chunks in
-// reverse).  With G = dL/dS at the chunk's end and the chunk matrices of
-// wkv7_device.h, Bbar = Btil diag(gamma_last), Kbar = Ktil diag(gamma_last):
-//     DSA     = (I - Lab)^-T (Bbar G^T + Mrb^T DY)        dsa_t = X_t b_t
-//     dv      = Kbar G^T + Lak^T DSA + Mrk^T DY            dv_t  = X_t k_t
-//     G_start = G diag(gamma_last) + DY^T Rhat + DSA^T Ahat
-// G_start (the gradient w.r.t. the state entering the chunk) goes to the
-// workspace; after chunk 0 it is dh0.  Rows of G are independent.
+// reverse).  With G = dL/dS at the chunk's end, G' = G diag(gamma_last) and
+// the chunk matrices of wkv7_device.h:
+//     DSA     = (I - Lab)^-T (Btil G'^T + Mrb^T DY)       dsa_t = X_t b_t
+//     dv      = Ktil G'^T + Lak^T DSA + Mrk^T DY            dv_t  = X_t k_t
+//     G_start = G' + DY^T Rhat + DSA^T Ahat
+// G_start (the gradient w.r.t. the state entering the chunk) goes to
+// dh_ckpt; after chunk 0 it is dh0.  Rows of G are independent.
 //
 // Kernel 2 (one workgroup per (head, chunk), all chunks at once).  From the
-// checkpoint S0 and the end gradient Ge it recomputes U (= sa_t) as in the
-// forward -- never by dividing the state by w -- and DSA as in kernel 1, then
-//     dr = Gamma     * (DY S0  + tril(DY U^T) Btil  + tril(DY V^T) Ktil)
-//     da = Gamma_-1  * (DSA S0 + stril(DSA U^T) Btil + stril(DSA V^T) Ktil)
-//     dk = Gamma^-1  * (V Ge gamma_last + striu(V DSA^T) Ahat + triu(V DY^T) Rhat)
-//     db = Gamma^-1  * (U Ge gamma_last + striu(U DSA^T) Ahat + triu(U DY^T) Rhat)
-// and dw from the identity (exact in real arithmetic, derived from the
-// update rule): with phi_t = w_t * dw_t and Gs = dL/dS0,
+// checkpoint S0 and the end gradient Ge (Ge' = Ge diag(gamma_last)) it
+// recomputes U (= sa_t) as in the forward -- never by dividing the state by
+// w -- and DSA as in kernel 1, then
+//     dr = Gamma    * (DY S0  + tril(DY U^T) Btil   + tril(DY V^T) Ktil)
+//     da = Gamma_-1 * (DSA S0 + stril(DSA U^T) Btil + stril(DSA V^T) Ktil)
+//     dk = Gamma^-1 * (V Ge'  + striu(V DSA^T) Ahat + triu(V DY^T) Rhat)
+//     db = Gamma^-1 * (U Ge'  + striu(U DSA^T) Ahat + triu(U DY^T) Rhat)
+// and dw from an identity that follows from the update rule: with
+// phi_t = w_t * dw_t and Gs = dL/dS0,
 //     phi_t = sum_i Gs[i][j] S0[i][j] - sum_{s<=t} a_s da_s
 //             + sum_{s<t} (k_s dk_s + b_s db_s - r_s dr_s),
 //     dw_t  = phi_t / w_t.
@@ -35,35 +36,41 @@ namespace wkv7 {
 namespace {
 
 // ------------------------------------------------------------- kernel 1
-template <int RB>
-struct StateLayout {
-    static constexpr int W = 0;
-    static constexpr int A = W + C * LDA;
-    static constexpr int R = A + C * LDA;
-    static constexpr int Bt = R + C * LDA;
-    static constexpr int Kt = Bt + C * LDA;
-    static constexpr int G = Kt + C * LDA;       // RB x LDA (i, j)
-    static constexpr int DYT = G + RB * LDA;     // RB x LDC (i, t)
-    static constexpr int Lab = DYT + RB * LDC;
-    static constexpr int Lak = Lab + C * LDC;
-    static constexpr int Mrb = Lak + C * LDC;
-    static constexpr int Mrk = Mrb + C * LDC;
-    static constexpr int Tinv = Mrk + C * LDC;
-    static constexpr int RhsT = Tinv + C * LDC;  // RB x LDC (i, t)
-    static constexpr int DsaT = RhsT + RB * LDC; // RB x LDC (i, t)
-    static constexpr int glast = DsaT + RB * LDC;
-    static constexpr int qp = glast + D;
-    static constexpr int total = qp + 8 * D;
-    static constexpr size_t bytes = total * sizeof(float);
+template <bool SPLIT, int RB>
+struct StateSmem {
+    using F = Fmt<SPLIT>;
+    static constexpr int A = 0;                          // Ahat rows (t, j)
+    static constexpr int R = A + F::bytes(C, D);         // Rhat rows
+    static constexpr int Bm = R + F::bytes(C, D);        // Btil rows
+    static constexpr int Km = Bm + F::bytes(C, D);       // Ktil rows
+    static constexpr int AT = Km + F::bytes(C, D);       // Ahat^T (j, t)
+    static constexpr int RT = AT + F::bytes(D, C);       // Rhat^T (j, t)
+    static constexpr int G = RT + F::bytes(D, C);        // G' rows (i, j)
+    static constexpr int DYT = G + F::bytes(RB, D);      // dy^T (i, t)
+    static constexpr int LakT = DYT + F::bytes(RB, C);   // (t, s) = Lak[s][t]
+    static constexpr int MrbT = LakT + F::bytes(C, C);
+    static constexpr int MrkT = MrbT + F::bytes(C, C);
+    static constexpr int TinvT = MrkT + F::bytes(C, C);
+    static constexpr int Rhs2T = TinvT + F::bytes(C, C);  // (i, t)
+    static constexpr int DsaT = Rhs2T + F::bytes(RB, C);  // (i, t)
+    static constexpr int glast = DsaT + F::bytes(RB, C);
+    static constexpr int qp = glast + D * 4;
+    static constexpr int total = qp + 8 * D * 4;
 };
 
 template <typename InT, bool SPLIT, int RB, int NT>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs p, int xcd) {
-    extern __shared__ float sm[];
-    using L = StateLayout<RB>;
+    static_assert(NT == 256, "one raw-chunk thread shape");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using L = StateSmem<SPLIT, RB>;
+    using M = Mat<SPLIT>;
     constexpr int NW = NT / 64;
     constexpr int NRB = D / RB;
+    constexpr int NTILE = 2 * (RB / 16);
+    constexpr int NGT = (RB / 16) * 4;
+    constexpr int NPER = (NGT + NW - 1) / NW;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
 
     int head, rb;
     block_map(blockIdx.x, NRB, xcd != 0, head, rb);
@@ -72,153 +79,241 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs p, int xcd) {
     const int64_t tstride = (int64_t)p.H * D;
     const int64_t soff = (int64_t)head * D * D + (int64_t)row0 * D;
 
-    float* W = sm + L::W;
-    float* A = sm + L::A;
-    float* R = sm + L::R;
-    float* Bt = sm + L::Bt;
-    float* Kt = sm + L::Kt;
-    float* G = sm + L::G;
-    float* DYT = sm + L::DYT;
-    float* Lab = sm + L::Lab;
-    float* Lak = sm + L::Lak;
-    float* Mrb = sm + L::Mrb;
-    float* Mrk = sm + L::Mrk;
-    float* Tinv = sm + L::Tinv;
-    float* RhsT = sm + L::RhsT;
-    float* DsaT = sm + L::DsaT;
-    float* glast = sm + L::glast;
-    float* qp = sm + L::qp;
+    const InT* gr = static_cast<const InT*>(p.r);
+    const InT* gw = static_cast<const InT*>(p.w);
+    const InT* gk = static_cast<const InT*>(p.k);
+    const InT* ga = static_cast<const InT*>(p.a);
+    const InT* gb = static_cast<const InT*>(p.b);
 
-    load_state_rows<NT, RB>(p.dhT ? p.dhT + soff : nullptr, G, tid);
+    const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
+    const M Bm = make_mat<SPLIT>(smem, L::Bm, C, D), Km = make_mat<SPLIT>(smem, L::Km, C, D);
+    const M AT = make_mat<SPLIT>(smem, L::AT, D, C), RT = make_mat<SPLIT>(smem, L::RT, D, C);
+    const M G = make_mat<SPLIT>(smem, L::G, RB, D), DYT = make_mat<SPLIT>(smem, L::DYT, RB, C);
+    const M LakT = make_mat<SPLIT>(smem, L::LakT, C, C), MrbT = make_mat<SPLIT>(smem, L::MrbT, C, C);
+    const M MrkT = make_mat<SPLIT>(smem, L::MrkT, C, C), TinvT = make_mat<SPLIT>(smem, L::TinvT, C, C);
+    const M Rhs2T = make_mat<SPLIT>(smem, L::Rhs2T, RB, C), DsaT = make_mat<SPLIT>(smem, L::DsaT, RB, C);
+    float* glast = reinterpret_cast<float*>(smem + L::glast);
+    float* qp = reinterpret_cast<float*>(smem + L::qp);
+
+    const PrepOut<SPLIT> po{A, R, Bm, Km, AT, RT, A, A, true, true, true, true, true, true, false, false,
+                            nullptr, glast};
+    const CcOut<SPLIT, NT> co{nullptr, LakT, LakT, MrbT, MrbT, MrkT, MrkT, false, true, false, true, false, true};
+
+    // wave-owned gradient tiles, from dhT
+    f32x4 gt[NPER];
+#pragma unroll
+    for (int q2 = 0; q2 < NPER; ++q2) {
+        const int job = wave + q2 * NW;
+        if (job < NGT) {
+            const int tm = job >> 2, tn = job & 3;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                gt[q2][q] = p.dhT ? p.dhT[soff + (tm * 16 + 4 * g4 + q) * D + tn * 16 + r16] : 0.f;
+        }
+    }
+
+    RawChunk<NT, InT> raw;
+    RawCols<NT, RB, float> rdy;
+    f32x4 tv;   // four entries of the chunk's (I - Lab)^-1: row tid/8, columns 4*(tid%8)..
+    const float* ginv = p.inv + (int64_t)head * p.NC * C * C + tid * 4;
+    {
+        const int c = p.NC - 1;
+        const int Cc = min(C, p.T - c * C);
+        const int64_t base = ((int64_t)bb * p.T + c * C) * tstride + (int64_t)hh * D;
+        raw.load(gw, ga, gr, gb, gk, base, tstride, Cc, tid);
+        rdy.load(p.dy, base, tstride, Cc, row0, tid);
+        tv = *reinterpret_cast<const f32x4*>(ginv + (int64_t)c * C * C);
+    }
+
+    constexpr int NVPER = (NTILE + NW - 1) / NW;
+    f32x4 dvv[NVPER];
+    // Stores of one finished chunk cc: dv (tokens < vcc) and the state gradient
+    // entering it (registers gt) into dh_ckpt.
+    auto store_prev = [&](int64_t vbase_, int vcc_, int cc_) {
+        if (p.dv) {
+#pragma unroll
+            for (int q2 = 0; q2 < NVPER; ++q2) {
+                const int job = wave + q2 * NW;
+                if (job < NTILE) {
+                    const int ti = job & 1, tn = job >> 1;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int t = ti * 16 + 4 * g4 + q;
+                        if (t < vcc_) p.dv[vbase_ + t * tstride + row0 + tn * 16 + r16] = dvv[q2][q];
+                    }
+                }
+            }
+        }
+        float* gout = p.gbuf + ((int64_t)head * p.NC + cc_) * D * D + (int64_t)row0 * D;
+#pragma unroll
+        for (int q2 = 0; q2 < NPER; ++q2) {
+            const int job = wave + q2 * NW;
+            if (job < NGT) {
+                const int tm = job >> 2, tn = job & 3;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) gout[(tm * 16 + 4 * g4 + q) * D + tn * 16 + r16] = gt[q2][q];
+            }
+        }
+    };
+
+    // dv and the state gradient of a chunk are stored at the start of the next
+    // iteration (no store between a prefetch and the wait for it)
+    int64_t vbase = 0;
+    int vCc = 0, cprev = 0;
 
     for (int c = p.NC - 1; c >= 0; --c) {
         const int t0 = c * C;
         const int Cc = min(C, p.T - t0);
         const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
-        __syncthreads();
-        load_chunk<InT, NT>(static_cast<const InT*>(p.w), base, tstride, Cc, 1.f, W, tid);
-        load_chunk<InT, NT>(static_cast<const InT*>(p.a), base, tstride, Cc, 0.f, A, tid);
-        load_chunk<InT, NT>(static_cast<const InT*>(p.r), base, tstride, Cc, 0.f, R, tid);
-        load_chunk<InT, NT>(static_cast<const InT*>(p.b), base, tstride, Cc, 0.f, Bt, tid);
-        load_chunk<InT, NT>(static_cast<const InT*>(p.k), base, tstride, Cc, 0.f, Kt, tid);
-        load_chunk_cols_T<float, NT, RB>(p.dy, base, tstride, Cc, row0, DYT, tid);
-        __syncthreads();
-        chunk_prep<NT>(W, A, R, Bt, Kt, glast, qp, tid);
 
-        chunk_cc<SPLIT, NT>(A, R, Bt, Kt, Lab, Lak, Mrb, Mrk, tid);
-        for (int e = tid; e < RB * D; e += NT) {
-            const int i = e >> 6, j = e & 63;
-            G[i * LDA + j] *= glast[j];  // G diag(gamma_last)
+        chunk_prep<NT, SPLIT>(raw, po, qp, tid);
+        rdy.template store_T<SPLIT, false>(DYT, tid);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) put(TinvT, (tid & 7) * 4 + q, tid >> 3, tv[q]);
+        if (c < p.NC - 1) store_prev(vbase, vCc, cprev);
+        {
+            const int cp = max(c - 1, 0);
+            const int64_t pbase = ((int64_t)bb * p.T + cp * C) * tstride + (int64_t)hh * D;
+            const int pCc = min(C, p.T - cp * C);
+            raw.load(gw, ga, gr, gb, gk, pbase, tstride, pCc, tid);
+            rdy.load(p.dy, pbase, tstride, pCc, row0, tid);
+            tv = *reinterpret_cast<const f32x4*>(ginv + (int64_t)cp * C * C);
         }
-        __syncthreads();
+        lds_barrier();
 
-        constexpr int NTILE = 2 * (RB / 16);
-        if (wave == NW - 1) tri_inverse(Lab, Tinv, lane);
-        if (NW == 1 || wave < NW - 1) {
-            const int nwk = NW == 1 ? 1 : NW - 1;
-            for (int job = wave; job < NTILE; job += nwk) {
+        chunk_cc<SPLIT, NT>(A, R, Bm, Km, co, tid);
+        f32x4 gs[NPER];   // G' = G diag(gamma_last)
+#pragma unroll
+        for (int q2 = 0; q2 < NPER; ++q2) {
+            const int job = wave + q2 * NW;
+            if (job < NGT) {
+                const int tm = job >> 2, tn = job & 3;
+                const float gl = glast[tn * 16 + r16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) gs[q2][q] = gt[q2][q] * gl;
+                store_rows<MASK_NONE>(G, gs[q2], tm * 16, tn * 16, lane);
+            }
+        }
+        lds_barrier();
+
+        for (int job = wave; job < NTILE; job += NW) {
+            const int ti = job & 1, tn = job >> 1;
+            f32x4 acc = mma<SPLIT, D>(zero4(), Bm, ti * 16, G, tn * 16, lane);
+            acc = mma<SPLIT, C>(acc, MrbT, ti * 16, DYT, tn * 16, lane);
+            store_cols<MASK_NONE>(Rhs2T, acc, ti * 16, tn * 16, lane);
+        }
+        lds_barrier();
+
+        for (int job = wave; job < NTILE; job += NW) {
+            const int ti = job & 1, tn = job >> 1;
+            const f32x4 acc = mma<SPLIT, C>(zero4(), TinvT, ti * 16, Rhs2T, tn * 16, lane);
+            store_cols<MASK_NONE>(DsaT, acc, ti * 16, tn * 16, lane);
+        }
+        lds_barrier();
+
+        // dv = Ktil G'^T + Lak^T DSA + Mrk^T DY
+#pragma unroll
+        for (int q2 = 0; q2 < NVPER; ++q2) {
+            const int job = wave + q2 * NW;
+            if (job < NTILE) {
                 const int ti = job & 1, tn = job >> 1;
-                f32x4 acc = mma<SPLIT, D>(zero4(), rows(Bt, LDA), ti * 16, rows(G, LDA), tn * 16, lane);
-                acc = mma<SPLIT, C>(acc, cols(Mrb, LDC), ti * 16, rows(DYT, LDC), tn * 16, lane);
-                store_tile<LDC, true, MASK_NONE>(RhsT, acc, ti * 16, tn * 16, lane);
+                f32x4 acc = mma<SPLIT, D>(zero4(), Km, ti * 16, G, tn * 16, lane);
+                acc = mma<SPLIT, C>(acc, LakT, ti * 16, DsaT, tn * 16, lane);
+                dvv[q2] = mma<SPLIT, C>(acc, MrkT, ti * 16, DYT, tn * 16, lane);
             }
         }
-        __syncthreads();
+        vbase = base;
+        vCc = Cc;
+        cprev = c;
 
-        for (int job = wave; job < NTILE; job += NW) {
-            const int ti = job & 1, tn = job >> 1;
-            const f32x4 acc = mma<SPLIT, C>(zero4(), cols(Tinv, LDC), ti * 16, rows(RhsT, LDC), tn * 16, lane);
-            store_tile<LDC, true, MASK_NONE>(DsaT, acc, ti * 16, tn * 16, lane);
-        }
-        __syncthreads();
-
-        // dv = Kbar G^T + Lak^T DSA + Mrk^T DY
-        for (int job = wave; job < NTILE; job += NW) {
-            const int ti = job & 1, tn = job >> 1;
-            f32x4 acc = mma<SPLIT, D>(zero4(), rows(Kt, LDA), ti * 16, rows(G, LDA), tn * 16, lane);
-            acc = mma<SPLIT, C>(acc, cols(Lak, LDC), ti * 16, rows(DsaT, LDC), tn * 16, lane);
-            acc = mma<SPLIT, C>(acc, cols(Mrk, LDC), ti * 16, rows(DYT, LDC), tn * 16, lane);
-            const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int t = ti * 16 + 4 * g + q;
-                if (t < Cc && p.dv) p.dv[base + t * tstride + row0 + tn * 16 + r] = acc[q];
-            }
-        }
-
-        // G <- G diag(gamma_last) + DY^T Rhat + DSA^T Ahat (G already scaled)
-        constexpr int NGTILE = (RB / 16) * 4;
-        constexpr int NPER = (NGTILE + NW - 1) / NW;
-        f32x4 gnew[NPER];
+        // G <- G' + DY^T Rhat + DSA^T Ahat
 #pragma unroll
         for (int q2 = 0; q2 < NPER; ++q2) {
             const int job = wave + q2 * NW;
-            if (job < NGTILE) {
+            if (job < NGT) {
                 const int tm = job >> 2, tn = job & 3;
-                const int r = lane & 15, g = lane >> 4;
-                f32x4 acc;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = G[(tm * 16 + 4 * g + q) * LDA + tn * 16 + r];
-                acc = mma<SPLIT, C>(acc, rows(DYT, LDC), tm * 16, cols(R, LDA), tn * 16, lane);
-                acc = mma<SPLIT, C>(acc, rows(DsaT, LDC), tm * 16, cols(A, LDA), tn * 16, lane);
-                gnew[q2] = acc;
+                f32x4 acc = mma<SPLIT, C>(gs[q2], DYT, tm * 16, RT, tn * 16, lane);
+                acc = mma<SPLIT, C>(acc, DsaT, tm * 16, AT, tn * 16, lane);
+                gt[q2] = acc;
             }
         }
-        __syncthreads();
-        float* gout = p.gbuf + ((int64_t)head * p.NC + c) * D * D + (int64_t)row0 * D;
-        float* dh0 = (c == 0 && p.dh0) ? p.dh0 + soff : nullptr;
+        lds_barrier();
+    }
+    store_prev(vbase, vCc, cprev);
+    if (p.dh0) {
 #pragma unroll
         for (int q2 = 0; q2 < NPER; ++q2) {
             const int job = wave + q2 * NW;
-            if (job < NGTILE) {
+            if (job < NGT) {
                 const int tm = job >> 2, tn = job & 3;
-                store_tile<LDA, false, MASK_NONE>(G, gnew[q2], tm * 16, tn * 16, lane);
-                const int r = lane & 15, g = lane >> 4;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t o = (int64_t)(tm * 16 + 4 * g + q) * D + tn * 16 + r;
-                    gout[o] = gnew[q2][q];
-                    if (dh0) dh0[o] = gnew[q2][q];
-                }
+                for (int q = 0; q < 4; ++q) p.dh0[soff + (tm * 16 + 4 * g4 + q) * D + tn * 16 + r16] = gt[q2][q];
             }
         }
     }
 }
 
 // ------------------------------------------------------------- kernel 2
-struct ChunkLayout {
-    static constexpr int W = 0;
-    static constexpr int A = W + C * LDA;
-    static constexpr int R = A + C * LDA;
-    static constexpr int Bt = R + C * LDA;
-    static constexpr int Kt = Bt + C * LDA;
-    static constexpr int V = Kt + C * LDA;      // (t, i)
-    static constexpr int DY = V + C * LDA;      // (t, i)
-    static constexpr int U = DY + C * LDA;      // (t, i)
-    static constexpr int DSA = U + C * LDA;     // (t, i)
-    static constexpr int S0 = DSA + C * LDA;    // D x LDA (i, j)
-    static constexpr int Ge = S0 + D * LDA;     // D x LDA (i, j)
-    static constexpr int P1 = Ge + D * LDA;     // C x LDC: Lab, then tril(DY U^T)
-    static constexpr int P2 = P1 + C * LDC;     //          Lak, then tril(DY V^T)
-    static constexpr int P3 = P2 + C * LDC;     //          Mrb, then stril(DSA U^T)
-    static constexpr int P4 = P3 + C * LDC;     //          Mrk, then stril(DSA V^T)
-    static constexpr int Tinv = P4 + C * LDC;
-    static constexpr int Hh = Tinv + C * LDC;   // C x LDA: k dk + b db - r dr - a da
-    static constexpr int Fa = Hh + C * LDA;     // C x LDA: a da
-    static constexpr int glast = Fa + C * LDA;
-    static constexpr int qp = glast + D;
-    static constexpr int red = qp + 8 * D;
-    static constexpr int total = red + 8 * D;
-    static constexpr size_t bytes = total * sizeof(float);
+// LDS plan (byte offsets).  Region X holds what phases 0-3 need; region Y
+// (phases 3-5) reuses region X's space once its contents are dead; region P
+// lives throughout.  See the phase comments in the kernel.
+template <bool SPLIT>
+struct ChunkSmem {
+    using F = Fmt<SPLIT>;
+    static constexpr int RM = F::bytes(C, D), TM = F::bytes(D, C), SM = F::bytes(D, D), CM = F::bytes(C, C);
+    static constexpr int F32C = C * LDF * 4;
+    // region X (phases 0-3)
+    static constexpr int XA = 0;                   // Ahat rows
+    static constexpr int XB = XA + RM;             // Btil rows
+    static constexpr int XR = XB + RM;             // Rhat rows   (dead after phase 1)
+    static constexpr int XK = XR + RM;             // Ktil rows   (dead after phase 1)
+    static constexpr int XVT = XK + RM;            // v^T (i, t)
+    static constexpr int XDYT = XVT + TM;          // dy^T (i, t)
+    static constexpr int XS0 = XDYT + TM;          // S0 rows (i, j)
+    static constexpr int XGe = XS0 + SM;           // Ge' rows (i, j)
+    static constexpr int XLak = XGe + SM;          // Lak rows (t, s)
+    static constexpr int XMrbT = XLak + CM;        // Mrb^T (t, s)
+    static constexpr int XRhsUT = XMrbT + CM;      // (i, t)
+    static constexpr int XRhsDT = XRhsUT + TM;     // (i, t)
+    static constexpr int XEND = XRhsDT + TM;
+    // (I - Lab)^-1, rows and transposed, written in phase 2 over Rhat/Ktil
+    static constexpr int XTinv = XR;               // (t, s)
+    static constexpr int XTinvT = XTinv + CM;      // (t, s) = Tinv[s][t]
+    static_assert(XTinvT + CM <= XVT, "inverse overflows Rhat/Ktil");
+    // region Y (phases 3-5)
+    static constexpr int YU = 0;                   // U rows (t, i)       over XA
+    static constexpr int YDSA = YU + RM;           // DSA rows (t, i)     over XB
+    static constexpr int YP = YDSA + RM;           // P1..P4 rows, then P1T..P4T
+    static constexpr int YS0T = YP + 8 * CM;       // half S0^T (j', i)
+    static constexpr int YGeT = YS0T + F::bytes(32, D);
+    static constexpr int YAT = YGeT + F::bytes(32, D);  // half Ahat^T (j', t)
+    static constexpr int YRT = YAT + F::bytes(32, C);
+    static constexpr int YBT = YRT + F::bytes(32, C);
+    static constexpr int YKT = YBT + F::bytes(32, C);
+    static constexpr int YHh = YKT + F::bytes(32, C);   // fp32 C x LDG
+    static constexpr int YFa = YHh + C * LDG * 4;
+    static constexpr int YEND = YFa + C * LDG * 4;
+    static_assert(YP >= XA + 2 * RM, "U/DSA must not overlap live phase-3 data");
+    // region P
+    static constexpr int P0 = (XEND > YEND ? XEND : YEND);
+    static constexpr int Gam = P0;                 // fp32 gamma [t][j]
+    static constexpr int DYr = Gam + C * LDG * 4;  // dy rows (t, i)
+    static constexpr int Vr = DYr + RM;            // v rows (t, i)
+    static constexpr int glast = Vr + RM;
+    static constexpr int qp = glast + D * 4;
+    static constexpr int red = qp + 8 * D * 4;
+    static constexpr int total = red + 4 * D * 4;
 };
-static_assert(ChunkLayout::bytes <= 160 * 1024, "chunk kernel LDS exceeds 160 KiB");
 
 template <typename InT, bool SPLIT, int NT>
 __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdArgs p, int xcd) {
-    extern __shared__ float sm[];
-    using L = ChunkLayout;
+    static_assert(NT == 256, "one raw-chunk thread shape");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using L = ChunkSmem<SPLIT>;
+    using M = Mat<SPLIT>;
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
 
     int head, c;
     block_map(blockIdx.x, p.NC, xcd != 0, head, c);
@@ -229,184 +324,254 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdArgs p, int xcd) {
     const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
     const int64_t hoff = (int64_t)head * D * D;
 
-    float* W = sm + L::W;
-    float* A = sm + L::A;
-    float* R = sm + L::R;
-    float* Bt = sm + L::Bt;
-    float* Kt = sm + L::Kt;
-    float* V = sm + L::V;
-    float* DY = sm + L::DY;
-    float* U = sm + L::U;
-    float* DSA = sm + L::DSA;
-    float* S0 = sm + L::S0;
-    float* Ge = sm + L::Ge;
-    float* P1 = sm + L::P1;
-    float* P2 = sm + L::P2;
-    float* P3 = sm + L::P3;
-    float* P4 = sm + L::P4;
-    float* Tinv = sm + L::Tinv;
-    float* Hh = sm + L::Hh;
-    float* Fa = sm + L::Fa;
-    float* glast = sm + L::glast;
-    float* qp = sm + L::qp;
-    float* red = sm + L::red;
+    const InT* gw = static_cast<const InT*>(p.w);
 
-    load_chunk<InT, NT>(static_cast<const InT*>(p.w), base, tstride, Cc, 1.f, W, tid);
-    load_chunk<InT, NT>(static_cast<const InT*>(p.a), base, tstride, Cc, 0.f, A, tid);
-    load_chunk<InT, NT>(static_cast<const InT*>(p.r), base, tstride, Cc, 0.f, R, tid);
-    load_chunk<InT, NT>(static_cast<const InT*>(p.b), base, tstride, Cc, 0.f, Bt, tid);
-    load_chunk<InT, NT>(static_cast<const InT*>(p.k), base, tstride, Cc, 0.f, Kt, tid);
-    load_chunk<InT, NT>(static_cast<const InT*>(p.v), base, tstride, Cc, 0.f, V, tid);
-    load_chunk<float, NT>(p.dy, base, tstride, Cc, 0.f, DY, tid);
-    load_state_rows<NT, D>(p.ckpt + ((int64_t)head * p.NC + c) * D * D, S0, tid);
-    const float* ge_src = (c + 1 < p.NC) ? p.gbuf + ((int64_t)head * p.NC + c + 1) * D * D
-                                         : (p.dhT ? p.dhT + hoff : nullptr);
-    load_state_rows<NT, D>(ge_src, Ge, tid);
-    __syncthreads();
-    chunk_prep<NT>(W, A, R, Bt, Kt, glast, qp, tid);
-
-    chunk_cc<SPLIT, NT>(A, R, Bt, Kt, P1, P2, P3, P4, tid);  // Lab, Lak, Mrb, Mrk
-    for (int e = tid; e < D * D; e += NT) {
-        const int i = e >> 6, j = e & 63;
-        Ge[i * LDA + j] *= glast[j];
+    // ---- phase 0: loads and chunk preparation
+    RawChunk<NT, InT> raw;
+    raw.load(gw, static_cast<const InT*>(p.a), static_cast<const InT*>(p.r), static_cast<const InT*>(p.b),
+             static_cast<const InT*>(p.k), base, tstride, Cc, tid);
+    RawCols<NT, D, InT> rv;
+    RawCols<NT, D, float> rdy;
+    rv.load(static_cast<const InT*>(p.v), base, tstride, Cc, 0, tid);
+    rdy.load(p.dy, base, tstride, Cc, 0, tid);
+    // four entries of the chunk's (I - Lab)^-1: row tid/8, columns 4*(tid%8)..
+    const f32x4 tv = *reinterpret_cast<const f32x4*>(p.inv + ((int64_t)head * p.NC + c) * C * C + tid * 4);
+    // state-sized inputs: thread holds row si = tid/4, columns sj0 .. sj0+15
+    const int si = tid >> 2, sj0 = (tid & 3) * 16;
+    const float* s0g = p.ckpt + ((int64_t)head * p.NC + c) * D * D;
+    const float* geg = (c + 1 < p.NC) ? p.gbuf + ((int64_t)head * p.NC + c + 1) * D * D
+                                      : (p.dhT ? p.dhT + hoff : nullptr);
+    f32x4 s0v[4], gev[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        s0v[q] = *reinterpret_cast<const f32x4*>(s0g + si * D + sj0 + 4 * q);
+        gev[q] = geg ? *reinterpret_cast<const f32x4*>(geg + si * D + sj0 + 4 * q) : zero4();
     }
-    __syncthreads();
+    // partial sums of diag(Gs^T S0): thread column rj, rows 16*rgrp .. +15
+    {
+        const float* gsg = p.gbuf + ((int64_t)head * p.NC + c) * D * D;
+        const int rj = tid & 63, rgrp = tid >> 6;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = rgrp * 16 + i;
+            acc = fmaf(gsg[row * D + rj], s0g[row * D + rj], acc);
+        }
+        reinterpret_cast<float*>(smem + L::red)[rgrp * 64 + rj] = acc;
+    }
 
-    // Right-hand sides: U buffer <- Ahat S0^T + Lak V, DSA buffer <- Bbar Ge^T + Mrb^T DY.
-    if (wave == NW - 1) tri_inverse(P1, Tinv, lane);
-    if (NW == 1 || wave < NW - 1) {
-        const int nwk = NW == 1 ? 1 : NW - 1;
-        for (int job = wave; job < 16; job += nwk) {
+    const M XA = make_mat<SPLIT>(smem, L::XA, C, D), XB = make_mat<SPLIT>(smem, L::XB, C, D);
+    const M XR = make_mat<SPLIT>(smem, L::XR, C, D), XK = make_mat<SPLIT>(smem, L::XK, C, D);
+    const M XVT = make_mat<SPLIT>(smem, L::XVT, D, C), XDYT = make_mat<SPLIT>(smem, L::XDYT, D, C);
+    const M XS0 = make_mat<SPLIT>(smem, L::XS0, D, D), XGe = make_mat<SPLIT>(smem, L::XGe, D, D);
+    const M XLak = make_mat<SPLIT>(smem, L::XLak, C, C), XMrbT = make_mat<SPLIT>(smem, L::XMrbT, C, C);
+    const M XRhsUT = make_mat<SPLIT>(smem, L::XRhsUT, D, C), XRhsDT = make_mat<SPLIT>(smem, L::XRhsDT, D, C);
+    const M XTinv = make_mat<SPLIT>(smem, L::XTinv, C, C), XTinvT = make_mat<SPLIT>(smem, L::XTinvT, C, C);
+    float* gam = reinterpret_cast<float*>(smem + L::Gam);
+    const M DYr = make_mat<SPLIT>(smem, L::DYr, C, D), Vr = make_mat<SPLIT>(smem, L::Vr, C, D);
+    float* glast = reinterpret_cast<float*>(smem + L::glast);
+    float* qp = reinterpret_cast<float*>(smem + L::qp);
+    float* red = reinterpret_cast<float*>(smem + L::red);
+
+    const PrepOut<SPLIT> po{XA, XR, XB, XK, XA, XA, XA, XA, true, true, true, true, false, false, false, false,
+                            gam, glast};
+    chunk_prep<NT, SPLIT>(raw, po, qp, tid);
+    rv.template store_T<SPLIT, true>(XVT, tid);
+    rv.template store_rows<SPLIT, true>(Vr, tid);
+    rdy.template store_T<SPLIT, false>(XDYT, tid);
+    rdy.template store_rows<SPLIT, false>(DYr, tid);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) put4(XS0, si, sj0 + 4 * q, s0v[q]);
+    lds_barrier();
+
+    // ---- phase 1: C x C matrices; Ge' = Ge diag(gamma_last)
+    const CcOut<SPLIT, NT> co{nullptr, XLak, XLak, XMrbT, XMrbT, XMrbT, XMrbT, true, false, false, true, false, false};
+    chunk_cc<SPLIT, NT>(XA, XR, XB, XK, co, tid);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gev[q][e] *= glast[sj0 + 4 * q + e];
+        put4(XGe, si, sj0 + 4 * q, gev[q]);
+    }
+    lds_barrier();
+
+    // ---- phase 2: RHS_U = Ahat S0^T + Lak V, RHS_D = Btil Ge'^T + Mrb^T DY; (I - Lab)^-1 to LDS
+    put4(XTinv, tid >> 3, (tid & 7) * 4, tv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) put(XTinvT, (tid & 7) * 4 + q, tid >> 3, tv[q]);
+    {
+        for (int job = wave; job < 16; job += NW) {
             const int which = job >> 3, ti = (job >> 2) & 1, tn = job & 3;
             f32x4 acc;
             if (which == 0) {
-                acc = mma<SPLIT, D>(zero4(), rows(A, LDA), ti * 16, rows(S0, LDA), tn * 16, lane);
-                acc = mma<SPLIT, C>(acc, rows(P2, LDC), ti * 16, cols(V, LDA), tn * 16, lane);
-                store_tile<LDA, false, MASK_NONE>(U, acc, ti * 16, tn * 16, lane);
+                acc = mma<SPLIT, D>(zero4(), XA, ti * 16, XS0, tn * 16, lane);
+                acc = mma<SPLIT, C, false, true>(acc, XLak, ti * 16, XVT, tn * 16, lane);
+                store_cols<MASK_NONE>(XRhsUT, acc, ti * 16, tn * 16, lane);
             } else {
-                acc = mma<SPLIT, D>(zero4(), rows(Bt, LDA), ti * 16, rows(Ge, LDA), tn * 16, lane);
-                acc = mma<SPLIT, C>(acc, cols(P3, LDC), ti * 16, cols(DY, LDA), tn * 16, lane);
-                store_tile<LDA, false, MASK_NONE>(DSA, acc, ti * 16, tn * 16, lane);
+                acc = mma<SPLIT, D>(zero4(), XB, ti * 16, XGe, tn * 16, lane);
+                acc = mma<SPLIT, C>(acc, XMrbT, ti * 16, XDYT, tn * 16, lane);
+                store_cols<MASK_NONE>(XRhsDT, acc, ti * 16, tn * 16, lane);
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // U = (I - Lab)^-1 RHS_U, DSA = (I - Lab)^-T RHS_D (in place via registers).
-    {
-        constexpr int NPER = (16 + NW - 1) / NW;
-        f32x4 res[NPER];
-#pragma unroll
-        for (int q2 = 0; q2 < NPER; ++q2) {
-            const int job = wave + q2 * NW;
-            if (job < 16) {
-                const int which = job >> 3, ti = (job >> 2) & 1, tn = job & 3;
-                if (which == 0)
-                    res[q2] = mma<SPLIT, C>(zero4(), rows(Tinv, LDC), ti * 16, cols(U, LDA), tn * 16, lane);
-                else
-                    res[q2] = mma<SPLIT, C>(zero4(), cols(Tinv, LDC), ti * 16, cols(DSA, LDA), tn * 16, lane);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q2 = 0; q2 < NPER; ++q2) {
-            const int job = wave + q2 * NW;
-            if (job < 16) {
-                const int which = job >> 3, ti = (job >> 2) & 1, tn = job & 3;
-                store_tile<LDA, false, MASK_NONE>(which == 0 ? U : DSA, res[q2], ti * 16, tn * 16, lane);
-            }
+    // ---- phase 3: U^T = RHS_U^T Tinv^T and DSA^T = RHS_D^T Tinv, stored as U, DSA rows (t, i)
+    const M YU = make_mat<SPLIT>(smem, L::YU, C, D), YDSA = make_mat<SPLIT>(smem, L::YDSA, C, D);
+    for (int job = wave; job < 16; job += NW) {
+        const int which = job >> 3, ti = job & 3, tt = (job >> 2) & 1;   // ti: i tile, tt: t tile
+        if (which == 0) {
+            const f32x4 acc = mma<SPLIT, C>(zero4(), XRhsUT, ti * 16, XTinv, tt * 16, lane);
+            store_cols<MASK_NONE>(YU, acc, ti * 16, tt * 16, lane);
+        } else {
+            const f32x4 acc = mma<SPLIT, C>(zero4(), XRhsDT, ti * 16, XTinvT, tt * 16, lane);
+            store_cols<MASK_NONE>(YDSA, acc, ti * 16, tt * 16, lane);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // P1 = tril(DY U^T), P2 = tril(DY V^T), P3 = stril(DSA U^T), P4 = stril(DSA V^T)
+    // ---- phase 4: P1 = tril(DY U^T), P2 = tril(DY V^T), P3 = stril(DSA U^T), P4 = stril(DSA V^T),
+    //      rows and transposed; first half of the j-indexed transposed operands.
+    // P1..P4 rows at YP + m*CM, transposed at YP + (4+m)*CM (m = 0..3)
+    auto Pr = [&](int m) { return make_mat<SPLIT>(smem, L::YP + m * L::CM, C, C); };
+    auto Pt = [&](int m) { return make_mat<SPLIT>(smem, L::YP + (4 + m) * L::CM, C, C); };
     for (int job = wave; job < 12; job += NW) {
         const int mat = job / 3, tile = job % 3;
         const int ti = tile == 0 ? 0 : 1, tj = tile == 2 ? 1 : 0;
-        const Op X = rows(mat < 2 ? DY : DSA, LDA);
-        const Op Y = rows((mat & 1) ? V : U, LDA);
-        const f32x4 acc = mma<SPLIT, D>(zero4(), X, ti * 16, Y, tj * 16, lane);
-        float* M = mat == 0 ? P1 : mat == 1 ? P2 : mat == 2 ? P3 : P4;
-        if (mat < 2) store_tile<LDC, false, MASK_LOWER>(M, acc, ti * 16, tj * 16, lane);
-        else store_tile<LDC, false, MASK_STRICT>(M, acc, ti * 16, tj * 16, lane);
-    }
-    for (int e = tid; e < 4 * 256; e += NT) {
-        const int m = e >> 8, t = (e & 255) >> 4, s = 16 + (e & 15);
-        float* M = m == 0 ? P1 : m == 1 ? P2 : m == 2 ? P3 : P4;
-        M[t * LDC + s] = 0.f;
-    }
-    // partial sums of diag(Gs^T S0) over row groups (Gs = gradient entering the chunk)
-    {
-        const float* gs = p.gbuf + ((int64_t)head * p.NC + c) * D * D;
-        constexpr int NG = NT / 64, RPG = D / NG;
-        const int j = tid & 63, grp = tid >> 6;
-        float acc = 0.f;
-        for (int i = grp * RPG; i < (grp + 1) * RPG; ++i) acc = fmaf(gs[i * D + j], S0[i * LDA + j], acc);
-        red[grp * 64 + j] = acc;
-    }
-    __syncthreads();
-
-    // Outputs dr, da, dk, db per 16x16 position, plus the dw ingredients.
-    for (int pos = wave; pos < 8; pos += NW) {
-        const int ti = pos >> 2, tj = pos & 3;
-        f32x4 aR = mma<SPLIT, D>(zero4(), rows(DY, LDA), ti * 16, cols(S0, LDA), tj * 16, lane);
-        aR = mma<SPLIT, C>(aR, rows(P1, LDC), ti * 16, cols(Bt, LDA), tj * 16, lane);
-        aR = mma<SPLIT, C>(aR, rows(P2, LDC), ti * 16, cols(Kt, LDA), tj * 16, lane);
-        f32x4 aA = mma<SPLIT, D>(zero4(), rows(DSA, LDA), ti * 16, cols(S0, LDA), tj * 16, lane);
-        aA = mma<SPLIT, C>(aA, rows(P3, LDC), ti * 16, cols(Bt, LDA), tj * 16, lane);
-        aA = mma<SPLIT, C>(aA, rows(P4, LDC), ti * 16, cols(Kt, LDA), tj * 16, lane);
-        f32x4 aK = mma<SPLIT, D>(zero4(), rows(V, LDA), ti * 16, cols(Ge, LDA), tj * 16, lane);
-        aK = mma<SPLIT, C>(aK, cols(P4, LDC), ti * 16, cols(A, LDA), tj * 16, lane);
-        aK = mma<SPLIT, C>(aK, cols(P2, LDC), ti * 16, cols(R, LDA), tj * 16, lane);
-        f32x4 aB = mma<SPLIT, D>(zero4(), rows(U, LDA), ti * 16, cols(Ge, LDA), tj * 16, lane);
-        aB = mma<SPLIT, C>(aB, cols(P3, LDC), ti * 16, cols(A, LDA), tj * 16, lane);
-        aB = mma<SPLIT, C>(aB, cols(P1, LDC), ti * 16, cols(R, LDA), tj * 16, lane);
-        const int r = lane & 15, g = lane >> 4;
-        const int j = tj * 16 + r;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = ti * 16 + 4 * g + q;
-            const float gt = W[t * LDA + j];
-            const float gp = t > 0 ? W[(t - 1) * LDA + j] : 1.f;
-            const float inv = 1.f / gt;
-            const float f = A[t * LDA + j] * aA[q];                       // a da
-            const float e = Kt[t * LDA + j] * aK[q] + Bt[t * LDA + j] * aB[q] - R[t * LDA + j] * aR[q];
-            Hh[t * LDA + j] = e - f;
-            Fa[t * LDA + j] = f;
-            if (t < Cc) {
-                const int64_t o = base + t * tstride + j;
-                p.dr[o] = aR[q] * gt;
-                p.da[o] = aA[q] * gp;
-                p.dk[o] = aK[q] * inv;
-                p.db[o] = aB[q] * inv;
-            }
+        const M X = mat < 2 ? DYr : YDSA;
+        f32x4 acc;
+        if (mat & 1) acc = mma<SPLIT, D, false, true>(zero4(), X, ti * 16, Vr, tj * 16, lane);
+        else acc = mma<SPLIT, D>(zero4(), X, ti * 16, YU, tj * 16, lane);
+        if (mat < 2) {
+            store_rows<MASK_LOWER>(Pr(mat), acc, ti * 16, tj * 16, lane);
+            store_cols<MASK_LOWER>(Pt(mat), acc, ti * 16, tj * 16, lane);
+        } else {
+            store_rows<MASK_STRICT>(Pr(mat), acc, ti * 16, tj * 16, lane);
+            store_cols<MASK_STRICT>(Pt(mat), acc, ti * 16, tj * 16, lane);
         }
     }
-    __syncthreads();
+    if (wave == NW - 1) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            zero_block(Pr(m), 0, 16, lane);
+            zero_block(Pt(m), 16, 0, lane);
+        }
+    }
 
+    const M YS0T = make_mat<SPLIT>(smem, L::YS0T, 32, D), YGeT = make_mat<SPLIT>(smem, L::YGeT, 32, D);
+    const M YAT = make_mat<SPLIT>(smem, L::YAT, 32, C), YRT = make_mat<SPLIT>(smem, L::YRT, 32, C);
+    const M YBT = make_mat<SPLIT>(smem, L::YBT, 32, C), YKT = make_mat<SPLIT>(smem, L::YKT, 32, C);
+    float* hh_ = reinterpret_cast<float*>(smem + L::YHh);
+    float* fa_ = reinterpret_cast<float*>(smem + L::YFa);
+
+    // Writes the transposed operands for columns j in [32*half, 32*half + 32).
+    auto fill_half = [&](int half) {
+        if ((sj0 >> 5) == half) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int jl = sj0 - 32 * half + 4 * q + e;
+                    put(YS0T, jl, si, s0v[q][e]);
+                    put(YGeT, jl, si, gev[q][e]);
+                }
+            }
+        }
+        constexpr int TPG = RawChunk<NT, InT>::TPG;
+        const int jp = tid & 31, q = tid >> 5;
+        if ((jp >> 4) == half) {
+            const int t0q = q * TPG;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int j = 2 * jp + e, jl = j - 32 * half;
+                f32x4 av, rv4, bv, kv;
+#pragma unroll
+                for (int tt = 0; tt < TPG; ++tt) {
+                    const int t = t0q + tt;
+                    const float g = gam[t * LDG + j];
+                    const float gp = t > 0 ? gam[(t - 1) * LDG + j] : 1.f;
+                    const float ig = rcp(g);
+                    const float2 a2 = raw.get(raw.a[tt], tt, tid, 0.f), r2 = raw.get(raw.r[tt], tt, tid, 0.f);
+                    const float2 b2 = raw.get(raw.b[tt], tt, tid, 0.f), k2 = raw.get(raw.k[tt], tt, tid, 0.f);
+                    av[tt] = (e ? a2.y : a2.x) * gp;
+                    rv4[tt] = (e ? r2.y : r2.x) * g;
+                    bv[tt] = (e ? b2.y : b2.x) * ig;
+                    kv[tt] = (e ? k2.y : k2.x) * ig;
+                }
+                put4(YAT, jl, t0q, av);
+                put4(YRT, jl, t0q, rv4);
+                put4(YBT, jl, t0q, bv);
+                put4(YKT, jl, t0q, kv);
+            }
+        }
+    };
+    static_assert(RawChunk<NT, InT>::TPG == 4, "fill_half packs four tokens");
+    fill_half(0);
+    lds_barrier();
+
+    // ---- phase 5: outputs, one j half at a time
+    for (int half = 0; half < 2; ++half) {
+        // four 16 x 16 positions (t tile, j tile) per half, one per wave
+        for (int pos = wave; pos < 4; pos += NW) {
+            const int ti = pos >> 1, tj = pos & 1;
+            const int jl0 = tj * 16;
+            f32x4 aR = mma<SPLIT, D>(zero4(), DYr, ti * 16, YS0T, jl0, lane);
+            aR = mma<SPLIT, C>(aR, Pr(0), ti * 16, YBT, jl0, lane);
+            aR = mma<SPLIT, C>(aR, Pr(1), ti * 16, YKT, jl0, lane);
+            f32x4 aA = mma<SPLIT, D>(zero4(), YDSA, ti * 16, YS0T, jl0, lane);
+            aA = mma<SPLIT, C>(aA, Pr(2), ti * 16, YBT, jl0, lane);
+            aA = mma<SPLIT, C>(aA, Pr(3), ti * 16, YKT, jl0, lane);
+            f32x4 aK = mma<SPLIT, D, true, false>(zero4(), Vr, ti * 16, YGeT, jl0, lane);
+            aK = mma<SPLIT, C>(aK, Pt(3), ti * 16, YAT, jl0, lane);
+            aK = mma<SPLIT, C>(aK, Pt(1), ti * 16, YRT, jl0, lane);
+            f32x4 aB = mma<SPLIT, D>(zero4(), YU, ti * 16, YGeT, jl0, lane);
+            aB = mma<SPLIT, C>(aB, Pt(2), ti * 16, YAT, jl0, lane);
+            aB = mma<SPLIT, C>(aB, Pt(0), ti * 16, YRT, jl0, lane);
+            const int jl = jl0 + r16, j = 32 * half + jl;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = ti * 16 + 4 * g4 + q;
+                const float g = gam[t * LDG + j];
+                const float gp = t > 0 ? gam[(t - 1) * LDG + j] : 1.f;
+                const float ig = rcp(g);
+                if (t < Cc) {
+                    const int64_t o = base + t * tstride + j;
+                    p.dr[o] = aR[q] * g;
+                    p.da[o] = aA[q] * gp;
+                    p.dk[o] = aK[q] * ig;
+                    p.db[o] = aB[q] * ig;
+                }
+                // k dk = Ktil * aK, b db = Btil * aB, r dr = Rhat * aR, a da = Ahat * aA
+                const float fa = get(YAT, jl, t) * aA[q];
+                const float ev = get(YKT, jl, t) * aK[q] + get(YBT, jl, t) * aB[q] - get(YRT, jl, t) * aR[q];
+                hh_[t * LDG + j] = ev - fa;
+                fa_[t * LDG + j] = fa;
+            }
+        }
+        lds_barrier();
+        if (half == 0) {
+            fill_half(1);
+            lds_barrier();
+        }
+    }
+
+    // ---- dw: phi_t = diag(Gs^T S0) - sum_{s<=t} a da + sum_{s<t} (k dk + b db - r dr)
     if (tid < 64) {
         const int j = tid;
-        constexpr int NG = NT / 64;
-        float acc = 0.f;
-#pragma unroll
-        for (int grp = 0; grp < NG; ++grp) acc += red[grp * 64 + j];
-        const InT* gw = static_cast<const InT*>(p.w);
+        float acc = red[j] + red[64 + j] + red[128 + j] + red[192 + j];
         for (int t = 0; t < Cc; ++t) {
             const int64_t o = base + t * tstride + j;
-            float wv;
-            if constexpr (sizeof(InT) == 2) wv = __uint_as_float((uint32_t)gw[o] << 16);
-            else wv = gw[o];
-            p.dw[o] = (acc - Fa[t * LDA + j]) / wv;
-            acc += Hh[t * LDA + j];
+            p.dw[o] = (acc - fa_[t * LDG + j]) / load1(gw + o);
+            acc += hh_[t * LDG + j];
         }
     }
 }
 
 template <typename F>
-hipError_t set_smem(F kern, size_t bytes, bool& done) {
+hipError_t set_smem(F kern, int bytes, bool& done) {
     if (done) return hipSuccess;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e == hipSuccess) done = true;
     return e;
 }
@@ -414,35 +579,38 @@ hipError_t set_smem(F kern, size_t bytes, bool& done) {
 template <typename InT, bool SPLIT, int RB>
 hipError_t launch_state(const BwdArgs& a, hipStream_t s) {
     constexpr int NT = 256;
-    using L = StateLayout<RB>;
+    using L = StateSmem<SPLIT, RB>;
+    static_assert(L::total <= 160 * 1024, "state kernel LDS exceeds 160 KiB");
     auto kern = bwd_state_kernel<InT, SPLIT, RB, NT>;
     static bool done = false;
-    hipError_t e = set_smem(kern, L::bytes, done);
+    hipError_t e = set_smem(kern, L::total, done);
     if (e != hipSuccess) return e;
     const int heads = a.B * a.H;
     const int xcd = (heads % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3(heads * (D / RB)), dim3(NT), L::bytes, s, a, xcd);
+    hipLaunchKernelGGL(kern, dim3(heads * (D / RB)), dim3(NT), L::total, s, a, xcd);
     return hipGetLastError();
 }
 
 template <typename InT, bool SPLIT>
 hipError_t launch_state_typed(const BwdArgs& a, hipStream_t s) {
     const int heads = a.B * a.H;
-    if (heads >= 256) return launch_state<InT, SPLIT, 64>(a, s);
-    if (heads >= 128) return launch_state<InT, SPLIT, 32>(a, s);
+    if (heads > 128) return launch_state<InT, SPLIT, 64>(a, s);
+    if (heads > 64) return launch_state<InT, SPLIT, 32>(a, s);
     return launch_state<InT, SPLIT, 16>(a, s);
 }
 
 template <typename InT, bool SPLIT>
 hipError_t launch_inputs_typed(const BwdArgs& a, hipStream_t s) {
     constexpr int NT = 256;
+    using L = ChunkSmem<SPLIT>;
+    static_assert(L::total <= 160 * 1024, "chunk kernel LDS exceeds 160 KiB");
     auto kern = bwd_chunk_kernel<InT, SPLIT, NT>;
     static bool done = false;
-    hipError_t e = set_smem(kern, ChunkLayout::bytes, done);
+    hipError_t e = set_smem(kern, L::total, done);
     if (e != hipSuccess) return e;
     const int heads = a.B * a.H;
     const int xcd = (heads % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3(heads * a.NC), dim3(NT), ChunkLayout::bytes, s, a, xcd);
+    hipLaunchKernelGGL(kern, dim3(heads * a.NC), dim3(NT), L::total, s, a, xcd);
     return hipGetLastError();
 }
 

@@ -14,18 +14,21 @@
 // (C x C) matrices -- work for the matrix cores (MFMA):
 //     U   = (I - Lab)^-1 (Ahat S0^T + Lak V)
 //     Y   = Rhat S0^T + Mrb U + Mrk V
-//     S_C = (S0 + U^T Btil + V^T Ktil) diag(gamma_{C-1})
+//     S_C = (S0 + U^T Btil + V^T Ktil) diag(gamma_last)
 // where Lab = strict_lower(Ahat Btil^T), Lak = strict_lower(Ahat Ktil^T),
 // Mrb = lower(Rhat Btil^T), Mrk = lower(Rhat Ktil^T).  The backward kernels
 // use the same matrices (see wkv7_bwd.hip).
 //
-// Matrix products read fp32 operands from LDS.  Two precisions:
-//   SPLIT = false : v_mfma_f32_16x16x4_f32 (full fp32; used for fp32 inputs)
-//   SPLIT = true  : every fp32 operand x is split into bf16 hi = rn(x) and
-//                   lo = rn(x - hi); hi*hi + hi*lo + lo*hi on
-//                   v_mfma_f32_16x16x32_bf16 (about 2^-17 relative per
-//                   product; used for bf16 inputs).
-// Both accumulate in fp32 and produce the same 16x16 output layout.
+// Every product is C[m][n] = sum_k X[m][k] Y[n][k] with both operands held in
+// LDS with k contiguous ("Mat").  Two storage formats:
+//   SPLIT = true  (bf16 inputs): each fp32 value x is stored once as two bf16
+//                 planes, hi = rn(x) and lo = rn(x - hi); a product is
+//                 hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16 (about
+//                 2^-17 relative per product, fp32 accumulation).  Operands
+//                 known to be exact in bf16 (the raw v) skip their lo term.
+//   SPLIT = false (fp32 inputs): one fp32 plane, v_mfma_f32_16x16x4_f32.
+// Rows are padded (by 8 bf16 / 4 fp32) so that the 16-byte operand reads of
+// one MFMA hit distinct LDS banks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,19 +36,229 @@
 
 namespace wkv7 {
 
-constexpr int D = 64;    // head size (state is D x D)
-constexpr int C = 32;    // chunk length (checkpoint interval)
-constexpr int LDA = 68;  // LDS row stride (floats) for rows of 64 values
-constexpr int LDC = 36;  // LDS row stride (floats) for rows of 32 values
+constexpr int D = 64;  // head size (state is D x D)
+constexpr int C = 32;  // chunk length (checkpoint interval)
+constexpr int LDF = 36;  // row stride (floats) of fp32 C x C scratch matrices
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Wait for this wave's outstanding LDS operations and keep the compiler from
+// moving memory accesses across (intra-wave LDS hand-off).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for LDS hand-offs.  Unlike __syncthreads() it does not
+// wait for the wave's outstanding global loads and stores, so prefetches of
+// the next chunk stay in flight across it.  (No kernel here reads global
+// data that another wave of the same workgroup wrote.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 1/x with v_rcp_f32 (at most 1 ulp off).
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ---------------------------------------------------------------------------
-// Block -> (outer, inner) mapping.  Blocks that share `outer` (one head) and
-// differ in `inner` (row block or chunk) read the same inputs; with xcd = true
-// they are placed on the same XCD (blocks are dealt to the 8 XCDs round
-// robin), so those reads share one L2.  Requires n_outer % 8 == 0.
+// LDS matrix formats and handles.
+template <bool SPLIT>
+struct Fmt {
+    static constexpr int pad = SPLIT ? 8 : 4;
+    static constexpr int esz = SPLIT ? 2 : 4;
+    static constexpr int planes = SPLIT ? 2 : 1;
+    // bytes of a rows x K matrix (multiple of 16)
+    static constexpr int bytes(int rows, int K) { return rows * (K + pad) * esz * planes; }
+    static constexpr int ld(int K) { return K + pad; }
+};
+
+template <bool SPLIT>
+struct Mat {
+    char* p;    // LDS base
+    int ld;     // row stride in elements
+    int plane;  // elements per plane (lo plane offset, SPLIT only)
+};
+
+template <bool SPLIT>
+__device__ __forceinline__ Mat<SPLIT> make_mat(char* smem, int off, int rows, int K) {
+    return Mat<SPLIT>{smem + off, Fmt<SPLIT>::ld(K), rows * Fmt<SPLIT>::ld(K)};
+}
+
+__device__ __forceinline__ void split1(float v, __bf16& hi, __bf16& lo) {
+    hi = (__bf16)v;
+    lo = (__bf16)(v - (float)hi);
+}
+
+// element (m, k) <- v
+__device__ __forceinline__ void put(Mat<true> M, int m, int k, float v) {
+    __bf16* h = reinterpret_cast<__bf16*>(M.p) + m * M.ld + k;
+    __bf16 hi, lo;
+    split1(v, hi, lo);
+    h[0] = hi;
+    h[M.plane] = lo;
+}
+__device__ __forceinline__ void put(Mat<false> M, int m, int k, float v) {
+    reinterpret_cast<float*>(M.p)[m * M.ld + k] = v;
+}
+// element (m, k) <- v, v exact in bf16 (hi plane only; lo is never read)
+__device__ __forceinline__ void put_exact(Mat<true> M, int m, int k, float v) {
+    reinterpret_cast<__bf16*>(M.p)[m * M.ld + k] = (__bf16)v;
+}
+__device__ __forceinline__ void put_exact(Mat<false> M, int m, int k, float v) { put(M, m, k, v); }
+
+// value of element (m, k) (hi + lo for the split format)
+__device__ __forceinline__ float get(Mat<true> M, int m, int k) {
+    const __bf16* h = reinterpret_cast<const __bf16*>(M.p) + m * M.ld + k;
+    return (float)h[0] + (float)h[M.plane];
+}
+__device__ __forceinline__ float get(Mat<false> M, int m, int k) {
+    return reinterpret_cast<const float*>(M.p)[m * M.ld + k];
+}
+
+// elements (m, k..k+1) <- v0, v1   (k even)
+__device__ __forceinline__ void put2(Mat<true> M, int m, int k, float v0, float v1) {
+    __bf16* h = reinterpret_cast<__bf16*>(M.p) + m * M.ld + k;
+    bf16x2 hi, lo;
+    __bf16 a, b;
+    split1(v0, a, b);
+    hi[0] = a; lo[0] = b;
+    split1(v1, a, b);
+    hi[1] = a; lo[1] = b;
+    *reinterpret_cast<bf16x2*>(h) = hi;
+    *reinterpret_cast<bf16x2*>(h + M.plane) = lo;
+}
+__device__ __forceinline__ void put2(Mat<false> M, int m, int k, float v0, float v1) {
+    *reinterpret_cast<float2*>(reinterpret_cast<float*>(M.p) + m * M.ld + k) = make_float2(v0, v1);
+}
+__device__ __forceinline__ void put2_exact(Mat<true> M, int m, int k, float v0, float v1) {
+    bf16x2 hi;
+    hi[0] = (__bf16)v0;
+    hi[1] = (__bf16)v1;
+    *reinterpret_cast<bf16x2*>(reinterpret_cast<__bf16*>(M.p) + m * M.ld + k) = hi;
+}
+__device__ __forceinline__ void put2_exact(Mat<false> M, int m, int k, float v0, float v1) { put2(M, m, k, v0, v1); }
+
+// elements (m, k..k+3) <- v   (k % 4 == 0)
+__device__ __forceinline__ void put4(Mat<true> M, int m, int k, f32x4 v) {
+    __bf16* h = reinterpret_cast<__bf16*>(M.p) + m * M.ld + k;
+    bf16x4 hi, lo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        __bf16 a, b;
+        split1(v[q], a, b);
+        hi[q] = a;
+        lo[q] = b;
+    }
+    *reinterpret_cast<bf16x4*>(h) = hi;
+    *reinterpret_cast<bf16x4*>(h + M.plane) = lo;
+}
+__device__ __forceinline__ void put4(Mat<false> M, int m, int k, f32x4 v) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(M.p) + m * M.ld + k) = v;
+}
+__device__ __forceinline__ void put4_exact(Mat<true> M, int m, int k, f32x4 v) {
+    bf16x4 hi;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hi[q] = (__bf16)v[q];
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(M.p) + m * M.ld + k) = hi;
+}
+__device__ __forceinline__ void put4_exact(Mat<false> M, int m, int k, f32x4 v) { put4(M, m, k, v); }
+
+// ---------------------------------------------------------------------------
+// acc += X[m0:m0+16, 0:K] * Y[n0:n0+16, 0:K]^T   (one wave, one 16x16 tile).
+// XEX / YEX: operand exact in bf16 (skip its lo term; SPLIT only).
+// Output layout: acc[q] holds element (m0 + 4*(lane/16) + q, n0 + lane%16).
+template <bool SPLIT, int K, bool XEX = false, bool YEX = false>
+__device__ __forceinline__ f32x4 mma(f32x4 acc, Mat<SPLIT> X, int m0, Mat<SPLIT> Y, int n0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    if constexpr (SPLIT) {
+        const __bf16* xp = reinterpret_cast<const __bf16*>(X.p) + (m0 + r) * X.ld + 8 * g;
+        const __bf16* yp = reinterpret_cast<const __bf16*>(Y.p) + (n0 + r) * Y.ld + 8 * g;
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(xp + k0);
+            const bf16x8 yh = *reinterpret_cast<const bf16x8*>(yp + k0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, acc, 0, 0, 0);
+            if constexpr (!YEX) {
+                const bf16x8 yl = *reinterpret_cast<const bf16x8*>(yp + Y.plane + k0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yl, acc, 0, 0, 0);
+            }
+            if constexpr (!XEX) {
+                const bf16x8 xl = *reinterpret_cast<const bf16x8*>(xp + X.plane + k0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yh, acc, 0, 0, 0);
+            }
+        }
+    } else {
+        const float* xp = reinterpret_cast<const float*>(X.p) + (m0 + r) * X.ld + g;
+        const float* yp = reinterpret_cast<const float*>(Y.p) + (n0 + r) * Y.ld + g;
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[k0], yp[k0], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+enum Mask { MASK_NONE = 0, MASK_LOWER = 1, MASK_STRICT = 2 };
+
+template <int MASK>
+__device__ __forceinline__ float masked(float v, int m, int n) {
+    if (MASK == MASK_LOWER && m < n) return 0.f;
+    if (MASK == MASK_STRICT && m <= n) return 0.f;
+    return v;
+}
+
+// Tile (m0.., n0..) -> M[m][n]  (row m, k = n)
+template <int MASK, bool SPLIT>
+__device__ __forceinline__ void store_rows(Mat<SPLIT> M, f32x4 acc, int m0, int n0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = m0 + 4 * g + q, n = n0 + r;
+        put(M, m, n, masked<MASK>(acc[q], m, n));
+    }
+}
+
+// Tile (m0.., n0..) -> M[n][m]  (row n, k = m; four consecutive k per lane)
+template <int MASK, bool SPLIT>
+__device__ __forceinline__ void store_cols(Mat<SPLIT> M, f32x4 acc, int m0, int n0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    f32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = masked<MASK>(acc[q], m0 + 4 * g + q, n0 + r);
+    put4(M, n0 + r, m0 + 4 * g, v);
+}
+
+// fp32 tile store into a plain row-major LDS array (stride ld floats)
+template <int MASK>
+__device__ __forceinline__ void store_f32(float* M, int ld, f32x4 acc, int m0, int n0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = m0 + 4 * g + q, n = n0 + r;
+        M[m * ld + n] = masked<MASK>(acc[q], m, n);
+    }
+}
+
+// Zero the 16x16 block (m0.., k0..) of a matrix.
+template <bool SPLIT>
+__device__ __forceinline__ void zero_block(Mat<SPLIT> M, int m0, int k0, int lane) {
+    const int m = m0 + (lane >> 2), k = k0 + (lane & 3) * 4;
+    put4(M, m, k, zero4());
+}
+
+// ---------------------------------------------------------------------------
+// Global loads of two consecutive values widened to fp32.
+__device__ __forceinline__ float2 load2(const float* p) { return *reinterpret_cast<const float2*>(p); }
+__device__ __forceinline__ float2 load2(const uint16_t* p) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));  // bf16 -> fp32 exact
+}
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+
+// Block -> (outer, inner).  Blocks sharing `outer` (one head) differ in
+// `inner` (row block or chunk) and read the same inputs; with xcd = true they
+// are placed on one XCD (blocks are dealt to the 8 XCDs round robin), so those
+// reads share one L2.  Requires n_outer % 8 == 0.
 __device__ __forceinline__ void block_map(int blk, int inner_n, bool xcd, int& outer, int& inner) {
     if (xcd) {
         const int x = blk & 7, slot = blk >> 3;
@@ -58,236 +271,339 @@ __device__ __forceinline__ void block_map(int blk, int inner_n, bool xcd, int& o
 }
 
 // ---------------------------------------------------------------------------
-// Global loads of 8 consecutive values, widened to fp32.
-__device__ __forceinline__ void load8(const float* p, float* o) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-}
-__device__ __forceinline__ void load8(const uint16_t* p, float* o) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        o[2 * q] = __uint_as_float(w[q] << 16);              // bf16 -> fp32 is exact
-        o[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+// Two consecutive input values as loaded from global memory (bf16 pair packed
+// in one 32-bit word, or an fp32 pair), widened to fp32 only when used, so
+// that a prefetch does not wait for its data.
+template <typename InT>
+struct Pair;
+template <>
+struct Pair<uint16_t> {
+    using T = uint32_t;
+    static __device__ __forceinline__ T load(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+    static __device__ __forceinline__ float2 f(T u) {
+        return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));  // exact
     }
-}
-
-// Load one chunk (C tokens x 64 values) of a (B,T,H,D) tensor into LDS rows
-// dst[t*LDA + j].  Tokens t >= Cc get `fill`.
-template <typename InT, int NT>
-__device__ __forceinline__ void load_chunk(const InT* __restrict__ src, int64_t base, int64_t tstride,
-                                           int Cc, float fill, float* dst, int tid) {
-    for (int e = tid; e < C * 8; e += NT) {
-        const int t = e >> 3, j0 = (e & 7) * 8;
-        float v[8];
-        if (t < Cc) {
-            load8(src + base + t * tstride + j0, v);
-        } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = fill;
-        }
-        float4* d = reinterpret_cast<float4*>(dst + t * LDA + j0);
-        d[0] = make_float4(v[0], v[1], v[2], v[3]);
-        d[1] = make_float4(v[4], v[5], v[6], v[7]);
-    }
-}
-
-// Load columns [col0, col0+NCOL) of one chunk transposed: dst[i*LDC + t].
-template <typename InT, int NT, int NCOL>
-__device__ __forceinline__ void load_chunk_cols_T(const InT* __restrict__ src, int64_t base, int64_t tstride,
-                                                  int Cc, int col0, float* dst, int tid) {
-    constexpr int G = NCOL / 8;
-    for (int e = tid; e < C * G; e += NT) {
-        const int t = e / G, i0 = (e % G) * 8;
-        float v[8];
-        if (t < Cc) {
-            load8(src + base + t * tstride + col0 + i0, v);
-        } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = 0.f;
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) dst[(i0 + q) * LDC + t] = v[q];
-    }
-}
-
-// Copy NROW rows of a row-major 64-wide fp32 global matrix into LDS rows
-// (stride LDA); src == nullptr gives zeros.
-template <int NT, int NROW>
-__device__ __forceinline__ void load_state_rows(const float* __restrict__ src, float* dst, int tid) {
-    for (int e = tid; e < NROW * 16; e += NT) {
-        const int i = e >> 4, j4 = (e & 15) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (src) v = *reinterpret_cast<const float4*>(src + i * D + j4);
-        *reinterpret_cast<float4*>(dst + i * LDA + j4) = v;
-    }
-}
-
-template <int NT, int NROW>
-__device__ __forceinline__ void store_state_rows(const float* src, float* __restrict__ dst, int tid) {
-    for (int e = tid; e < NROW * 16; e += NT) {
-        const int i = e >> 4, j4 = (e & 15) * 4;
-        *reinterpret_cast<float4*>(dst + i * D + j4) = *reinterpret_cast<const float4*>(src + i * LDA + j4);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// LDS operand view: element (m, k) = p[m*sm + k*sk].
-struct Op {
-    const float* p;
-    int sm, sk;
 };
-__device__ __forceinline__ Op rows(const float* p, int ld) { return Op{p, ld, 1}; }  // (m,k) = p[m][k]
-__device__ __forceinline__ Op cols(const float* p, int ld) { return Op{p, 1, ld}; }  // (m,k) = p[k][m]
+template <>
+struct Pair<float> {
+    using T = float2;
+    static __device__ __forceinline__ T load(const float* p) { return *reinterpret_cast<const float2*>(p); }
+    static __device__ __forceinline__ float2 f(T v) { return v; }
+};
 
-// acc += X[m0:m0+16, 0:K] * Y[n0:n0+16, 0:K]^T   (one wave, one 16x16 tile)
-// Output layout: acc[q] holds element (m0 + 4*(lane/16) + q, n0 + lane%16).
-template <bool SPLIT, int K>
-__device__ __forceinline__ f32x4 mma(f32x4 acc, Op X, int m0, Op Y, int n0, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    if constexpr (!SPLIT) {
-        const float* xp = X.p + (m0 + r) * X.sm + g * X.sk;
-        const float* yp = Y.p + (n0 + r) * Y.sm + g * Y.sk;
+// Raw chunk inputs, prefetched into registers one chunk ahead.  Thread tid
+// holds columns 2*jp, 2*jp+1 (jp = tid % 32) of tokens q*TPG .. q*TPG+TPG-1
+// (q = tid / 32) for w, a, r, b, k.  Tokens at or beyond `cc` (the chunk's
+// length) read the last valid token and are replaced at use: w = 1, the
+// rest 0.
+template <int NT, typename InT>
+struct RawChunk {
+    static constexpr int NG = NT / 32;
+    static constexpr int TPG = C / NG;
+    static_assert(NT % 32 == 0 && C % NG == 0 && TPG >= 1, "raw chunk thread shape");
+    using W = typename Pair<InT>::T;
+    W w[TPG], a[TPG], r[TPG], b[TPG], k[TPG];
+    int cc;
+
+    __device__ __forceinline__ void load(const InT* pw, const InT* pa, const InT* pr, const InT* pb,
+                                         const InT* pk, int64_t base, int64_t tstride, int Cc, int tid) {
+        const int jp = tid & 31, q = tid >> 5;
+        cc = Cc;
 #pragma unroll
-        for (int k0 = 0; k0 < K; k0 += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[k0 * X.sk], yp[k0 * Y.sk], acc, 0, 0, 0);
-    } else {
-        const float* xp = X.p + (m0 + r) * X.sm + 8 * g * X.sk;
-        const float* yp = Y.p + (n0 + r) * Y.sm + 8 * g * Y.sk;
-#pragma unroll
-        for (int k0 = 0; k0 < K; k0 += 32) {
-            bf16x8 xh, xl, yh, yl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xv = xp[(k0 + e) * X.sk];
-                const float yv = yp[(k0 + e) * Y.sk];
-                const __bf16 xhe = (__bf16)xv;
-                const __bf16 yhe = (__bf16)yv;
-                xh[e] = xhe;
-                yh[e] = yhe;
-                xl[e] = (__bf16)(xv - (float)xhe);
-                yl[e] = (__bf16)(yv - (float)yhe);
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yl, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yh, acc, 0, 0, 0);
+        for (int tt = 0; tt < TPG; ++tt) {
+            const int t = min(q * TPG + tt, Cc - 1);
+            const int64_t o = base + t * tstride + 2 * jp;
+            w[tt] = Pair<InT>::load(pw + o);
+            a[tt] = Pair<InT>::load(pa + o);
+            r[tt] = Pair<InT>::load(pr + o);
+            b[tt] = Pair<InT>::load(pb + o);
+            k[tt] = Pair<InT>::load(pk + o);
         }
     }
-    return acc;
-}
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// Write a 16x16 tile to an LDS matrix, optionally transposed, optionally
-// keeping only the lower triangle of the full matrix (strict: row > col).
-enum Mask { MASK_NONE = 0, MASK_LOWER = 1, MASK_STRICT = 2 };
-template <int LD, bool TRANS, int MASK>
-__device__ __forceinline__ void store_tile(float* M, f32x4 acc, int m0, int n0, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int m = m0 + 4 * g + q, n = n0 + r;
-        float v = acc[q];
-        if (MASK == MASK_LOWER && m < n) v = 0.f;
-        if (MASK == MASK_STRICT && m <= n) v = 0.f;
-        if (TRANS) M[n * LD + m] = v;
-        else M[m * LD + n] = v;
+    __device__ __forceinline__ bool valid(int tt, int tid) const { return (tid >> 5) * TPG + tt < cc; }
+    __device__ __forceinline__ float2 get(const W& x, int tt, int tid, float fill) const {
+        return valid(tt, tid) ? Pair<InT>::f(x) : make_float2(fill, fill);
     }
-}
+};
 
-// ---------------------------------------------------------------------------
-// Chunk preparation.  On entry W, A, R, Bt, Kt (C x LDA) hold raw w, a, r, b,
-// k of the chunk (padding tokens: w = 1, the rest 0).  On exit W holds
-// gamma_t, A = a*gamma_{t-1}, R = r*gamma_t, Bt = b/gamma_t, Kt = k/gamma_t,
-// and glast[j] = gamma_{C-1}[j].  qp is LDS scratch of (NT/64) x 64 floats.
-// Ends with a barrier.
-template <int NT>
-__device__ __forceinline__ void chunk_prep(float* W, float* A, float* R, float* Bt, float* Kt,
-                                           float* glast, float* qp, int tid) {
-    constexpr int NG = NT / 64, TPG = C / NG;
-    static_assert(NT % 64 == 0 && C % NG == 0, "chunk_prep thread shape");
-    const int j = tid & 63, q = tid >> 6;
-    float loc[TPG];
-    float p = 1.f;
+// Where chunk_prep writes.  Null handles are skipped.
+template <bool SPLIT>
+struct PrepOut {
+    Mat<SPLIT> A, R, B, K;        // rows (t, j)
+    Mat<SPLIT> AT, RT, BT, KT;    // transposed (j, t)
+    bool a, r, b, k, at, rt, bt, kt;
+    float* gamma;                 // fp32 [t][j] (stride 68) or null
+    float* glast;                 // fp32 [64]
+};
+constexpr int LDG = 68;           // row stride of the fp32 gamma array
+
+// Chunk preparation from the registers of RawChunk: gamma (cumulative product
+// of w within the chunk), the scaled operands, gamma_last.  `qp` is LDS
+// scratch of NG x 64 floats.  Contains one barrier; the caller must barrier
+// before the outputs are read.
+template <int NT, bool SPLIT, typename InT>
+__device__ __forceinline__ void chunk_prep(const RawChunk<NT, InT>& raw, const PrepOut<SPLIT>& o, float* qp,
+                                           int tid) {
+    constexpr int NG = RawChunk<NT, InT>::NG, TPG = RawChunk<NT, InT>::TPG;
+    const int jp = tid & 31, q = tid >> 5, j0 = 2 * jp;
+    float2 loc[TPG];
+    float2 p = make_float2(1.f, 1.f);
 #pragma unroll
     for (int tt = 0; tt < TPG; ++tt) {
-        p *= W[(q * TPG + tt) * LDA + j];
+        const float2 wv = raw.get(raw.w[tt], tt, tid, 1.f);
+        p.x *= wv.x;
+        p.y *= wv.y;
         loc[tt] = p;
     }
-    qp[q * 64 + j] = p;
-    __syncthreads();
-    float pre = 1.f, tot = 1.f;
+    qp[q * 64 + j0] = p.x;
+    qp[q * 64 + j0 + 1] = p.y;
+    lds_barrier();
+    float2 pre = make_float2(1.f, 1.f);
 #pragma unroll
     for (int q2 = 0; q2 < NG; ++q2) {
-        const float x = qp[q2 * 64 + j];
-        if (q2 < q) pre *= x;
-        tot *= x;
+        if (q2 < q) {
+            pre.x *= qp[q2 * 64 + j0];
+            pre.y *= qp[q2 * 64 + j0 + 1];
+        }
     }
-    float gprev = pre;
+    float2 gprev = pre;
+    float gt[2][TPG], at[2][TPG], rt[2][TPG], bt[2][TPG], kt[2][TPG];
 #pragma unroll
     for (int tt = 0; tt < TPG; ++tt) {
         const int t = q * TPG + tt;
-        const float g = (q == 0) ? loc[tt] : pre * loc[tt];
-        const float inv = 1.f / g;
-        A[t * LDA + j] *= gprev;
-        R[t * LDA + j] *= g;
-        Bt[t * LDA + j] *= inv;
-        Kt[t * LDA + j] *= inv;
-        W[t * LDA + j] = g;
+        const float2 g = (q == 0) ? loc[tt] : make_float2(pre.x * loc[tt].x, pre.y * loc[tt].y);
+        const float ix = rcp(g.x), iy = rcp(g.y);
+        const float2 av = raw.get(raw.a[tt], tt, tid, 0.f), rv = raw.get(raw.r[tt], tt, tid, 0.f);
+        const float2 bv = raw.get(raw.b[tt], tt, tid, 0.f), kv = raw.get(raw.k[tt], tt, tid, 0.f);
+        const float ax = av.x * gprev.x, ay = av.y * gprev.y;
+        const float rx = rv.x * g.x, ry = rv.y * g.y;
+        const float bx = bv.x * ix, by = bv.y * iy;
+        const float kx = kv.x * ix, ky = kv.y * iy;
+        if (o.a) put2(o.A, t, j0, ax, ay);
+        if (o.r) put2(o.R, t, j0, rx, ry);
+        if (o.b) put2(o.B, t, j0, bx, by);
+        if (o.k) put2(o.K, t, j0, kx, ky);
+        if (o.gamma) *reinterpret_cast<float2*>(o.gamma + t * LDG + j0) = g;
+        gt[0][tt] = g.x; gt[1][tt] = g.y;
+        at[0][tt] = ax; at[1][tt] = ay;
+        rt[0][tt] = rx; rt[1][tt] = ry;
+        bt[0][tt] = bx; bt[1][tt] = by;
+        kt[0][tt] = kx; kt[1][tt] = ky;
         gprev = g;
     }
-    if (q == 0) glast[j] = tot;
-    __syncthreads();
+    if (q == NG - 1) {
+        o.glast[j0] = gt[0][TPG - 1];
+        o.glast[j0 + 1] = gt[1][TPG - 1];
+    }
+    // transposed copies: TPG consecutive tokens of one column per thread
+    const int t0 = q * TPG;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+#pragma unroll
+        for (int tt = 0; tt < TPG; tt += (TPG >= 4 ? 4 : TPG)) {
+            if constexpr (TPG >= 4) {
+                if (o.at) put4(o.AT, j0 + e, t0 + tt, f32x4{at[e][tt], at[e][tt + 1], at[e][tt + 2], at[e][tt + 3]});
+                if (o.rt) put4(o.RT, j0 + e, t0 + tt, f32x4{rt[e][tt], rt[e][tt + 1], rt[e][tt + 2], rt[e][tt + 3]});
+                if (o.bt) put4(o.BT, j0 + e, t0 + tt, f32x4{bt[e][tt], bt[e][tt + 1], bt[e][tt + 2], bt[e][tt + 3]});
+                if (o.kt) put4(o.KT, j0 + e, t0 + tt, f32x4{kt[e][tt], kt[e][tt + 1], kt[e][tt + 2], kt[e][tt + 3]});
+            } else {
+#pragma unroll
+                for (int u = 0; u < TPG; ++u) {
+                    if (o.at) put(o.AT, j0 + e, t0 + u, at[e][u]);
+                    if (o.rt) put(o.RT, j0 + e, t0 + u, rt[e][u]);
+                    if (o.bt) put(o.BT, j0 + e, t0 + u, bt[e][u]);
+                    if (o.kt) put(o.KT, j0 + e, t0 + u, kt[e][u]);
+                }
+            }
+        }
+    }
 }
 
-// Tinv = (I - L)^-1 for a strictly lower triangular C x C matrix L (row
-// stride LDC), by forward substitution; one wave, lane k < 32 owns column k.
-__device__ __forceinline__ void tri_inverse(const float* L, float* Tinv, int lane) {
-    if (lane < C) {
-        const int k = lane;
-        float x[C];
+// ---------------------------------------------------------------------------
+// Column block [col0, col0+NCOL) of one chunk of a (B,T,H,D) tensor, held in
+// registers: thread tid holds the pair of columns col0 + 2*(tid % (NCOL/2))
+// (+0, +1) for tokens tid / (NCOL/2) + s*(NT / (NCOL/2)), s = 0..PER-1.
+template <int NT, int NCOL, typename InT>
+struct RawCols {
+    static constexpr int PAIRS = NCOL / 2;
+    static constexpr int TSTEP = NT / PAIRS;          // tokens covered per sweep
+    static constexpr int PER = (C + TSTEP - 1) / TSTEP;
+    static_assert(NT % PAIRS == 0, "raw column thread shape");
+    using W = typename Pair<InT>::T;
+    W v[PER];
+    int cc;
+
+    __device__ __forceinline__ void load(const InT* src, int64_t base, int64_t tstride, int Cc, int col0, int tid) {
+        const int ip = tid % PAIRS, t1 = tid / PAIRS;
+        cc = Cc;
 #pragma unroll
-        for (int t = 0; t < C; ++t) {
-            float acc0 = (t == k) ? 1.f : 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+        for (int s = 0; s < PER; ++s) {
+            const int t = min(t1 + s * TSTEP, Cc - 1);
+            v[s] = Pair<InT>::load(src + base + t * tstride + col0 + 2 * ip);
+        }
+    }
+    __device__ __forceinline__ float2 value(int s, int tid) const {
+        const int t = tid / PAIRS + s * TSTEP;
+        return t < cc ? Pair<InT>::f(v[s]) : make_float2(0.f, 0.f);
+    }
+    // M[i][t] = value (transposed: row = column index i, k = token)
+    template <bool SPLIT, bool EXACT>
+    __device__ __forceinline__ void store_T(Mat<SPLIT> M, int tid) const {
+        const int ip = tid % PAIRS, t1 = tid / PAIRS;
 #pragma unroll
-            for (int s = 0; s < t; s += 4) {
-                acc0 = fmaf(L[t * LDC + s], x[s], acc0);
-                if (s + 1 < t) acc1 = fmaf(L[t * LDC + s + 1], x[s + 1], acc1);
-                if (s + 2 < t) acc2 = fmaf(L[t * LDC + s + 2], x[s + 2], acc2);
-                if (s + 3 < t) acc3 = fmaf(L[t * LDC + s + 3], x[s + 3], acc3);
+        for (int s = 0; s < PER; ++s) {
+            const int t = t1 + s * TSTEP;
+            if (t < C) {
+                const float2 x = value(s, tid);
+                if (EXACT) {
+                    put_exact(M, 2 * ip, t, x.x);
+                    put_exact(M, 2 * ip + 1, t, x.y);
+                } else {
+                    put(M, 2 * ip, t, x.x);
+                    put(M, 2 * ip + 1, t, x.y);
+                }
             }
-            x[t] = (acc0 + acc1) + (acc2 + acc3);
+        }
+    }
+    // M[t][i] = value (rows: row = token, k = column index)
+    template <bool SPLIT, bool EXACT>
+    __device__ __forceinline__ void store_rows(Mat<SPLIT> M, int tid) const {
+        const int ip = tid % PAIRS, t1 = tid / PAIRS;
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int t = t1 + s * TSTEP;
+            if (t < C) {
+                const float2 x = value(s, tid);
+                if (EXACT) put2_exact(M, t, 2 * ip, x.x, x.y);
+                else put2(M, t, 2 * ip, x.x, x.y);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// The chunk's C x C matrices.  Lab (strictly lower) goes to an fp32 array for
+// the triangular inverse; Lak (strict), Mrb, Mrk (lower) are stored as
+// operands, each in the orientation(s) the caller asks for (null = skip).
+// 12 lower tiles spread over the waves; the upper-right tiles are zeroed.
+// No barrier at the end.
+template <bool SPLIT, int NT>
+struct CcOut {
+    float* labf;  // null: Lab not wanted
+    Mat<SPLIT> lak, lakT, mrb, mrbT, mrk, mrkT;
+    bool has_lak, has_lakT, has_mrb, has_mrbT, has_mrk, has_mrkT;
+};
+
+// Store the three lower tiles of a C x C matrix as rows and/or transposed,
+// zeroing the upper-right tile.
+template <int MASK, bool SPLIT>
+__device__ __forceinline__ void cc_store(Mat<SPLIT> Mr, bool rows_, Mat<SPLIT> Mt, bool trans, f32x4 t00,
+                                         f32x4 t10, f32x4 t11, int lane) {
+    if (rows_) {
+        store_rows<MASK>(Mr, t00, 0, 0, lane);
+        store_rows<MASK>(Mr, t10, 16, 0, lane);
+        store_rows<MASK>(Mr, t11, 16, 16, lane);
+        zero_block(Mr, 0, 16, lane);
+    }
+    if (trans) {
+        store_cols<MASK>(Mt, t00, 0, 0, lane);
+        store_cols<MASK>(Mt, t10, 16, 0, lane);
+        store_cols<MASK>(Mt, t11, 16, 16, lane);
+        zero_block(Mt, 16, 0, lane);
+    }
+}
+
+template <bool SPLIT, int NT>
+__device__ __forceinline__ void chunk_cc(Mat<SPLIT> A, Mat<SPLIT> R, Mat<SPLIT> B, Mat<SPLIT> K,
+                                         const CcOut<SPLIT, NT>& o, int tid) {
+    static_assert(NT == 256, "one matrix per wave");
+    const int lane = tid & 63, wave = tid >> 6;
+    // wave 3: Lab (A, B); wave 0: Lak (A, K); wave 1: Mrb (R, B); wave 2: Mrk (R, K)
+    const int mat = wave == 3 ? 0 : wave + 1;
+    if (mat == 0 && !o.labf) return;
+    if (mat == 3 && !o.has_mrk && !o.has_mrkT) return;
+    const Mat<SPLIT> X = mat < 2 ? A : R;
+    const Mat<SPLIT> Y = (mat & 1) ? K : B;
+    // lower tiles (0,0), (1,0), (1,1), computed together
+    f32x4 t00 = zero4(), t10 = zero4(), t11 = zero4();
+    t00 = mma<SPLIT, D>(t00, X, 0, Y, 0, lane);
+    t10 = mma<SPLIT, D>(t10, X, 16, Y, 0, lane);
+    t11 = mma<SPLIT, D>(t11, X, 16, Y, 16, lane);
+    if (mat == 0) {
+        store_f32<MASK_STRICT>(o.labf, LDF, t00, 0, 0, lane);
+        store_f32<MASK_STRICT>(o.labf, LDF, t10, 16, 0, lane);
+        store_f32<MASK_STRICT>(o.labf, LDF, t11, 16, 16, lane);
+        for (int e = lane; e < 256; e += 64) o.labf[(e >> 4) * LDF + 16 + (e & 15)] = 0.f;
+        return;
+    }
+    // one uniform branch per matrix: no run-time selection between the handles
+    if (mat == 1) cc_store<MASK_STRICT>(o.lak, o.has_lak, o.lakT, o.has_lakT, t00, t10, t11, lane);
+    else if (mat == 2) cc_store<MASK_LOWER>(o.mrb, o.has_mrb, o.mrbT, o.has_mrbT, t00, t10, t11, lane);
+    else cc_store<MASK_LOWER>(o.mrk, o.has_mrk, o.mrkT, o.has_mrkT, t00, t10, t11, lane);
+}
+
+// ---------------------------------------------------------------------------
+// T = (I - L)^-1 for the strictly lower C x C matrix L (fp32, stride LDF), by
+// 16 x 16 blocks: T11 = (I - L11)^-1 and T22 = (I - L22)^-1 by forward
+// substitution (lanes 0..15 and 16..31, one column each), then
+// T21 = T22 (L21 T11) with two fp32 MFMA products.  One wave.  `tf` (fp32,
+// stride LDF) receives T; `scr` is 16 x 20 floats of scratch.
+__device__ __forceinline__ void tri_inverse(const float* L, float* tf, float* scr, int lane) {
+    if (lane < 32) {
+        const int k = lane & 15, base = lane & 16;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const float* Lrow = L + (base + t) * LDF + base;
+            float acc0 = (t == k) ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int s = 0; s < t; s += 2) {
+                acc0 = fmaf(Lrow[s], x[s], acc0);
+                if (s + 1 < t) acc1 = fmaf(Lrow[s + 1], x[s + 1], acc1);
+            }
+            x[t] = acc0 + acc1;
         }
 #pragma unroll
-        for (int t = 0; t < C; ++t) Tinv[t * LDC + k] = x[t];
+        for (int t = 0; t < 16; ++t) {
+            tf[(base + t) * LDF + base + k] = x[t];
+            if (base == 0) tf[t * LDF + 16 + k] = 0.f;
+        }
     }
+    wave_lds_sync();
+    // P = L21 T11  (row t-16, column n)
+    const int r = lane & 15, g = lane >> 4;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(L[(16 + r) * LDF + k0 + g], tf[(k0 + g) * LDF + r], acc, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) scr[(4 * g + q) * 20 + r] = acc[q];
+    wave_lds_sync();
+    // T21 = T22 P
+    acc = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tf[(16 + r) * LDF + 16 + k0 + g], scr[(k0 + g) * 20 + r], acc, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tf[(16 + 4 * g + q) * LDF + r] = acc[q];
+    wave_lds_sync();
 }
 
-// The four C x C matrices of a chunk: Lab, Lak (strictly lower), Mrb, Mrk
-// (lower incl. diagonal).  12 lower tiles spread over the waves, plus the
-// zero upper-right tile of each.  No barrier at the end.
-template <bool SPLIT, int NT>
-__device__ __forceinline__ void chunk_cc(const float* A, const float* R, const float* Bt, const float* Kt,
-                                         float* Lab, float* Lak, float* Mrb, float* Mrk, int tid) {
-    constexpr int NW = NT / 64;
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int job = wave; job < 12; job += NW) {
-        const int mat = job / 3, tile = job % 3;
-        const int ti = tile == 0 ? 0 : 1, tj = tile == 2 ? 1 : 0;
-        const Op X = rows(mat < 2 ? A : R, LDA);
-        const Op Y = rows((mat & 1) ? Kt : Bt, LDA);
-        const f32x4 acc = mma<SPLIT, D>(zero4(), X, ti * 16, Y, tj * 16, lane);
-        float* M = mat == 0 ? Lab : mat == 1 ? Lak : mat == 2 ? Mrb : Mrk;
-        if (mat < 2) store_tile<LDC, false, MASK_STRICT>(M, acc, ti * 16, tj * 16, lane);
-        else store_tile<LDC, false, MASK_LOWER>(M, acc, ti * 16, tj * 16, lane);
-    }
-    for (int e = tid; e < 4 * 256; e += NT) {
-        const int m = e >> 8, t = (e & 255) >> 4, s = 16 + (e & 15);
-        float* M = m == 0 ? Lab : m == 1 ? Lak : m == 2 ? Mrb : Mrk;
-        M[t * LDC + s] = 0.f;
+// Copy the fp32 C x C matrix tf into operand form: rows (T[t][s]) and/or
+// transposed (T[s][t]).  One wave.
+template <bool SPLIT>
+__device__ __forceinline__ void tinv_store(const float* tf, Mat<SPLIT> T, bool rows_, Mat<SPLIT> TT, bool trans,
+                                           int lane) {
+    // lane -> row t = lane / 2, columns 16*(lane%2) .. +15
+    const int t = lane >> 1, s0 = (lane & 1) * 16;
+#pragma unroll
+    for (int s4 = 0; s4 < 16; s4 += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tf + t * LDF + s0 + s4);
+        if (rows_) put4(T, t, s0 + s4, v);
+        if (trans) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) put(TT, s0 + s4 + q, t, v[q]);
+        }
     }
 }
 

@@ -9,6 +9,7 @@ namespace wkv7 {
 
 struct FwdArgs {
     const void *r, *w, *k, *v, *a, *b;
+    const float* inv;  // (B,H,NC,32,32): (I - Lab)^-1 of every chunk
     const float* h0;
     float* y;
     float* ckpt;
@@ -18,6 +19,7 @@ struct FwdArgs {
 
 struct BwdArgs {
     const void *r, *w, *k, *v, *a, *b;
+    const float* inv;  // (B,H,NC,32,32): (I - Lab)^-1 of every chunk
     const float* dy;
     const float* dhT;
     const float* ckpt;
@@ -27,7 +29,14 @@ struct BwdArgs {
     int B, T, H, NC;
 };
 
+struct InvArgs {
+    const void *w, *a, *b;
+    float* inv;  // output (B,H,NC,32,32)
+    int B, T, H, NC;
+};
+
 // Each returns hipSuccess or the launch error.
+hipError_t launch_chunk_inv(const InvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_fwd_chunked(const FwdArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_state(const BwdArgs& a, bool bf16, hipStream_t s);   // kernel 1

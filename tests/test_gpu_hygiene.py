@@ -85,10 +85,15 @@ def test_device_buffers_rejected_before_launch():
     ck = torch.empty(B, H, L.num_chunks(T), D, D, device=DEV)
     p = [t.data_ptr() for t in ins]
     s = torch.cuda.current_stream().cuda_stream
-    # y aliasing r, hT inside the checkpoints, misaligned y
-    assert lib.wkv7_fwd(B, T, H, D, 1, *p, None, p[0], ck.data_ptr(), None, s) == 5
-    assert lib.wkv7_fwd(B, T, H, D, 1, *p, None, y.data_ptr(), ck.data_ptr(), ck.data_ptr() + 64, s) == 5
-    assert lib.wkv7_fwd(B, T, H, D, 1, *p, None, y.data_ptr() + 4, ck.data_ptr(), None, s) == 4
+    wsb = L.fwd_workspace_bytes(B, T, H)
+    fws = torch.empty(wsb // 4, device=DEV)
+    w_ = (fws.data_ptr(), wsb)
+    # y aliasing r, hT inside the checkpoints, misaligned y, workspace too small
+    assert lib.wkv7_fwd(B, T, H, D, 1, *p, None, p[0], ck.data_ptr(), None, *w_, s) == 5
+    assert lib.wkv7_fwd(B, T, H, D, 1, *p, None, y.data_ptr(), ck.data_ptr(), ck.data_ptr() + 64, *w_, s) == 5
+    assert lib.wkv7_fwd(B, T, H, D, 1, *p, None, y.data_ptr() + 4, ck.data_ptr(), None, *w_, s) == 4
+    assert lib.wkv7_fwd(B, T, H, D, 1, *p, None, y.data_ptr(), ck.data_ptr(), None, fws.data_ptr(), wsb - 4,
+                        s) == 7
     ws = torch.empty(16, device=DEV)
     with pytest.raises(L.Wkv7Error, match="workspace"):
         L.bwd(dy, *ins, ck, None, workspace=ws)

@@ -124,3 +124,29 @@ def test_split_sequence_state_passing():
     cat = torch.cat([y1, y2], dim=1)
     assert (cat - y).norm() / y.norm() < 1e-5
     assert (h2 - hT).norm() / hT.norm() < 1e-5
+
+
+@pytest.mark.parametrize("dtype,T", [(F32, 70), (BF16, 64), (BF16, 5)])
+def test_chunk_inverse_matches_direct_solve(dtype, T):
+    """(I - L)^-1 of every chunk against numpy's inverse of the same L built in
+    float64 from the same (rounded) inputs."""
+    x = make_inputs(2, T, 3, dtype, seed=300 + T)
+    dev = torch.device("cuda:0")
+    note(f"chunk inverse {dtype} T{T}")
+    inv = L.chunk_inverse(x.w.to(dev), x.a.to(dev), x.b.to(dev)).double().cpu().numpy()
+    w, a, b = (t.double().numpy() for t in (x.w, x.a, x.b))
+    B, _, H, D = w.shape
+    worst = 0.0
+    for bb in range(B):
+        for hh in range(H):
+            for c in range(inv.shape[2]):
+                sl = slice(32 * c, min(T, 32 * c + 32))
+                n = sl.stop - sl.start
+                W = np.ones((32, D)); A = np.zeros((32, D)); Bv = np.zeros((32, D))
+                W[:n], A[:n], Bv[:n] = w[bb, sl, hh], a[bb, sl, hh], b[bb, sl, hh]
+                g = np.cumprod(W, axis=0)
+                gp = np.vstack([np.ones((1, D)), g[:-1]])
+                Lm = np.tril((A * gp) @ (Bv / g).T, -1)
+                ref = np.linalg.inv(np.eye(32) - Lm)
+                worst = max(worst, np.linalg.norm(inv[bb, hh, c] - ref) / np.linalg.norm(ref))
+    assert worst < (1e-6 if dtype == F32 else 2e-5), worst
