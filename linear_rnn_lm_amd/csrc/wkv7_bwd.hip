@@ -555,14 +555,40 @@ __global__ __launch_bounds__(NT) void bwd_chunk_kernel(BwdArgs p, int xcd) {
         }
     }
 
-    // ---- dw: phi_t = diag(Gs^T S0) - sum_{s<=t} a da + sum_{s<t} (k dk + b db - r dr)
-    if (tid < 64) {
-        const int j = tid;
-        float acc = red[j] + red[64 + j] + red[128 + j] + red[192 + j];
-        for (int t = 0; t < Cc; ++t) {
-            const int64_t o = base + t * tstride + j;
-            p.dw[o] = (acc - fa_[t * LDG + j]) / load1(gw + o);
-            acc += hh_[t * LDG + j];
+    // ---- dw: phi_t = diag(Gs^T S0) - sum_{s<=t} a da + sum_{s<t} (k dk + b db - r dr),
+    //      dw_t = phi_t / w_t.  Thread (jp, q) scans tokens 4q..4q+3 of columns 2jp, 2jp+1.
+    {
+        constexpr int TPG = RawChunk<NT, InT>::TPG;
+        const int jp = tid & 31, q = tid >> 5, j0 = 2 * jp;
+        float2 hx[TPG], fx[TPG];
+        float2 tot = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int tt = 0; tt < TPG; ++tt) {
+            const int t = q * TPG + tt;
+            hx[tt] = *reinterpret_cast<const float2*>(hh_ + t * LDG + j0);
+            fx[tt] = *reinterpret_cast<const float2*>(fa_ + t * LDG + j0);
+            tot.x += hx[tt].x;
+            tot.y += hx[tt].y;
+        }
+        qp[q * 64 + j0] = tot.x;
+        qp[q * 64 + j0 + 1] = tot.y;
+        lds_barrier();
+        float2 acc = make_float2(red[j0] + red[64 + j0] + red[128 + j0] + red[192 + j0],
+                                 red[j0 + 1] + red[64 + j0 + 1] + red[128 + j0 + 1] + red[192 + j0 + 1]);
+        for (int q2 = 0; q2 < q; ++q2) {
+            acc.x += qp[q2 * 64 + j0];
+            acc.y += qp[q2 * 64 + j0 + 1];
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPG; ++tt) {
+            const int t = q * TPG + tt;
+            if (t < Cc) {
+                const float2 wv = Pair<InT>::f(raw.w[tt]);
+                *reinterpret_cast<float2*>(p.dw + base + t * tstride + j0) =
+                    make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y));
+            }
+            acc.x += hx[tt].x;
+            acc.y += hx[tt].y;
         }
     }
 }

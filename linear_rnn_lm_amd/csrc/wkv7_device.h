@@ -113,15 +113,20 @@ __device__ __forceinline__ float get(Mat<false> M, int m, int k) {
     return reinterpret_cast<const float*>(M.p)[m * M.ld + k];
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// split of two values with packed conversions: hi = rn(v), lo = rn(v - hi)
+__device__ __forceinline__ void split2(f32x2 v, bf16x2& hi, bf16x2& lo) {
+    hi = __builtin_convertvector(v, bf16x2);
+    const f32x2 back = __builtin_convertvector(hi, f32x2);
+    lo = __builtin_convertvector(v - back, bf16x2);
+}
+
 // elements (m, k..k+1) <- v0, v1   (k even)
 __device__ __forceinline__ void put2(Mat<true> M, int m, int k, float v0, float v1) {
     __bf16* h = reinterpret_cast<__bf16*>(M.p) + m * M.ld + k;
     bf16x2 hi, lo;
-    __bf16 a, b;
-    split1(v0, a, b);
-    hi[0] = a; lo[0] = b;
-    split1(v1, a, b);
-    hi[1] = a; lo[1] = b;
+    split2(f32x2{v0, v1}, hi, lo);
     *reinterpret_cast<bf16x2*>(h) = hi;
     *reinterpret_cast<bf16x2*>(h + M.plane) = lo;
 }
@@ -139,16 +144,11 @@ __device__ __forceinline__ void put2_exact(Mat<false> M, int m, int k, float v0,
 // elements (m, k..k+3) <- v   (k % 4 == 0)
 __device__ __forceinline__ void put4(Mat<true> M, int m, int k, f32x4 v) {
     __bf16* h = reinterpret_cast<__bf16*>(M.p) + m * M.ld + k;
-    bf16x4 hi, lo;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        __bf16 a, b;
-        split1(v[q], a, b);
-        hi[q] = a;
-        lo[q] = b;
-    }
-    *reinterpret_cast<bf16x4*>(h) = hi;
-    *reinterpret_cast<bf16x4*>(h + M.plane) = lo;
+    bf16x2 h0, l0, h1, l1;
+    split2(f32x2{v[0], v[1]}, h0, l0);
+    split2(f32x2{v[2], v[3]}, h1, l1);
+    *reinterpret_cast<bf16x4*>(h) = bf16x4{h0[0], h0[1], h1[0], h1[1]};
+    *reinterpret_cast<bf16x4*>(h + M.plane) = bf16x4{l0[0], l0[1], l1[0], l1[1]};
 }
 __device__ __forceinline__ void put4(Mat<false> M, int m, int k, f32x4 v) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(M.p) + m * M.ld + k) = v;
