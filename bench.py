@@ -58,6 +58,64 @@ def kernel_bytes(wl, in_bytes: int) -> dict:
     }
 
 
+KERNEL_NAMES = {"chunk_inv_kernel": "chunk_inverse", "fwd_chunked_kernel": "fwd",
+                "bwd_state_kernel": "bwd_state", "bwd_chunk_kernel": "bwd_inputs"}
+COPY_MIB = 256
+
+
+def copy_calibration(dev, reps: int = 3) -> None:
+    """A plain device copy of known size (256 MiB read, 256 MiB written, as a
+    negation so that it is one elementwise kernel and not a DMA): the reference
+    that scales the HBM byte counters of the other kernels."""
+    import torch
+    src = torch.ones(COPY_MIB << 18, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _pmc_rows(d: str):
+    import csv
+    import glob
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def traffic_from(d: str, workload: str) -> dict:
+    """HBM bytes per launch of every kernel from two rocprofv3 --pmc runs
+    (d/fetch: FETCH_SIZE, d/write: WRITE_SIZE, KiB per dispatch), each scaled
+    by what the same counter reads for the 256 MiB copy."""
+    from linear_rnn_lm_amd.inputs import WORKLOADS
+    wl = WORKLOADS[workload]
+    meas = {}
+    for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        vals = {}
+        for r in _pmc_rows(os.path.join(d, sub)):
+            if r["Counter_Name"] != ctr:
+                continue
+            name = r["Kernel_Name"]
+            key = "copy" if "neg" in name else next((v for k, v in KERNEL_NAMES.items() if k in name), None)
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        if "copy" not in vals:
+            raise RuntimeError(f"no copy kernel in the {ctr} run under {d}")
+        scale = (COPY_MIB * 1024) / (sum(vals["copy"]) / len(vals["copy"]))
+        meas[ctr] = {k: sum(v) / len(v) * 1024 * scale for k, v in vals.items() if k != "copy"}
+        meas[ctr + "_copy_scale"] = scale
+    kb = kernel_bytes(wl, 2 if str(wl.dtype).endswith("bfloat16") else 4)
+    out = {"copy_scale": {"FETCH_SIZE": meas["FETCH_SIZE_copy_scale"], "WRITE_SIZE": meas["WRITE_SIZE_copy_scale"]},
+           "source_digest": source_digest(), "kernels": {}}
+    for k in KERNEL_NAMES.values():
+        fb, wb = meas["FETCH_SIZE"].get(k), meas["WRITE_SIZE"].get(k)
+        if fb is None or wb is None:
+            continue
+        out["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                             "algorithmic_bytes": kb[k], "ratio": (fb + wb) / kb[k]}
+    return out
+
+
 def cpu_baseline(wl, budget_s: float) -> dict:
     """The oracle, as it stands, on the host cores: whole fwd+bwd passes of the
     workload (a subset of heads if one pass would exceed the budget)."""
@@ -98,7 +156,22 @@ def main() -> int:
     ap.add_argument("--workload", default="debug_36m")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="no GPU work: write profiles/traffic.json from rocprofv3 --pmc runs in DIR/fetch, DIR/write")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        tr = {}
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f)
+        tr[args.workload] = traffic_from(args.traffic_from, args.workload)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(tr, f, indent=1, sort_keys=True)
+        print(json.dumps(tr[args.workload], indent=1))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported. "
@@ -111,6 +184,8 @@ def main() -> int:
     from linear_rnn_lm_amd.inputs import WORKLOADS, workload_inputs
 
     wl = WORKLOADS[args.workload]
+    if args.copy_calibration:
+        copy_calibration(torch.device("cuda:0"))
     if wl.T == 1:
         print("bench.py: the one-token recurrent-step workload is measured by its own benchmark "
               "(forward only); pick a training workload", file=sys.stderr)
@@ -201,9 +276,9 @@ def main() -> int:
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        ent = tr.get(args.workload, {}).get(dom)
-        if ent and ent.get("source_digest") == source_digest():
-            traffic = ent["bytes_per_launch"]
+        ent = tr.get(args.workload, {})
+        if ent.get("source_digest") == source_digest() and dom in ent.get("kernels", {}):
+            traffic = ent["kernels"][dom]["bytes_per_launch"]
     except (OSError, ValueError):
         pass
 

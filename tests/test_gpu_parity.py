@@ -42,6 +42,7 @@ def test_small_shapes(B, T, H, dtype, with_h0, with_dhT):
     g = run_gpu(x, dhT)
     o = run_oracle(x, dhT)
     errs, bad = compare(g, o, dtype)
+    note(f"rel-L2 {errs}")
     assert not bad, f"over tolerance: {bad}; errors {errs}"
 
 
@@ -50,6 +51,7 @@ def test_tiny_fp32_workload():
     x = workload_inputs(wl)
     note("workload tiny_fp32")
     errs, bad = compare(run_gpu(x), run_oracle(x), wl.dtype)
+    note(f"rel-L2 {errs}")
     assert not bad, errs
 
 
@@ -62,6 +64,7 @@ def test_training_workload_full(name):
     g = run_gpu(x)
     o = run_oracle(x)
     errs, bad = compare(g, o, wl.dtype)
+    note(f"rel-L2 {errs}")
     assert not bad, errs
 
 
@@ -75,6 +78,7 @@ def test_rwkv_1b5_sampled_heads():
     bsel, hsel = [0, 7, 3], [0, 31]
     o = run_oracle(slice_heads(x, bsel, hsel))
     errs, bad = compare(select_heads(g, bsel, hsel), o, wl.dtype)
+    note(f"rel-L2 {errs}")
     assert not bad, errs
     for n in ("y", "dr", "dw", "dk", "dv", "da", "db"):
         assert np.isfinite(g[n]).all(), n
@@ -95,6 +99,7 @@ def test_rwkv_7b_step_layer(layer):
     o = run_oracle(x, bwd=False)
     errs, bad = compare({"y": y.double().cpu().numpy(), "hT": state.double().cpu().numpy()}, o, wl.dtype,
                         names=["y", "hT"])
+    note(f"rel-L2 {errs}")
     assert not bad, errs
 
 
@@ -105,6 +110,7 @@ def test_sequential_path_matches_oracle(T):
     g = run_gpu(x, sequential=True, bwd=False)
     o = run_oracle(x, bwd=False)
     errs, bad = compare(g, o, BF16)
+    note(f"rel-L2 {errs}")
     assert not bad, errs
 
 
