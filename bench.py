@@ -1,9 +1,10 @@
 """Throughput of the WKV7 forward + backward on one MI355X.
 
-One step = the whole hot path over one batch: wkv7_fwd (y, checkpoints, final
-state), then the backward (state-gradient pass, then the per-token input
-gradients) for a loss gradient dy.  Inputs are seeded synthetic tensors of the
-workload's shape, resident in HBM before timing starts.
+One step = the whole hot path over one batch: the per-chunk operands (shared
+by forward and backward), the forward scan (y, checkpoints, final state), the
+backward scan (state gradient at every chunk boundary, dv), then the per-token
+input gradients, for a loss gradient dy.  Inputs are seeded synthetic tensors
+of the workload's shape, resident in HBM before timing starts.
 
 Prints one JSON line.  Default workload: B12 T1024 H6 D64, bf16 inputs
 (the 36M "debug" training layer).
@@ -26,6 +27,7 @@ HBM_PEAK_GBS = 8000.0
 D = 64
 CSRC = os.path.join(ROOT, "linear_rnn_lm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+OPS_BYTES = 36864      # transition operands P, M, E, F of one chunk of one head
 
 
 def source_digest() -> str:
@@ -47,19 +49,30 @@ def kernel_bytes(wl, in_bytes: int) -> dict:
     st = heads * D * D * 4
     ck = heads * nc * D * D * 4
     inv = heads * nc * 32 * 32 * 4
+    ops = heads * nc * OPS_BYTES
     h0 = st if wl.with_h0 else 0
     return {
-        "chunk_inverse": 3 * tok_in + inv,
-        "fwd": 6 * tok_in + inv + tok32 + ck + h0 + st,
-        "bwd_state": 5 * tok_in + inv + tok32 + tok32 + ck + st,
+        "chunk_prepare": 5 * tok_in + inv + ops,
+        "fwd_scan": tok_in + ops + h0 + tok32 + ck + st,
+        "bwd_scan": tok32 + ops + tok32 + ck + st,
         "bwd_inputs": 6 * tok_in + inv + tok32 + 2 * ck + 5 * tok32,
         # whole path, algorithmic: fwd 1536 B and bwd 3072 B per head-token (bf16 inputs)
         "path": (6 * tok_in + tok32 + ck + h0 + st) + (6 * tok_in + tok32 + ck + 6 * tok32 + st),
     }
 
 
-KERNEL_NAMES = {"chunk_inv_kernel": "chunk_inverse", "fwd_chunked_kernel": "fwd",
-                "bwd_state_kernel": "bwd_state", "bwd_chunk_kernel": "bwd_inputs"}
+def kernel_key(name: str):
+    """bench key of a kernel name as the profiler prints it (None: not ours)."""
+    if "chunk_prepare_kernel" in name:
+        return "chunk_prepare"
+    if "scan_kernel" in name:
+        return "bwd_scan" if ", true>(" in name else "fwd_scan"
+    if "bwd_chunk_kernel" in name:
+        return "bwd_inputs"
+    return None
+
+
+KERNEL_KEYS = ("chunk_prepare", "fwd_scan", "bwd_scan", "bwd_inputs")
 COPY_MIB = 256
 
 
@@ -96,7 +109,7 @@ def traffic_from(d: str, workload: str) -> dict:
             if r["Counter_Name"] != ctr:
                 continue
             name = r["Kernel_Name"]
-            key = "copy" if "neg" in name else next((v for k, v in KERNEL_NAMES.items() if k in name), None)
+            key = "copy" if "neg" in name else kernel_key(name)
             if key:
                 vals.setdefault(key, []).append(float(r["Counter_Value"]))
         if "copy" not in vals:
@@ -107,7 +120,7 @@ def traffic_from(d: str, workload: str) -> dict:
     kb = kernel_bytes(wl, 2 if str(wl.dtype).endswith("bfloat16") else 4)
     out = {"copy_scale": {"FETCH_SIZE": meas["FETCH_SIZE_copy_scale"], "WRITE_SIZE": meas["WRITE_SIZE_copy_scale"]},
            "source_digest": source_digest(), "kernels": {}}
-    for k in KERNEL_NAMES.values():
+    for k in KERNEL_KEYS:
         fb, wb = meas["FETCH_SIZE"].get(k), meas["WRITE_SIZE"].get(k)
         if fb is None or wb is None:
             continue
@@ -203,7 +216,7 @@ def main() -> int:
     ck = torch.empty(B, H, nc, D, D, **f32)
     hT = torch.empty(B, H, D, D, **f32)
     dck = torch.empty(B, H, nc, D, D, **f32)
-    inv = torch.empty(B, H, nc, 32, 32, **f32)
+    ops = torch.empty(L.chunk_ops_bytes(B, T, H) // 4, **f32)
     dv = torch.empty(B, T, H, D, **f32)
     dh0 = torch.empty(B, H, D, D, **f32)
     grads = [torch.empty(B, T, H, D, **f32) for _ in range(5)]
@@ -214,29 +227,29 @@ def main() -> int:
     p = [t.data_ptr() for t in ins]
     ph0 = None if h0 is None else h0.data_ptr()
 
-    pinv = inv.data_ptr()
+    pops = ops.data_ptr()
 
-    def k_inv():
-        st = lib.wkv7_chunk_inverse(B, T, H, D, code, p[1], p[4], p[5], pinv, sh)
+    def k_prep():
+        st = lib.wkv7_chunk_prepare(B, T, H, D, code, p[0], p[1], p[2], p[4], p[5], pops, sh)
         assert st == 0, lib.wkv7_status_str(st)
 
     def k_fwd():
-        st = lib.wkv7_fwd_chunks(B, T, H, D, code, *p, pinv, ph0, y.data_ptr(), ck.data_ptr(), hT.data_ptr(), sh)
+        st = lib.wkv7_fwd_scan(B, T, H, D, code, p[3], pops, ph0, y.data_ptr(), ck.data_ptr(), hT.data_ptr(), sh)
         assert st == 0, lib.wkv7_status_str(st)
 
-    def k_state():
-        st = lib.wkv7_bwd_state(B, T, H, D, code, dy.data_ptr(), None, p[0], p[1], p[2], p[4], p[5], pinv,
-                                dck.data_ptr(), dv.data_ptr(), dh0.data_ptr(), sh)
+    def k_bscan():
+        st = lib.wkv7_bwd_scan(B, T, H, D, code, dy.data_ptr(), None, pops, dck.data_ptr(), dv.data_ptr(),
+                               dh0.data_ptr(), sh)
         assert st == 0, lib.wkv7_status_str(st)
 
     def k_inputs():
-        st = lib.wkv7_bwd_inputs(B, T, H, D, code, dy.data_ptr(), None, *p, pinv, ck.data_ptr(), dck.data_ptr(),
+        st = lib.wkv7_bwd_inputs(B, T, H, D, code, dy.data_ptr(), None, *p, pops, ck.data_ptr(), dck.data_ptr(),
                                  *[g.data_ptr() for g in grads], sh)
         assert st == 0, lib.wkv7_status_str(st)
 
-    # one training step: the chunk inverses (shared by forward and backward), the
-    # forward, the state-gradient pass, the input gradients
-    kernels = [("chunk_inverse", k_inv), ("fwd", k_fwd), ("bwd_state", k_state), ("bwd_inputs", k_inputs)]
+    # one training step: the chunk operands (shared by forward and backward),
+    # the forward scan, the backward scan, the input gradients
+    kernels = [("chunk_prepare", k_prep), ("fwd_scan", k_fwd), ("bwd_scan", k_bscan), ("bwd_inputs", k_inputs)]
 
     def step():
         for _, fn in kernels:
@@ -299,7 +312,7 @@ def main() -> int:
         "config": {"workload": f"{wl.name}: WKV7 fwd+bwd {wl.description}, chunk 32",
                    "B": B, "T": T, "H": H, "D": D,
                    "in_dtype": "bf16" if in_bytes == 2 else "f32", "state_dtype": "f32"},
-        "fwd_tokens_per_s": tokens / ((per_kernel_ms["fwd"] + per_kernel_ms["chunk_inverse"]) * 1e-3),
+        "fwd_tokens_per_s": tokens / ((per_kernel_ms["fwd_scan"] + per_kernel_ms["chunk_prepare"]) * 1e-3),
         "kernel_ms": per_kernel_ms,
         "path_hbm": {"algorithmic_bytes": kb["path"],
                      "achieved_GBs": kb["path"] / (ms_per_step * 1e-3) / 1e9,

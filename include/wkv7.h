@@ -86,34 +86,48 @@ int64_t wkv7_num_chunks(int64_t T);
 /* Static string naming a status code (never NULL). */
 const char *wkv7_status_str(int status);
 
-/* Bytes of the per-chunk inverses: B*H*NC*32*32*4.  0 for invalid shapes. */
-size_t wkv7_chunk_inv_bytes(int B, int T, int H, int D);
+/* Bytes of the chunk operands (see wkv7_chunk_prepare): B*H*NC*(4096 + 36864).
+ * 0 for invalid shapes. */
+size_t wkv7_chunk_ops_bytes(int B, int T, int H, int D);
 
-/* Bytes of device workspace wkv7_fwd needs: wkv7_chunk_inv_bytes(...) when
+/* Bytes of device workspace wkv7_fwd needs: wkv7_chunk_ops_bytes(...) when
  * T > 1, else 0.  0 for invalid shapes. */
 size_t wkv7_fwd_workspace_bytes(int B, int T, int H, int D);
 
 /* Bytes of device workspace wkv7_bwd needs: one fp32 D x D state gradient per
- * chunk (B*H*NC*D*D*4) plus wkv7_chunk_inv_bytes(...).  0 for invalid shapes. */
+ * chunk (B*H*NC*D*D*4) plus wkv7_chunk_ops_bytes(...).  0 for invalid shapes. */
 size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int D);
 
 /*
- * Per-chunk factor of the chunked evaluation.  Within chunk c (tokens
- * 32c .. 32c+31; a shorter last chunk is padded with w = 1, a = b = 0) let
- * g_t be the running product of w over the chunk's tokens up to t, and
- *     L[t][s] = sum_j a_t[j] g_{t-1}[j] b_s[j] / g_s[j]   for s < t, else 0
- * (the coupling of token s's b into token t's sa through the decays in
- * between; rwkv-mlx page, "Metal kernel architecture", forward block, unrolled
- * over one chunk).  Writes chunk_inv[b][h][c] = (I - L)^-1, 32 x 32 fp32,
- * row-major: (B, H, NC, 32, 32).  It depends on w, a, b only, so the forward
- * and the backward of one step may share it.
+ * Per-chunk operands of the chunked evaluation: everything about a chunk
+ * that depends on its r, w, k, a, b but not on the state.  Within chunk c
+ * (tokens 32c .. 32c+31; a shorter last chunk is padded with w = 1 and
+ * r = k = a = b = 0) let g_t be the running product of w over the chunk's
+ * tokens up to t.  Unrolling the forward block of the rwkv-mlx page ("Metal
+ * kernel architecture") over the chunk gives, for the state S0 entering the
+ * chunk and the chunk's v rows V,
+ *     S_end = S0 P + V^T M,      Y = E S0^T + F V,
+ * and for the backward block, with G the gradient at the chunk's end,
+ *     G_start = G P^T + DY^T E,  dv = M G^T + F^T DY,
+ * where P (D x D), M, E (32 x D) and F (32 x 32) depend on r, w, k, a, b only
+ * (through the decays g and the 32 x 32 coupling
+ *     L[t][s] = sum_j a_t[j] g_{t-1}[j] b_s[j] / g_s[j]  for s < t
+ * of token s's b into token t's sa; P, M, E, F involve (I - L)^-1).
  *
- *   w, a, b   : (B,T,H,D), in_dtype, required.
- *   chunk_inv : output, required, wkv7_chunk_inv_bytes(...) bytes.
+ * chunk_ops receives, in this order:
+ *   (B, H, NC, 32, 32) fp32: (I - L)^-1 of every chunk, row-major;
+ *   (B, H, NC) blocks of 36864 bytes: P, M, E, F of every chunk, in a
+ *   library-internal format (bf16 hi/lo planes for bf16 inputs, fp32 for
+ *   fp32 inputs).  Only this library's kernels read them.
+ * The forward and the backward of one step may share one chunk_ops.
+ *
+ *   r, w, k, a, b : (B,T,H,D), in_dtype, required.
+ *   chunk_ops     : output, required, wkv7_chunk_ops_bytes(...) bytes.
  */
-wkv7_status wkv7_chunk_inverse(int B, int T, int H, int D, wkv7_dtype in_dtype,
-                               const void *w, const void *a, const void *b,
-                               float *chunk_inv, void *stream);
+wkv7_status wkv7_chunk_prepare(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                               const void *r, const void *w, const void *k,
+                               const void *a, const void *b,
+                               void *chunk_ops, void *stream);
 
 /*
  * Forward (rwkv-mlx page, "Metal kernel architecture", forward block).
@@ -128,9 +142,9 @@ wkv7_status wkv7_chunk_inverse(int B, int T, int H, int D, wkv7_dtype in_dtype,
  *                      not otherwise overlap h0.
  *   workspace        : device scratch of wkv7_fwd_workspace_bytes(...) bytes;
  *                      may be NULL when that is 0 (T == 1).  Clobbered; on
- *                      return it holds the chunk inverses (wkv7_chunk_inverse).
+ *                      return it holds the chunk operands (wkv7_chunk_prepare).
  * At least one of y, h_ckpt, hT must be non-NULL.
- * Equivalent to wkv7_chunk_inverse into the workspace, then wkv7_fwd_chunks.
+ * Equivalent to wkv7_chunk_prepare into the workspace, then wkv7_fwd_scan.
  */
 wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
                      const void *r, const void *w, const void *k,
@@ -139,14 +153,14 @@ wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Forward given the chunk inverses (from wkv7_chunk_inverse for the same w,
- * a, b).  Arguments as wkv7_fwd; chunk_inv is required.
+ * Forward given the chunk operands (from wkv7_chunk_prepare for the same r, w,
+ * k, a, b): the state is carried from chunk to chunk, S_end = S0 P + V^T M,
+ * and every chunk's y = E S0^T + F V.  Arguments as wkv7_fwd; chunk_ops is
+ * required.
  */
-wkv7_status wkv7_fwd_chunks(int B, int T, int H, int D, wkv7_dtype in_dtype,
-                            const void *r, const void *w, const void *k,
-                            const void *v, const void *a, const void *b,
-                            const float *chunk_inv, const float *h0,
-                            float *y, float *h_ckpt, float *hT, void *stream);
+wkv7_status wkv7_fwd_scan(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                          const void *v, const void *chunk_ops, const float *h0,
+                          float *y, float *h_ckpt, float *hT, void *stream);
 
 /*
  * Backward (rwkv-mlx page, "Metal kernel architecture", backward block:
@@ -163,8 +177,9 @@ wkv7_status wkv7_fwd_chunks(int B, int T, int H, int D, wkv7_dtype in_dtype,
  *   workspace        : device scratch of at least
  *                      wkv7_bwd_workspace_bytes(B,T,H,D) bytes, required; its
  *                      contents on entry do not matter and are clobbered.
- * Equivalent to wkv7_chunk_inverse, wkv7_bwd_state (the workspace's first
- * part as dh_ckpt), then wkv7_bwd_inputs.
+ * Equivalent to wkv7_chunk_prepare (into the workspace after its first
+ * part), wkv7_bwd_scan (the workspace's first part as dh_ckpt), then
+ * wkv7_bwd_inputs.
  */
 wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
                      const float *dy, const float *dhT,
@@ -177,24 +192,22 @@ wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
                      void *stream);
 
 /*
- * Backward, first stage: the gradient of the loss w.r.t. the state at every
- * chunk boundary, walking the chunks in reverse (rwkv-mlx page, "Metal kernel
- * architecture", backward block).  Needs neither v nor the checkpoints: the
- * state gradient obeys its own recurrence, driven by dy, r, w, a, b.
+ * Backward, first stage: the gradient w.r.t. the state at every chunk
+ * boundary, walking the chunks in reverse (rwkv-mlx page, "Metal kernel
+ * architecture", backward block), and dv.  The state gradient obeys its own
+ * recurrence, driven by dy and the chunk operands: G_start = G P^T + DY^T E,
+ * dv = M G^T + F^T DY.  Needs neither the inputs nor the checkpoints.
  *
- *   dy, dhT, r, w, k, a, b : as for wkv7_bwd.
- *   chunk_inv: from wkv7_chunk_inverse for the same w, a, b, required.
+ *   dy, dhT  : as for wkv7_bwd.
+ *   chunk_ops: from wkv7_chunk_prepare for the forward's r, w, k, a, b.
  *   dh_ckpt  : (B,H,NC,D,D) fp32 output, required: dh_ckpt[c] is the gradient
  *              w.r.t. checkpoint c (the state entering chunk c).
  *   dv       : (B,T,H,D) fp32 output (the gradient w.r.t. v), or NULL.
  *   dh0      : (B,H,D,D) fp32 output (equals dh_ckpt[0]), or NULL.
  */
-wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype,
-                           const float *dy, const float *dhT,
-                           const void *r, const void *w, const void *k,
-                           const void *a, const void *b, const float *chunk_inv,
-                           float *dh_ckpt, float *dv, float *dh0,
-                           void *stream);
+wkv7_status wkv7_bwd_scan(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                          const float *dy, const float *dhT, const void *chunk_ops,
+                          float *dh_ckpt, float *dv, float *dh0, void *stream);
 
 /*
  * Backward, second stage: dr, dw, dk, da, db for every token, all chunks in
@@ -202,15 +215,16 @@ wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype,
  * dividing by w).
  *
  *   dy, dhT, r..b, h_ckpt : as for wkv7_bwd.
- *   chunk_inv: from wkv7_chunk_inverse for the same w, a, b, required.
- *   dh_ckpt  : (B,H,NC,D,D) written by wkv7_bwd_state for the same inputs.
+ *   chunk_ops: from wkv7_chunk_prepare for the same inputs, required (only
+ *              its (I - L)^-1 part is read).
+ *   dh_ckpt  : (B,H,NC,D,D) written by wkv7_bwd_scan for the same inputs.
  *   dr, dw, dk, da, db : (B,T,H,D) fp32 outputs, required.
  */
 wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype,
                             const float *dy, const float *dhT,
                             const void *r, const void *w, const void *k,
                             const void *v, const void *a, const void *b,
-                            const float *chunk_inv, const float *h_ckpt,
+                            const void *chunk_ops, const float *h_ckpt,
                             const float *dh_ckpt,
                             float *dr, float *dw, float *dk, float *da, float *db,
                             void *stream);

@@ -18,9 +18,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["lib", "fwd", "fwd_sequential", "fwd_chunks", "chunk_inverse", "bwd", "bwd_state",
+__all__ = ["lib", "fwd", "fwd_sequential", "fwd_scan", "chunk_prepare", "chunk_inverse", "bwd", "bwd_scan",
            "bwd_inputs", "step", "WKV7", "Wkv7Error",
-           "num_chunks", "workspace_bytes", "CHUNK", "HEAD_SIZE"]
+           "num_chunks", "workspace_bytes", "chunk_ops_bytes", "CHUNK", "HEAD_SIZE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwkv7.so")
@@ -52,21 +52,21 @@ def lib():
         L.wkv7_num_chunks.restype = i64
         L.wkv7_status_str.argtypes = [i]
         L.wkv7_status_str.restype = ctypes.c_char_p
-        for q in ("wkv7_bwd_workspace_bytes", "wkv7_fwd_workspace_bytes", "wkv7_chunk_inv_bytes"):
+        for q in ("wkv7_bwd_workspace_bytes", "wkv7_fwd_workspace_bytes", "wkv7_chunk_ops_bytes"):
             getattr(L, q).argtypes = [i, i, i, i]
             getattr(L, q).restype = sz
-        L.wkv7_chunk_inverse.argtypes = [i, i, i, i, i] + [vp] * 3 + [vp] + [vp]
-        L.wkv7_chunk_inverse.restype = i
+        L.wkv7_chunk_prepare.argtypes = [i, i, i, i, i] + [vp] * 5 + [vp] + [vp]
+        L.wkv7_chunk_prepare.restype = i
         L.wkv7_fwd.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 4 + [vp, sz] + [vp]
         L.wkv7_fwd.restype = i
-        L.wkv7_fwd_chunks.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 5 + [vp]
-        L.wkv7_fwd_chunks.restype = i
+        L.wkv7_fwd_scan.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 4 + [vp]
+        L.wkv7_fwd_scan.restype = i
         L.wkv7_fwd_sequential.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 4 + [vp]
         L.wkv7_fwd_sequential.restype = i
         L.wkv7_bwd.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] + [vp] * 7 + [vp, sz, vp]
         L.wkv7_bwd.restype = i
-        L.wkv7_bwd_state.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 5 + [vp] + [vp] * 3 + [vp]
-        L.wkv7_bwd_state.restype = i
+        L.wkv7_bwd_scan.argtypes = [i, i, i, i, i] + [vp] * 3 + [vp] * 3 + [vp]
+        L.wkv7_bwd_scan.restype = i
         L.wkv7_bwd_inputs.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] * 3 + [vp] * 5 + [vp]
         L.wkv7_bwd_inputs.restype = i
         _lib = L
@@ -115,8 +115,8 @@ def fwd_workspace_bytes(B: int, T: int, H: int, D: int = HEAD_SIZE) -> int:
     return int(lib().wkv7_fwd_workspace_bytes(B, T, H, D))
 
 
-def chunk_inv_bytes(B: int, T: int, H: int, D: int = HEAD_SIZE) -> int:
-    return int(lib().wkv7_chunk_inv_bytes(B, T, H, D))
+def chunk_ops_bytes(B: int, T: int, H: int, D: int = HEAD_SIZE) -> int:
+    return int(lib().wkv7_chunk_ops_bytes(B, T, H, D))
 
 
 def _f32_bytes(nbytes, device):
@@ -153,26 +153,32 @@ def fwd(r, w, k, v, a, b, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
     return y, ckpt, hT
 
 
-def chunk_inverse(w, a, b, out=None):
-    """(I - L)^-1 of every chunk, (B, H, NC, 32, 32) fp32 (see include/wkv7.h)."""
-    import torch
-    B, T, H, D = _shape(w)
+def chunk_prepare(r, w, k, a, b, out=None):
+    """Per-chunk operands of r, w, k, a, b (see include/wkv7.h), as a flat
+    fp32 tensor of chunk_ops_bytes(...) bytes; the forward and the backward of
+    one step may share it."""
+    B, T, H, D = _shape(r)
     if out is None:
-        out = torch.empty((B, H, num_chunks(T), CHUNK, CHUNK), device=w.device, dtype=torch.float32)
-    st = lib().wkv7_chunk_inverse(B, T, H, D, _dtype_code(w), _ptr(w), _ptr(a), _ptr(b), _ptr(out),
-                                  _stream(w.device))
-    _check("wkv7_chunk_inverse", st)
+        out = _f32_bytes(chunk_ops_bytes(B, T, H, D), r.device)
+    st = lib().wkv7_chunk_prepare(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, a, b)), _ptr(out),
+                                  _stream(r.device))
+    _check("wkv7_chunk_prepare", st)
     return out
 
 
-def fwd_chunks(r, w, k, v, a, b, chunk_inv, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
-               y=None, ckpt=None, hT=None):
-    """Forward given the chunk inverses of the same w, a, b."""
-    B, T, H, D = _shape(r)
-    y, ckpt, hT = _fwd_outputs(r, want_y, want_ckpt, want_hT, y, ckpt, hT)
-    st = lib().wkv7_fwd_chunks(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, v, a, b)), _ptr(chunk_inv),
-                               _ptr(h0), _ptr(y), _ptr(ckpt), _ptr(hT), _stream(r.device))
-    _check("wkv7_fwd_chunks", st)
+def chunk_inverse(chunk_ops, B, T, H):
+    """View of the (I - L)^-1 part of chunk operands: (B, H, NC, 32, 32) fp32."""
+    n = B * H * num_chunks(T) * CHUNK * CHUNK
+    return chunk_ops[:n].view(B, H, num_chunks(T), CHUNK, CHUNK)
+
+
+def fwd_scan(v, chunk_ops, h0=None, *, want_y=True, want_ckpt=True, want_hT=True, y=None, ckpt=None, hT=None):
+    """Forward given the chunk operands of the same r, w, k, a, b."""
+    B, T, H, D = _shape(v)
+    y, ckpt, hT = _fwd_outputs(v, want_y, want_ckpt, want_hT, y, ckpt, hT)
+    st = lib().wkv7_fwd_scan(B, T, H, D, _dtype_code(v), _ptr(v), _ptr(chunk_ops), _ptr(h0), _ptr(y),
+                             _ptr(ckpt), _ptr(hT), _stream(v.device))
+    _check("wkv7_fwd_scan", st)
     return y, ckpt, hT
 
 
@@ -212,31 +218,32 @@ def bwd(dy, r, w, k, v, a, b, ckpt, dhT=None, *, want_dh0=True, workspace=None, 
     return (*out, dh0)
 
 
-def bwd_state(dy, r, w, k, a, b, chunk_inv, dhT=None, *, want_dv=True, want_dh0=True, dh_ckpt=None):
+def bwd_scan(dy, chunk_ops, dhT=None, *, in_dtype=None, want_dv=True, want_dh0=True, dh_ckpt=None):
     """First backward stage: returns (dh_ckpt, dv, dh0); dh_ckpt[:, :, c] is the
-    gradient w.r.t. checkpoint c."""
+    gradient w.r.t. checkpoint c.  in_dtype: the dtype of the forward's inputs
+    (it fixes the operand format), a torch dtype."""
     import torch
-    B, T, H, D = _shape(r)
-    f32 = dict(device=r.device, dtype=torch.float32)
+    B, T, H, D = _shape(dy)
+    f32 = dict(device=dy.device, dtype=torch.float32)
     if dh_ckpt is None:
         dh_ckpt = torch.empty((B, H, num_chunks(T), D, D), **f32)
     dv = torch.empty((B, T, H, D), **f32) if want_dv else None
     dh0 = torch.empty((B, H, D, D), **f32) if want_dh0 else None
-    st = lib().wkv7_bwd_state(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
-                              *map(_ptr, (r, w, k, a, b)), _ptr(chunk_inv), _ptr(dh_ckpt), _ptr(dv), _ptr(dh0),
-                              _stream(r.device))
-    _check("wkv7_bwd_state", st)
+    code = BF16 if in_dtype == torch.bfloat16 else F32
+    st = lib().wkv7_bwd_scan(B, T, H, D, code, _ptr(dy), _ptr(dhT), _ptr(chunk_ops), _ptr(dh_ckpt), _ptr(dv),
+                             _ptr(dh0), _stream(dy.device))
+    _check("wkv7_bwd_scan", st)
     return dh_ckpt, dv, dh0
 
 
-def bwd_inputs(dy, r, w, k, v, a, b, chunk_inv, ckpt, dh_ckpt, dhT=None, *, out=None):
+def bwd_inputs(dy, r, w, k, v, a, b, chunk_ops, ckpt, dh_ckpt, dhT=None, *, out=None):
     """Second backward stage: returns (dr, dw, dk, da, db)."""
     import torch
     B, T, H, D = _shape(r)
     if out is None:
         out = [torch.empty((B, T, H, D), device=r.device, dtype=torch.float32) for _ in range(5)]
     st = lib().wkv7_bwd_inputs(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
-                               *map(_ptr, (r, w, k, v, a, b)), _ptr(chunk_inv), _ptr(ckpt), _ptr(dh_ckpt),
+                               *map(_ptr, (r, w, k, v, a, b)), _ptr(chunk_ops), _ptr(ckpt), _ptr(dh_ckpt),
                                *map(_ptr, out), _stream(r.device))
     _check("wkv7_bwd_inputs", st)
     return tuple(out)
@@ -253,30 +260,30 @@ def _make_autograd():
             ins = [x.contiguous() for x in (r, w, k, v, a, b)]
             h0c = None if h0 is None else h0.contiguous().float()
             T = ins[0].shape[1]
-            if T > 1:   # chunked path: one chunk inverse serves forward and backward
-                inv = chunk_inverse(ins[1], ins[4], ins[5])
-                y, ckpt, hT = fwd_chunks(*ins, inv, h0c)
+            if T > 1:   # chunked path: one set of chunk operands serves forward and backward
+                ops = chunk_prepare(ins[0], ins[1], ins[2], ins[4], ins[5])
+                y, ckpt, hT = fwd_scan(ins[3], ops, h0c)
             else:
-                inv = None
+                ops = None
                 y, ckpt, hT = fwd(*ins, h0c)
-            ctx.save_for_backward(*ins, ckpt, inv)
+            ctx.save_for_backward(*ins, ckpt, ops)
             ctx.has_h0 = h0 is not None
             return y, hT
 
         @staticmethod
         def backward(ctx, dy, dhT):
-            *ins, ckpt, inv = ctx.saved_tensors
+            *ins, ckpt, ops = ctx.saved_tensors
             if dy is None:
                 dy = torch.zeros(ins[0].shape, dtype=torch.float32, device=ins[0].device)
             else:
                 dy = dy.contiguous().float()
             dhT = None if dhT is None else dhT.contiguous().float()
-            if inv is None:
+            if ops is None:
                 dr, dw, dk, dv, da, db, dh0 = bwd(dy, *ins, ckpt, dhT)
             else:
                 r, w, k, v, a, b = ins
-                dh_ck, dv, dh0 = bwd_state(dy, r, w, k, a, b, inv, dhT)
-                dr, dw, dk, da, db = bwd_inputs(dy, r, w, k, v, a, b, inv, ckpt, dh_ck, dhT)
+                dh_ck, dv, dh0 = bwd_scan(dy, ops, dhT, in_dtype=r.dtype)
+                dr, dw, dk, da, db = bwd_inputs(dy, r, w, k, v, a, b, ops, ckpt, dh_ck, dhT)
             cast = lambda g, x: g.to(x.dtype)
             grads = [cast(g, x) for g, x in zip((dr, dw, dk, dv, da, db), ins)]
             return (*grads, dh0 if ctx.has_h0 else None)

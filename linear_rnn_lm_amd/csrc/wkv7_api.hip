@@ -131,14 +131,30 @@ wkv7::BwdArgs bwd_args(int B, int T, int H, const Sizes& sz, const float* dy, co
 
 wkv7_status status_of(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP; }
 
+// chunk_ops: the (I - Lab)^-1 of every chunk (fp32 32 x 32), then the
+// transition operands of every chunk (kOpsBytes each).
 int64_t inv_bytes(const Sizes& sz) { return sz.heads * sz.nc * kChunk * kChunk * 4; }
+int64_t ops_bytes(const Sizes& sz) { return inv_bytes(sz) + sz.heads * sz.nc * wkv7::kOpsBytes; }
 
-wkv7_status launch_inverse(int B, int T, int H, const Sizes& sz, bool bf16, const void* w, const void* a,
-                           const void* b, float* inv, hipStream_t s) {
-    wkv7::InvArgs ia;
-    ia.w = w; ia.a = a; ia.b = b; ia.inv = inv;
-    ia.B = B; ia.T = T; ia.H = H; ia.NC = (int)sz.nc;
-    return status_of(wkv7::launch_chunk_inv(ia, bf16, s));
+wkv7_status launch_prepare(int B, int T, int H, const Sizes& sz, bool bf16, const void* r, const void* w,
+                           const void* k, const void* a, const void* b, void* chunk_ops, hipStream_t s) {
+    wkv7::PrepArgs pa;
+    pa.r = r; pa.w = w; pa.k = k; pa.a = a; pa.b = b;
+    pa.inv = static_cast<float*>(chunk_ops);
+    pa.ops = static_cast<char*>(chunk_ops) + inv_bytes(sz);
+    pa.B = B; pa.T = T; pa.H = H; pa.NC = (int)sz.nc;
+    return status_of(wkv7::launch_chunk_prepare(pa, bf16, s));
+}
+
+wkv7_status launch_scan(int B, int T, int H, const Sizes& sz, bool bf16, bool bwd, const void* x,
+                        const void* chunk_ops, const float* s0, float* out, float* ckpt, float* sT,
+                        hipStream_t s) {
+    wkv7::ScanArgs sa;
+    sa.x = x;
+    sa.ops = static_cast<const char*>(chunk_ops) + inv_bytes(sz);
+    sa.s0 = s0; sa.out = out; sa.ckpt = ckpt; sa.sT = sT;
+    sa.B = B; sa.T = T; sa.H = H; sa.NC = (int)sz.nc;
+    return status_of(wkv7::launch_scan(sa, bf16, bwd, s));
 }
 
 }  // namespace
@@ -165,55 +181,60 @@ const char* wkv7_status_str(int status) {
     }
 }
 
-size_t wkv7_chunk_inv_bytes(int B, int T, int H, int D) {
+size_t wkv7_chunk_ops_bytes(int B, int T, int H, int D) {
     Sizes sz;
     if (check_shape(B, T, H, D, &sz) != WKV7_OK) return 0;
-    return (size_t)inv_bytes(sz);
+    return (size_t)ops_bytes(sz);
 }
 
 size_t wkv7_fwd_workspace_bytes(int B, int T, int H, int D) {
     Sizes sz;
     if (check_shape(B, T, H, D, &sz) != WKV7_OK) return 0;
-    return T <= kSequentialMaxT ? 0 : (size_t)inv_bytes(sz);
+    return T <= kSequentialMaxT ? 0 : (size_t)ops_bytes(sz);
 }
 
 size_t wkv7_bwd_workspace_bytes(int B, int T, int H, int D) {
     Sizes sz;
     if (check_shape(B, T, H, D, &sz) != WKV7_OK) return 0;
-    return (size_t)(sz.ckpt_elems * 4 + inv_bytes(sz));
+    return (size_t)(sz.ckpt_elems * 4 + ops_bytes(sz));
 }
 
-wkv7_status wkv7_chunk_inverse(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* w, const void* a,
-                               const void* b, float* chunk_inv, void* stream) {
+wkv7_status wkv7_chunk_prepare(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
+                               const void* k, const void* a, const void* b, void* chunk_ops, void* stream) {
     wkv7_status st = check_dtype(in_dtype);
     if (st != WKV7_OK) return st;
     Sizes sz;
     st = check_shape(B, T, H, D, &sz);
     if (st != WKV7_OK) return st;
     const int64_t tin = sz.tok_elems * elem_size(in_dtype);
-    const Buf bufs[4] = {{w, tin, true, false}, {a, tin, true, false}, {b, tin, true, false},
-                         {chunk_inv, inv_bytes(sz), true, true}};
-    st = check_bufs(bufs, 4);
+    const Buf bufs[6] = {{r, tin, true, false}, {w, tin, true, false}, {k, tin, true, false},
+                         {a, tin, true, false}, {b, tin, true, false}, {chunk_ops, ops_bytes(sz), true, true}};
+    st = check_bufs(bufs, 6);
     if (st != WKV7_OK) return st;
-    st = check_alias(bufs, 4);
+    st = check_alias(bufs, 6);
     if (st != WKV7_OK) return st;
-    return launch_inverse(B, T, H, sz, in_dtype == WKV7_BF16, w, a, b, chunk_inv, static_cast<hipStream_t>(stream));
+    return launch_prepare(B, T, H, sz, in_dtype == WKV7_BF16, r, w, k, a, b, chunk_ops,
+                          static_cast<hipStream_t>(stream));
 }
 
-wkv7_status wkv7_fwd_chunks(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
-                            const void* k, const void* v, const void* a, const void* b, const float* chunk_inv,
-                            const float* h0, float* y, float* h_ckpt, float* hT, void* stream) {
+wkv7_status wkv7_fwd_scan(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* v, const void* chunk_ops,
+                          const float* h0, float* y, float* h_ckpt, float* hT, void* stream) {
+    wkv7_status st = check_dtype(in_dtype);
+    if (st != WKV7_OK) return st;
     Sizes sz;
-    wkv7_status st = check_fwd(B, T, H, D, in_dtype, r, w, k, v, a, b, h0, y, h_ckpt, hT, &sz);
+    st = check_shape(B, T, H, D, &sz);
     if (st != WKV7_OK) return st;
-    const Buf bufs[4] = {{chunk_inv, inv_bytes(sz), true, false}, {y, sz.tok_elems * 4, false, true},
-                         {h_ckpt, sz.ckpt_elems * 4, false, true}, {hT, sz.state_elems * 4, false, true}};
-    st = check_bufs(bufs, 4);
+    const int64_t tin = sz.tok_elems * elem_size(in_dtype), s32 = sz.state_elems * 4;
+    const Buf bufs[6] = {{v, tin, true, false},  {chunk_ops, ops_bytes(sz), true, false},
+                         {h0, s32, false, false}, {y, sz.tok_elems * 4, false, true},
+                         {h_ckpt, sz.ckpt_elems * 4, false, true}, {hT, s32, false, true}};
+    st = check_bufs(bufs, 6);
     if (st != WKV7_OK) return st;
-    st = check_alias(bufs, 4);
+    if (!y && !h_ckpt && !hT) return WKV7_ERR_ARG;
+    st = check_alias(bufs, 6, h0, hT);
     if (st != WKV7_OK) return st;
-    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, chunk_inv, h0, y, h_ckpt, hT);
-    return status_of(wkv7::launch_fwd_chunked(fa, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
+    return launch_scan(B, T, H, sz, in_dtype == WKV7_BF16, false, v, chunk_ops, h0, y, h_ckpt, hT,
+                       static_cast<hipStream_t>(stream));
 }
 
 wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
@@ -230,20 +251,18 @@ wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const void
         return status_of(wkv7::launch_fwd_sequential(fa, bf16, s));
     }
     if (workspace && !aligned16(workspace)) return WKV7_ERR_ALIGN;
-    if (!workspace || workspace_bytes < (size_t)inv_bytes(sz)) return WKV7_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < (size_t)ops_bytes(sz)) return WKV7_ERR_WORKSPACE;
     const int64_t tin = sz.tok_elems * elem_size(in_dtype);
     const Buf bufs[11] = {{r, tin, true, false},   {w, tin, true, false},  {k, tin, true, false},
                           {v, tin, true, false},   {a, tin, true, false},  {b, tin, true, false},
                           {h0, sz.state_elems * 4, false, false},
                           {y, sz.tok_elems * 4, false, true}, {h_ckpt, sz.ckpt_elems * 4, false, true},
-                          {hT, sz.state_elems * 4, false, true}, {workspace, inv_bytes(sz), true, true}};
+                          {hT, sz.state_elems * 4, false, true}, {workspace, ops_bytes(sz), true, true}};
     st = check_alias(bufs, 11, h0, hT);
     if (st != WKV7_OK) return st;
-    float* inv = static_cast<float*>(workspace);
-    st = launch_inverse(B, T, H, sz, bf16, w, a, b, inv, s);
+    st = launch_prepare(B, T, H, sz, bf16, r, w, k, a, b, workspace, s);
     if (st != WKV7_OK) return st;
-    const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, inv, h0, y, h_ckpt, hT);
-    return status_of(wkv7::launch_fwd_chunked(fa, bf16, s));
+    return launch_scan(B, T, H, sz, bf16, false, v, workspace, h0, y, h_ckpt, hT, s);
 }
 
 wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r,
@@ -257,34 +276,27 @@ wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype,
     return status_of(wkv7::launch_fwd_sequential(fa, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
 }
 
-wkv7_status wkv7_bwd_state(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy,
-                           const float* dhT, const void* r, const void* w, const void* k, const void* a,
-                           const void* b, const float* chunk_inv, float* dh_ckpt, float* dv, float* dh0,
-                           void* stream) {
+wkv7_status wkv7_bwd_scan(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy, const float* dhT,
+                          const void* chunk_ops, float* dh_ckpt, float* dv, float* dh0, void* stream) {
     wkv7_status st = check_dtype(in_dtype);
     if (st != WKV7_OK) return st;
     Sizes sz;
     st = check_shape(B, T, H, D, &sz);
     if (st != WKV7_OK) return st;
-    const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
-    const Buf bufs[11] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
-                          {w, tin, true, false},  {k, tin, true, false},    {a, tin, true, false},
-                          {b, tin, true, false},  {chunk_inv, inv_bytes(sz), true, false},
-                          {dh_ckpt, sz.ckpt_elems * 4, true, true}, {dv, t32, false, true},
-                          {dh0, s32, false, true}};
-    st = check_bufs(bufs, 11);
+    const int64_t t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
+    const Buf bufs[6] = {{dy, t32, true, false},  {dhT, s32, false, false}, {chunk_ops, ops_bytes(sz), true, false},
+                         {dh_ckpt, sz.ckpt_elems * 4, true, true}, {dv, t32, false, true}, {dh0, s32, false, true}};
+    st = check_bufs(bufs, 6);
     if (st != WKV7_OK) return st;
-    st = check_alias(bufs, 11);
+    st = check_alias(bufs, 6);
     if (st != WKV7_OK) return st;
-    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, nullptr, a, b, chunk_inv, nullptr, dh_ckpt);
-    ba.dv = dv;
-    ba.dh0 = dh0;
-    return status_of(wkv7::launch_bwd_state(ba, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
+    return launch_scan(B, T, H, sz, in_dtype == WKV7_BF16, true, dy, chunk_ops, dhT, dv, dh_ckpt, dh0,
+                       static_cast<hipStream_t>(stream));
 }
 
 wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy,
                             const float* dhT, const void* r, const void* w, const void* k, const void* v,
-                            const void* a, const void* b, const float* chunk_inv, const float* h_ckpt,
+                            const void* a, const void* b, const void* chunk_ops, const float* h_ckpt,
                             const float* dh_ckpt, float* dr, float* dw, float* dk, float* da, float* db,
                             void* stream) {
     wkv7_status st = check_dtype(in_dtype);
@@ -296,7 +308,7 @@ wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype, con
     const int64_t c32 = sz.ckpt_elems * 4;
     const Buf bufs[16] = {{dy, t32, true, false},  {dhT, s32, false, false}, {r, tin, true, false},
                           {w, tin, true, false},   {k, tin, true, false},    {v, tin, true, false},
-                          {a, tin, true, false},   {b, tin, true, false},    {chunk_inv, inv_bytes(sz), true, false},
+                          {a, tin, true, false},   {b, tin, true, false},    {chunk_ops, ops_bytes(sz), true, false},
                           {h_ckpt, c32, true, false}, {dh_ckpt, c32, true, false}, {dr, t32, true, true},
                           {dw, t32, true, true},   {dk, t32, true, true},    {da, t32, true, true},
                           {db, t32, true, true}};
@@ -304,8 +316,8 @@ wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype, con
     if (st != WKV7_OK) return st;
     st = check_alias(bufs, 16);
     if (st != WKV7_OK) return st;
-    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, chunk_inv, h_ckpt,
-                                const_cast<float*>(dh_ckpt));
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, static_cast<const float*>(chunk_ops),
+                                h_ckpt, const_cast<float*>(dh_ckpt));
     ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.da = da; ba.db = db;
     return status_of(wkv7::launch_bwd_inputs(ba, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
 }
@@ -322,7 +334,7 @@ wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const floa
     if (st != WKV7_OK) return st;
     const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
     const int64_t c32 = sz.ckpt_elems * 4;
-    const int64_t need = c32 + inv_bytes(sz);
+    const int64_t need = c32 + ops_bytes(sz);
     const Buf bufs[17] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
                           {w, tin, true, false},  {k, tin, true, false},    {v, tin, true, false},
                           {a, tin, true, false},  {b, tin, true, false},    {h_ckpt, c32, true, false},
@@ -335,16 +347,17 @@ wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const floa
     st = check_alias(bufs, 17);
     if (st != WKV7_OK) return st;
     float* gbuf = static_cast<float*>(workspace);
-    float* inv = gbuf + sz.ckpt_elems;
+    void* ops = gbuf + sz.ckpt_elems;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = in_dtype == WKV7_BF16;
-    st = launch_inverse(B, T, H, sz, bf16, w, a, b, inv, s);
+    st = launch_prepare(B, T, H, sz, bf16, r, w, k, a, b, ops, s);
     if (st != WKV7_OK) return st;
-    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, inv, h_ckpt, gbuf);
-    ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.dv = dv; ba.da = da; ba.db = db; ba.dh0 = dh0;
-    hipError_t e = wkv7::launch_bwd_state(ba, bf16, s);
-    if (e == hipSuccess) e = wkv7::launch_bwd_inputs(ba, bf16, s);
-    return status_of(e);
+    st = launch_scan(B, T, H, sz, bf16, true, dy, ops, dhT, dv, gbuf, dh0, s);
+    if (st != WKV7_OK) return st;
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, static_cast<const float*>(ops), h_ckpt,
+                                gbuf);
+    ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.da = da; ba.db = db;
+    return status_of(wkv7::launch_bwd_inputs(ba, bf16, s));
 }
 
 }  // extern "C"

@@ -1,25 +1,19 @@
-// wkv7_bwd.hip -- chunked WKV7 backward on the matrix cores (gfx950).
+// wkv7_bwd.hip -- per-token input gradients of the WKV7 backward (gfx950).
 //
 // Reverse-mode of the per-token update (rwkv-mlx page, "Metal kernel
 // architecture", backward block: chunks in reverse, from checkpoints).  With
 // X_t = dL/dS_t (all later uses of S_t, including y_t) the gradient state
-// obeys X_{t-1} = X_t (diag w_t + b_t a_t^T) + dy_{t-1} r_{t-1}^T, the same
-// diagonal-plus-rank-1 recurrence as the forward but in reverse time.  It
-// does not involve the forward state, so it is a pass of its own:
-//
-// Kernel 1 (state gradient, one workgroup per head row block, chunks in
-// reverse).  With G = dL/dS at the chunk's end, G' = G diag(gamma_last) and
-// the chunk matrices of wkv7_device.h:
-//     DSA     = (I - Lab)^-T (Btil G'^T + Mrb^T DY)       dsa_t = X_t b_t
-//     dv      = Ktil G'^T + Lak^T DSA + Mrk^T DY            dv_t  = X_t k_t
-//     G_start = G' + DY^T Rhat + DSA^T Ahat
-// G_start (the gradient w.r.t. the state entering the chunk) goes to
-// dh_ckpt; after chunk 0 it is dh0.  Rows of G are independent.
-//
-// Kernel 2 (one workgroup per (head, chunk), all chunks at once).  From the
-// checkpoint S0 and the end gradient Ge (Ge' = Ge diag(gamma_last)) it
-// recomputes U (= sa_t) as in the forward -- never by dividing the state by
-// w -- and DSA as in kernel 1, then
+// obeys X_{t-1} = X_t (diag w_t + b_t a_t^T) + dy_{t-1} r_{t-1}^T.  The scan
+// kernel (wkv7_scan.hip) walks that recurrence over the chunks and leaves the
+// gradient w.r.t. the state entering every chunk in dh_ckpt.  This kernel
+// takes it from there, one workgroup per (head, chunk), all chunks at once.
+// With the chunk matrices of wkv7_device.h, G' = Ge diag(gamma_last) for the
+// gradient Ge at the chunk's end and T = (I - Lab)^-1 (from the prepare
+// kernel), it recomputes from the checkpoint S0 -- never by dividing the
+// state by w --
+//     U   = T (Ahat S0^T + Lak V)                       u_t   = S_{t-1} a_t
+//     DSA = T^T (Btil G'^T + Mrb^T DY)                  dsa_t = X_t b_t
+// and then
 //     dr = Gamma    * (DY S0  + tril(DY U^T) Btil   + tril(DY V^T) Ktil)
 //     da = Gamma_-1 * (DSA S0 + stril(DSA U^T) Btil + stril(DSA V^T) Ktil)
 //     dk = Gamma^-1 * (V Ge'  + striu(V DSA^T) Ahat + triu(V DY^T) Rhat)
@@ -35,225 +29,6 @@
 namespace wkv7 {
 namespace {
 
-// ------------------------------------------------------------- kernel 1
-template <bool SPLIT, int RB>
-struct StateSmem {
-    using F = Fmt<SPLIT>;
-    static constexpr int A = 0;                          // Ahat rows (t, j)
-    static constexpr int R = A + F::bytes(C, D);         // Rhat rows
-    static constexpr int Bm = R + F::bytes(C, D);        // Btil rows
-    static constexpr int Km = Bm + F::bytes(C, D);       // Ktil rows
-    static constexpr int AT = Km + F::bytes(C, D);       // Ahat^T (j, t)
-    static constexpr int RT = AT + F::bytes(D, C);       // Rhat^T (j, t)
-    static constexpr int G = RT + F::bytes(D, C);        // G' rows (i, j)
-    static constexpr int DYT = G + F::bytes(RB, D);      // dy^T (i, t)
-    static constexpr int LakT = DYT + F::bytes(RB, C);   // (t, s) = Lak[s][t]
-    static constexpr int MrbT = LakT + F::bytes(C, C);
-    static constexpr int MrkT = MrbT + F::bytes(C, C);
-    static constexpr int TinvT = MrkT + F::bytes(C, C);
-    static constexpr int Rhs2T = TinvT + F::bytes(C, C);  // (i, t)
-    static constexpr int DsaT = Rhs2T + F::bytes(RB, C);  // (i, t)
-    static constexpr int glast = DsaT + F::bytes(RB, C);
-    static constexpr int qp = glast + D * 4;
-    static constexpr int total = qp + 8 * D * 4;
-};
-
-template <typename InT, bool SPLIT, int RB, int NT>
-__global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs p, int xcd) {
-    static_assert(NT == 256, "one raw-chunk thread shape");
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    using L = StateSmem<SPLIT, RB>;
-    using M = Mat<SPLIT>;
-    constexpr int NW = NT / 64;
-    constexpr int NRB = D / RB;
-    constexpr int NTILE = 2 * (RB / 16);
-    constexpr int NGT = (RB / 16) * 4;
-    constexpr int NPER = (NGT + NW - 1) / NW;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r16 = lane & 15, g4 = lane >> 4;
-
-    int head, rb;
-    block_map(blockIdx.x, NRB, xcd != 0, head, rb);
-    const int bb = head / p.H, hh = head % p.H;
-    const int row0 = rb * RB;
-    const int64_t tstride = (int64_t)p.H * D;
-    const int64_t soff = (int64_t)head * D * D + (int64_t)row0 * D;
-
-    const InT* gr = static_cast<const InT*>(p.r);
-    const InT* gw = static_cast<const InT*>(p.w);
-    const InT* gk = static_cast<const InT*>(p.k);
-    const InT* ga = static_cast<const InT*>(p.a);
-    const InT* gb = static_cast<const InT*>(p.b);
-
-    const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
-    const M Bm = make_mat<SPLIT>(smem, L::Bm, C, D), Km = make_mat<SPLIT>(smem, L::Km, C, D);
-    const M AT = make_mat<SPLIT>(smem, L::AT, D, C), RT = make_mat<SPLIT>(smem, L::RT, D, C);
-    const M G = make_mat<SPLIT>(smem, L::G, RB, D), DYT = make_mat<SPLIT>(smem, L::DYT, RB, C);
-    const M LakT = make_mat<SPLIT>(smem, L::LakT, C, C), MrbT = make_mat<SPLIT>(smem, L::MrbT, C, C);
-    const M MrkT = make_mat<SPLIT>(smem, L::MrkT, C, C), TinvT = make_mat<SPLIT>(smem, L::TinvT, C, C);
-    const M Rhs2T = make_mat<SPLIT>(smem, L::Rhs2T, RB, C), DsaT = make_mat<SPLIT>(smem, L::DsaT, RB, C);
-    float* glast = reinterpret_cast<float*>(smem + L::glast);
-    float* qp = reinterpret_cast<float*>(smem + L::qp);
-
-    const PrepOut<SPLIT> po{A, R, Bm, Km, AT, RT, A, A, true, true, true, true, true, true, false, false,
-                            nullptr, glast};
-    const CcOut<SPLIT, NT> co{nullptr, LakT, LakT, MrbT, MrbT, MrkT, MrkT, false, true, false, true, false, true};
-
-    // wave-owned gradient tiles, from dhT
-    f32x4 gt[NPER];
-#pragma unroll
-    for (int q2 = 0; q2 < NPER; ++q2) {
-        const int job = wave + q2 * NW;
-        if (job < NGT) {
-            const int tm = job >> 2, tn = job & 3;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                gt[q2][q] = p.dhT ? p.dhT[soff + (tm * 16 + 4 * g4 + q) * D + tn * 16 + r16] : 0.f;
-        }
-    }
-
-    RawChunk<NT, InT> raw;
-    RawCols<NT, RB, float> rdy;
-    f32x4 tv;   // four entries of the chunk's (I - Lab)^-1: row tid/8, columns 4*(tid%8)..
-    const float* ginv = p.inv + (int64_t)head * p.NC * C * C + tid * 4;
-    {
-        const int c = p.NC - 1;
-        const int Cc = min(C, p.T - c * C);
-        const int64_t base = ((int64_t)bb * p.T + c * C) * tstride + (int64_t)hh * D;
-        raw.load(gw, ga, gr, gb, gk, base, tstride, Cc, tid);
-        rdy.load(p.dy, base, tstride, Cc, row0, tid);
-        tv = *reinterpret_cast<const f32x4*>(ginv + (int64_t)c * C * C);
-    }
-
-    constexpr int NVPER = (NTILE + NW - 1) / NW;
-    f32x4 dvv[NVPER];
-    // Stores of one finished chunk cc: dv (tokens < vcc) and the state gradient
-    // entering it (registers gt) into dh_ckpt.
-    auto store_prev = [&](int64_t vbase_, int vcc_, int cc_) {
-        if (p.dv) {
-#pragma unroll
-            for (int q2 = 0; q2 < NVPER; ++q2) {
-                const int job = wave + q2 * NW;
-                if (job < NTILE) {
-                    const int ti = job & 1, tn = job >> 1;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int t = ti * 16 + 4 * g4 + q;
-                        if (t < vcc_) p.dv[vbase_ + t * tstride + row0 + tn * 16 + r16] = dvv[q2][q];
-                    }
-                }
-            }
-        }
-        float* gout = p.gbuf + ((int64_t)head * p.NC + cc_) * D * D + (int64_t)row0 * D;
-#pragma unroll
-        for (int q2 = 0; q2 < NPER; ++q2) {
-            const int job = wave + q2 * NW;
-            if (job < NGT) {
-                const int tm = job >> 2, tn = job & 3;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) gout[(tm * 16 + 4 * g4 + q) * D + tn * 16 + r16] = gt[q2][q];
-            }
-        }
-    };
-
-    // dv and the state gradient of a chunk are stored at the start of the next
-    // iteration (no store between a prefetch and the wait for it)
-    int64_t vbase = 0;
-    int vCc = 0, cprev = 0;
-
-    for (int c = p.NC - 1; c >= 0; --c) {
-        const int t0 = c * C;
-        const int Cc = min(C, p.T - t0);
-        const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
-
-        chunk_prep<NT, SPLIT>(raw, po, qp, tid);
-        rdy.template store_T<SPLIT, false>(DYT, tid);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) put(TinvT, (tid & 7) * 4 + q, tid >> 3, tv[q]);
-        if (c < p.NC - 1) store_prev(vbase, vCc, cprev);
-        {
-            const int cp = max(c - 1, 0);
-            const int64_t pbase = ((int64_t)bb * p.T + cp * C) * tstride + (int64_t)hh * D;
-            const int pCc = min(C, p.T - cp * C);
-            raw.load(gw, ga, gr, gb, gk, pbase, tstride, pCc, tid);
-            rdy.load(p.dy, pbase, tstride, pCc, row0, tid);
-            tv = *reinterpret_cast<const f32x4*>(ginv + (int64_t)cp * C * C);
-        }
-        lds_barrier();
-
-        chunk_cc<SPLIT, NT>(A, R, Bm, Km, co, tid);
-        f32x4 gs[NPER];   // G' = G diag(gamma_last)
-#pragma unroll
-        for (int q2 = 0; q2 < NPER; ++q2) {
-            const int job = wave + q2 * NW;
-            if (job < NGT) {
-                const int tm = job >> 2, tn = job & 3;
-                const float gl = glast[tn * 16 + r16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) gs[q2][q] = gt[q2][q] * gl;
-                store_rows<MASK_NONE>(G, gs[q2], tm * 16, tn * 16, lane);
-            }
-        }
-        lds_barrier();
-
-        for (int job = wave; job < NTILE; job += NW) {
-            const int ti = job & 1, tn = job >> 1;
-            f32x4 acc = mma<SPLIT, D>(zero4(), Bm, ti * 16, G, tn * 16, lane);
-            acc = mma<SPLIT, C>(acc, MrbT, ti * 16, DYT, tn * 16, lane);
-            store_cols<MASK_NONE>(Rhs2T, acc, ti * 16, tn * 16, lane);
-        }
-        lds_barrier();
-
-        for (int job = wave; job < NTILE; job += NW) {
-            const int ti = job & 1, tn = job >> 1;
-            const f32x4 acc = mma<SPLIT, C>(zero4(), TinvT, ti * 16, Rhs2T, tn * 16, lane);
-            store_cols<MASK_NONE>(DsaT, acc, ti * 16, tn * 16, lane);
-        }
-        lds_barrier();
-
-        // dv = Ktil G'^T + Lak^T DSA + Mrk^T DY
-#pragma unroll
-        for (int q2 = 0; q2 < NVPER; ++q2) {
-            const int job = wave + q2 * NW;
-            if (job < NTILE) {
-                const int ti = job & 1, tn = job >> 1;
-                f32x4 acc = mma<SPLIT, D>(zero4(), Km, ti * 16, G, tn * 16, lane);
-                acc = mma<SPLIT, C>(acc, LakT, ti * 16, DsaT, tn * 16, lane);
-                dvv[q2] = mma<SPLIT, C>(acc, MrkT, ti * 16, DYT, tn * 16, lane);
-            }
-        }
-        vbase = base;
-        vCc = Cc;
-        cprev = c;
-
-        // G <- G' + DY^T Rhat + DSA^T Ahat
-#pragma unroll
-        for (int q2 = 0; q2 < NPER; ++q2) {
-            const int job = wave + q2 * NW;
-            if (job < NGT) {
-                const int tm = job >> 2, tn = job & 3;
-                f32x4 acc = mma<SPLIT, C>(gs[q2], DYT, tm * 16, RT, tn * 16, lane);
-                acc = mma<SPLIT, C>(acc, DsaT, tm * 16, AT, tn * 16, lane);
-                gt[q2] = acc;
-            }
-        }
-        lds_barrier();
-    }
-    store_prev(vbase, vCc, cprev);
-    if (p.dh0) {
-#pragma unroll
-        for (int q2 = 0; q2 < NPER; ++q2) {
-            const int job = wave + q2 * NW;
-            if (job < NGT) {
-                const int tm = job >> 2, tn = job & 3;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) p.dh0[soff + (tm * 16 + 4 * g4 + q) * D + tn * 16 + r16] = gt[q2][q];
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------- kernel 2
 // LDS plan (byte offsets).  Region X holds what phases 0-3 need; region Y
 // (phases 3-5) reuses region X's space once its contents are dead; region P
 // lives throughout.  See the phase comments in the kernel.
@@ -602,29 +377,6 @@ hipError_t set_smem(F kern, int bytes, bool& done) {
     return e;
 }
 
-template <typename InT, bool SPLIT, int RB>
-hipError_t launch_state(const BwdArgs& a, hipStream_t s) {
-    constexpr int NT = 256;
-    using L = StateSmem<SPLIT, RB>;
-    static_assert(L::total <= 160 * 1024, "state kernel LDS exceeds 160 KiB");
-    auto kern = bwd_state_kernel<InT, SPLIT, RB, NT>;
-    static bool done = false;
-    hipError_t e = set_smem(kern, L::total, done);
-    if (e != hipSuccess) return e;
-    const int heads = a.B * a.H;
-    const int xcd = (heads % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3(heads * (D / RB)), dim3(NT), L::total, s, a, xcd);
-    return hipGetLastError();
-}
-
-template <typename InT, bool SPLIT>
-hipError_t launch_state_typed(const BwdArgs& a, hipStream_t s) {
-    const int heads = a.B * a.H;
-    if (heads > 128) return launch_state<InT, SPLIT, 64>(a, s);
-    if (heads > 64) return launch_state<InT, SPLIT, 32>(a, s);
-    return launch_state<InT, SPLIT, 16>(a, s);
-}
-
 template <typename InT, bool SPLIT>
 hipError_t launch_inputs_typed(const BwdArgs& a, hipStream_t s) {
     constexpr int NT = 256;
@@ -641,11 +393,6 @@ hipError_t launch_inputs_typed(const BwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-hipError_t launch_bwd_state(const BwdArgs& a, bool bf16, hipStream_t s) {
-    if (bf16) return launch_state_typed<uint16_t, true>(a, s);
-    return launch_state_typed<float, false>(a, s);
-}
 
 hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, hipStream_t s) {
     if (bf16) return launch_inputs_typed<uint16_t, true>(a, s);

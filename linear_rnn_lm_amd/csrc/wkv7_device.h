@@ -607,4 +607,155 @@ __device__ __forceinline__ void tinv_store(const float* tf, Mat<SPLIT> T, bool r
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Fragments with a permuted k order (used by the chunk-operand kernels).
+//
+// A 32-wide block of the contraction index, [c0, c0 + 32), is dealt to the
+// lanes of a 16 x 16 MFMA tile so that lane (g = lane / 16, r = lane % 16)
+// holds the eight k values  c0 + 16h + 4g + q  (h = 0, 1; q = 0..3).  Both
+// operands of a product use the same order, so the sum over k is unchanged.
+// The point of this order: the accumulator of a 16 x 16 tile holds
+// acc[q] = X[m0 + 4g + q][n0 + r], which is exactly such a fragment of the
+// row n0 + r of X^T for k = m0 + 4g + q -- a result can be fed back as an
+// operand without leaving the registers.
+//   SPLIT = true : element e = 4h + q of bf16x8 hi / lo (value = hi + lo)
+//   SPLIT = false: v[h][q] (fp32), consumed by four 16x16x4 steps per h
+template <bool SPLIT>
+struct Frag;
+template <>
+struct Frag<true> {
+    bf16x8 hi, lo;
+};
+template <>
+struct Frag<false> {
+    f32x4 v[2];
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ bf16x4 as_bf16x4(i16x4 v) { return __builtin_bit_cast(bf16x4, v); }
+
+// Fragment of two accumulator tiles: h = 0 from a0, h = 1 from a1.
+template <bool SPLIT>
+__device__ __forceinline__ Frag<SPLIT> frag_acc(f32x4 a0, f32x4 a1) {
+    Frag<SPLIT> f;
+    if constexpr (SPLIT) {
+        bf16x2 h0, l0, h1, l1, h2, l2, h3, l3;
+        split2(f32x2{a0[0], a0[1]}, h0, l0);
+        split2(f32x2{a0[2], a0[3]}, h1, l1);
+        split2(f32x2{a1[0], a1[1]}, h2, l2);
+        split2(f32x2{a1[2], a1[3]}, h3, l3);
+        f.hi = bf16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+        f.lo = bf16x8{l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
+    } else {
+        f.v[0] = a0;
+        f.v[1] = a1;
+    }
+    return f;
+}
+
+// Fragment of values exact in bf16 (SPLIT: the lo part is never read).
+template <bool SPLIT>
+__device__ __forceinline__ Frag<SPLIT> frag_exact(f32x4 a0, f32x4 a1) {
+    if constexpr (SPLIT) {
+        Frag<SPLIT> f;
+        const bf16x4 x0 = __builtin_convertvector(a0, bf16x4), x1 = __builtin_convertvector(a1, bf16x4);
+        f.hi = cat8(x0, x1);
+        f.lo = f.hi;
+        return f;
+    } else {
+        return frag_acc<false>(a0, a1);
+    }
+}
+
+// Rows: lane (g, r) gets X[row0 + r][c0 + 16h + 4g + q].
+__device__ __forceinline__ Frag<true> frag_n(Mat<true> X, int row0, int c0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const __bf16* p = reinterpret_cast<const __bf16*>(X.p) + (row0 + r) * X.ld + c0 + 4 * g;
+    Frag<true> f;
+    f.hi = cat8(*reinterpret_cast<const bf16x4*>(p), *reinterpret_cast<const bf16x4*>(p + 16));
+    f.lo = cat8(*reinterpret_cast<const bf16x4*>(p + X.plane), *reinterpret_cast<const bf16x4*>(p + X.plane + 16));
+    return f;
+}
+__device__ __forceinline__ Frag<false> frag_n(Mat<false> X, int row0, int c0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const float* p = reinterpret_cast<const float*>(X.p) + (row0 + r) * X.ld + c0 + 4 * g;
+    Frag<false> f;
+    f.v[0] = *reinterpret_cast<const f32x4*>(p);
+    f.v[1] = *reinterpret_cast<const f32x4*>(p + 16);
+    return f;
+}
+
+// Columns: lane (g, r) gets X[c0 + 16h + 4g + q][col0 + r].  For the split
+// format this is the LDS transpose read (ds_read_b64_tr_b16): within each
+// group of 16 lanes, lane 4i + e receives element e of the 8-byte reads of
+// lanes i, i + 4, i + 8, i + 12; so lane s reads X[c0 + 4g + (s%16)/4]
+// [col0 + 4(s%4) .. +3].
+__device__ __forceinline__ Frag<true> frag_t(Mat<true> X, int col0, int c0, int lane) {
+    const int g = lane >> 4, l16 = lane & 15;
+    const __bf16* p = reinterpret_cast<const __bf16*>(X.p) + (c0 + 4 * g + (l16 >> 2)) * X.ld + col0 + 4 * (l16 & 3);
+    const __bf16* p1 = p + 16 * X.ld;
+    Frag<true> f;
+    f.hi = cat8(as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p))),
+                as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1))));
+    f.lo = cat8(as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + X.plane))),
+                as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1 + X.plane))));
+    return f;
+}
+__device__ __forceinline__ Frag<false> frag_t(Mat<false> X, int col0, int c0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const float* p = reinterpret_cast<const float*>(X.p) + (c0 + 4 * g) * X.ld + col0 + r;
+    Frag<false> f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) f.v[h][q] = p[(16 * h + q) * X.ld];
+    return f;
+}
+
+// acc += X Y^T over one 32-wide k block.  XEX / YEX: operand exact in bf16.
+template <bool XEX = false, bool YEX = false>
+__device__ __forceinline__ f32x4 fmma(f32x4 acc, const Frag<true>& x, const Frag<true>& y) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, y.hi, acc, 0, 0, 0);
+    if constexpr (!YEX) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, y.lo, acc, 0, 0, 0);
+    if constexpr (!XEX) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.lo, y.hi, acc, 0, 0, 0);
+    return acc;
+}
+template <bool XEX = false, bool YEX = false>
+__device__ __forceinline__ f32x4 fmma(f32x4 acc, const Frag<false>& x, const Frag<false>& y) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.v[h][q], y.v[h][q], acc, 0, 0, 0);
+    return acc;
+}
+
+// Elements (m, k..k+3) of an LDS operand as fp32 (hi + lo for the split format).
+__device__ __forceinline__ f32x4 get4(Mat<true> M, int m, int k) {
+    const __bf16* h = reinterpret_cast<const __bf16*>(M.p) + m * M.ld + k;
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(h), lo = *reinterpret_cast<const bf16x4*>(h + M.plane);
+    return __builtin_convertvector(hi, f32x4) + __builtin_convertvector(lo, f32x4);
+}
+__device__ __forceinline__ f32x4 get4(Mat<false> M, int m, int k) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(M.p) + m * M.ld + k);
+}
+
+// Four consecutive values into a global operand block: the split format keeps
+// a hi plane and, `plane` elements further, a lo plane.
+__device__ __forceinline__ void gput4(__bf16* X, int64_t plane, int64_t idx, f32x4 v) {
+    bf16x2 h0, l0, h1, l1;
+    split2(f32x2{v[0], v[1]}, h0, l0);
+    split2(f32x2{v[2], v[3]}, h1, l1);
+    *reinterpret_cast<bf16x4*>(X + idx) = bf16x4{h0[0], h0[1], h1[0], h1[1]};
+    *reinterpret_cast<bf16x4*>(X + plane + idx) = bf16x4{l0[0], l0[1], l1[0], l1[1]};
+}
+__device__ __forceinline__ void gput4(float* X, int64_t, int64_t idx, f32x4 v) {
+    *reinterpret_cast<f32x4*>(X + idx) = v;
+}
+
 }  // namespace wkv7

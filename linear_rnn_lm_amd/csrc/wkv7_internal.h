@@ -29,17 +29,31 @@ struct BwdArgs {
     int B, T, H, NC;
 };
 
-struct InvArgs {
-    const void *w, *a, *b;
-    float* inv;  // output (B,H,NC,32,32)
+// Bytes of one chunk's transition operands P, M, E, F (the same for both
+// storage formats: two bf16 planes or one fp32 plane).
+constexpr int kOpsBytes = 36864;
+
+struct PrepArgs {
+    const void *r, *w, *k, *a, *b;
+    float* inv;  // output (B,H,NC,32,32): (I - Lab)^-1 of every chunk
+    void* ops;   // output (B,H,NC) blocks of kOpsBytes
+    int B, T, H, NC;
+};
+
+struct ScanArgs {
+    const void* x;    // forward: v (input dtype); backward: dy (fp32)
+    const void* ops;  // (B,H,NC) blocks of kOpsBytes
+    const float* s0;  // forward: h0; backward: dhT (NULL = zero)
+    float* out;       // forward: y; backward: dv (NULL = skip)
+    float* ckpt;      // forward: state entering each chunk; backward: its gradient (NULL = skip)
+    float* sT;        // forward: hT; backward: dh0 (NULL = skip)
     int B, T, H, NC;
 };
 
 // Each returns hipSuccess or the launch error.
-hipError_t launch_chunk_inv(const InvArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_fwd_chunked(const FwdArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_chunk_prepare(const PrepArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_scan(const ScanArgs& a, bool bf16, bool bwd, hipStream_t s);
 hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_bwd_state(const BwdArgs& a, bool bf16, hipStream_t s);   // kernel 1
-hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, hipStream_t s);  // kernel 2
+hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace wkv7

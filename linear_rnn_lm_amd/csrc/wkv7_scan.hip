@@ -1,0 +1,475 @@
+// wkv7_scan.hip -- the WKV7 chunk recurrence as a scan over per-chunk
+// transition operands (gfx950).
+//
+// Unrolling the per-token update over one chunk (rwkv-mlx page, "Metal kernel
+// architecture", forward block; wkv7_device.h has the chunk matrices Ahat,
+// Rhat, Btil, Ktil, Lab, Lak, Mrb, Mrk) and eliminating U with
+// T = (I - Lab)^-1, W1 = T Ahat and Z = T Lak gives, for the state S0
+// entering the chunk and the chunk's v rows V,
+//     S_end = S0 P + V^T M,        Y = E S0^T + F V
+// with four operands that depend on the chunk's r, w, k, a, b only:
+//     P = (I + W1^T Btil) diag(gamma_last)        (D x D, rows j, columns j')
+//     M = (Z^T Btil + Ktil) diag(gamma_last)      (C x D)
+//     E = Rhat + Mrb W1                           (C x D)
+//     F = Mrb Z + Mrk                             (C x C, lower triangular)
+// The backward (same page, backward block) runs the transposed map: with G
+// the gradient at the chunk's end and DY the chunk's dy rows,
+//     G_start = G P^T + DY^T E,     dv = M G^T + F^T DY.
+//
+// Kernel "prepare": one workgroup per (head, chunk), all chunks at once: the
+// chunk matrices, T, and P, M, E, F, written to memory (T as fp32 for the
+// input-gradient kernel, P, M, E, F in the operand format: two bf16 planes
+// hi/lo for bf16 inputs, fp32 otherwise).
+// Kernel "scan": 16 state rows per wave, chunks in order (forward) or in
+// reverse (backward).  The state stays in the MFMA accumulators across
+// chunks: with the permuted k order of Frag (wkv7_device.h) a 16 x 16 result
+// tile is already an operand fragment of the next chunk's product, so the
+// only serial work per chunk is one D x D product per wave.  The operands of
+// the next chunk are fetched into registers one chunk ahead and staged in a
+// double-buffered LDS copy shared by the workgroup's waves.
+#include <type_traits>
+
+#include "wkv7_device.h"
+#include "wkv7_internal.h"
+
+namespace wkv7 {
+namespace {
+
+// Element offsets of P, M, E, F inside one chunk's operand block, in storage
+// elements (bf16 for the split format, which keeps the hi plane of a matrix
+// followed by its lo plane; fp32 otherwise).  Rows are unpadded.
+template <bool SPLIT>
+struct OpsLayout {
+    using E = typename std::conditional<SPLIT, __bf16, float>::type;
+    static constexpr int planes = SPLIT ? 2 : 1;
+    static constexpr int P = 0;                        // (j, j')  64 x 64
+    static constexpr int M = P + planes * D * D;       // (t, j)   32 x 64
+    static constexpr int E_ = M + planes * C * D;      // (t, j)   32 x 64
+    static constexpr int F = E_ + planes * C * D;      // (t, u)   32 x 32
+    static constexpr int total = F + planes * C * C;
+    static_assert(total * (int)sizeof(E) == kOpsBytes, "operand block size");
+};
+
+// ------------------------------------------------------------------ prepare
+template <bool SPLIT>
+struct PrepSmem {
+    using F = Fmt<SPLIT>;
+    static constexpr int A = 0;                        // Ahat rows (t, j)
+    static constexpr int R = A + F::bytes(C, D);       // Rhat rows
+    static constexpr int Bm = R + F::bytes(C, D);      // Btil rows
+    static constexpr int Km = Bm + F::bytes(C, D);     // Ktil rows
+    static constexpr int Tm = Km + F::bytes(C, D);     // T rows (t, s)
+    static constexpr int Lak = Tm + F::bytes(C, C);    // Lak rows (t, s)
+    static constexpr int Mrb = Lak + F::bytes(C, C);   // Mrb rows (t, s)
+    static constexpr int W1 = Mrb + F::bytes(C, C);    // W1 rows (t, j)
+    static constexpr int Zm = W1 + F::bytes(C, D);     // Z rows (t, u)
+    static constexpr int LabF = Zm + F::bytes(C, C);   // fp32 Lab, stride LDF
+    static constexpr int TF = LabF + C * LDF * 4;      // fp32 T, stride LDF
+    static constexpr int Scr = TF + C * LDF * 4;       // 16 x 20 fp32
+    static constexpr int glast = Scr + 16 * 20 * 4;    // fp32 [64]
+    static constexpr int qp = glast + D * 4;           // fp32 8 x 64
+    static constexpr int total = qp + 8 * D * 4;
+    static_assert(total <= 80 * 1024, "two workgroups per CU");
+};
+
+template <typename InT, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using L = PrepSmem<SPLIT>;
+    using M = Mat<SPLIT>;
+    using O = OpsLayout<SPLIT>;
+    using E = typename O::E;
+    constexpr int NT = 256;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int item = blockIdx.x;  // (head, chunk)
+    const int head = item / p.NC, c = item % p.NC;
+    const int bb = head / p.H, hh = head % p.H;
+    const int64_t tstride = (int64_t)p.H * D;
+    const int t0 = c * C, Cc = min(C, p.T - t0);
+    const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
+
+    RawChunk<NT, InT> raw;
+    raw.load(static_cast<const InT*>(p.w), static_cast<const InT*>(p.a), static_cast<const InT*>(p.r),
+             static_cast<const InT*>(p.b), static_cast<const InT*>(p.k), base, tstride, Cc, tid);
+
+    const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
+    const M Bm = make_mat<SPLIT>(smem, L::Bm, C, D), Km = make_mat<SPLIT>(smem, L::Km, C, D);
+    const M Tm = make_mat<SPLIT>(smem, L::Tm, C, C), Lak = make_mat<SPLIT>(smem, L::Lak, C, C);
+    const M Mrb = make_mat<SPLIT>(smem, L::Mrb, C, C), W1 = make_mat<SPLIT>(smem, L::W1, C, D);
+    const M Zm = make_mat<SPLIT>(smem, L::Zm, C, C);
+    float* glast = reinterpret_cast<float*>(smem + L::glast);
+    float* qp = reinterpret_cast<float*>(smem + L::qp);
+    float* labf = reinterpret_cast<float*>(smem + L::LabF);
+    float* tf = reinterpret_cast<float*>(smem + L::TF);
+    float* scr = reinterpret_cast<float*>(smem + L::Scr);
+
+    // ---- gamma, gamma_last and the scaled operand rows
+    const PrepOut<SPLIT> po{A, R, Bm, Km, A, A, A, A, true, true, true, true, false, false, false, false,
+                            nullptr, glast};
+    chunk_prep<NT, SPLIT>(raw, po, qp, tid);
+    lds_barrier();
+
+    // ---- C x C matrices and T (one wave each)
+    f32x4 mk0 = zero4(), mk1 = zero4(), mk2 = zero4();
+    if (wave == 3) {
+        const f32x4 t00 = mma<SPLIT, D>(zero4(), A, 0, Bm, 0, lane);
+        const f32x4 t10 = mma<SPLIT, D>(zero4(), A, 16, Bm, 0, lane);
+        const f32x4 t11 = mma<SPLIT, D>(zero4(), A, 16, Bm, 16, lane);
+        store_f32<MASK_STRICT>(labf, LDF, t00, 0, 0, lane);
+        store_f32<MASK_STRICT>(labf, LDF, t10, 16, 0, lane);
+        store_f32<MASK_STRICT>(labf, LDF, t11, 16, 16, lane);
+        for (int e = lane; e < 256; e += 64) labf[(e >> 4) * LDF + 16 + (e & 15)] = 0.f;
+        wave_lds_sync();
+        tri_inverse(labf, tf, scr, lane);
+        tinv_store<SPLIT>(tf, Tm, true, Tm, false, lane);
+        float* out = p.inv + (int64_t)item * C * C;
+        const int t = lane >> 1, s0 = (lane & 1) * 16;
+#pragma unroll
+        for (int s4 = 0; s4 < 16; s4 += 4)
+            *reinterpret_cast<f32x4*>(out + t * C + s0 + s4) = *reinterpret_cast<const f32x4*>(tf + t * LDF + s0 + s4);
+    } else if (wave == 0) {
+        const f32x4 t00 = mma<SPLIT, D>(zero4(), A, 0, Km, 0, lane);
+        const f32x4 t10 = mma<SPLIT, D>(zero4(), A, 16, Km, 0, lane);
+        const f32x4 t11 = mma<SPLIT, D>(zero4(), A, 16, Km, 16, lane);
+        cc_store<MASK_STRICT>(Lak, true, Lak, false, t00, t10, t11, lane);
+    } else if (wave == 1) {
+        const f32x4 t00 = mma<SPLIT, D>(zero4(), R, 0, Bm, 0, lane);
+        const f32x4 t10 = mma<SPLIT, D>(zero4(), R, 16, Bm, 0, lane);
+        const f32x4 t11 = mma<SPLIT, D>(zero4(), R, 16, Bm, 16, lane);
+        cc_store<MASK_LOWER>(Mrb, true, Mrb, false, t00, t10, t11, lane);
+    } else {
+        // Mrk as the start of F: element (u, t) = sum_j Ktil[u][j] Rhat[t][j], kept for u <= t.
+        // Tiles (u block, t block) = (0, 0), (0, 1), (1, 1); (1, 0) is zero.
+        mk0 = mma<SPLIT, D>(zero4(), Km, 0, R, 0, lane);
+        mk1 = mma<SPLIT, D>(zero4(), Km, 0, R, 16, lane);
+        mk2 = mma<SPLIT, D>(zero4(), Km, 16, R, 16, lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (4 * g4 + q > r16) {
+                mk0[q] = 0.f;
+                mk2[q] = 0.f;
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- W1 = T Ahat (rows t, columns j) and Z = T Lak (rows t, columns u)
+    for (int job = wave; job < 12; job += 4) {
+        if (job < 8) {
+            const int jb = job & 3, tb = job >> 2;
+            // element (j, t) = sum_s Ahat[s][j] T[t][s]
+            const f32x4 acc = fmma(zero4(), frag_t(A, 16 * jb, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
+            put4(W1, 16 * tb + r16, 16 * jb + 4 * g4, acc);
+        } else if (job < 11) {
+            const int ub = job == 10 ? 1 : 0, tb = job == 8 ? 0 : 1;
+            // element (u, t) = sum_s Lak[s][u] T[t][s]
+            const f32x4 acc = fmma(zero4(), frag_t(Lak, 16 * ub, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
+            put4(Zm, 16 * tb + r16, 16 * ub + 4 * g4, acc);
+        } else {
+            put4(Zm, r16, 16 + 4 * g4, zero4());  // t < 16 <= u
+        }
+    }
+    lds_barrier();
+
+    // ---- P, M, E, F to the chunk's operand block; every lane writes four
+    // consecutive columns of one row per tile
+    E* ob = reinterpret_cast<E*>(static_cast<char*>(p.ops) + (int64_t)item * kOpsBytes);
+    if (wave == 2) {
+        // F[t][u] = Mrk[t][u] + sum_s Mrb[t][s] Z[s][u]; accumulator element (u, t)
+        const f32x4 f00 = fmma(mk0, frag_t(Zm, 0, 0, lane), frag_n(Mrb, 0, 0, lane));
+        const f32x4 f01 = fmma(mk1, frag_t(Zm, 0, 0, lane), frag_n(Mrb, 16, 0, lane));
+        const f32x4 f11 = fmma(mk2, frag_t(Zm, 16, 0, lane), frag_n(Mrb, 16, 0, lane));
+        gput4(ob + O::F, C * C, r16 * C + 4 * g4, f00);
+        gput4(ob + O::F, C * C, (16 + r16) * C + 4 * g4, f01);
+        gput4(ob + O::F, C * C, (16 + r16) * C + 16 + 4 * g4, f11);
+        gput4(ob + O::F, C * C, r16 * C + 16 + 4 * g4, zero4());
+    }
+    const int w3 = wave == 3 ? 2 : wave;
+    const int jlo = wave == 2 ? 27 : 9 * w3, jhi = wave == 2 ? 32 : 9 * w3 + 9;
+    for (int jj = jlo; jj < jhi; ++jj) {
+        if (jj < 16) {
+            // P[j][j'] = (delta + sum_t W1[t][j] Btil[t][j']) gamma_last[j']; element (j', j)
+            const int pb = jj & 3, qb = jj >> 2;
+            f32x4 acc = fmma(zero4(), frag_t(Bm, 16 * pb, 0, lane), frag_t(W1, 16 * qb, 0, lane));
+            const int j = 16 * qb + r16, jp0 = 16 * pb + 4 * g4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = (acc[q] + (jp0 + q == j ? 1.f : 0.f)) * glast[jp0 + q];
+            gput4(ob + O::P, D * D, j * D + jp0, acc);
+        } else if (jj < 24) {
+            // M[t][j] = (sum_s Z[s][t] Btil[s][j] + Ktil[t][j]) gamma_last[j]; element (j, t)
+            const int jb = (jj - 16) & 3, tb = (jj - 16) >> 2;
+            f32x4 acc = fmma(zero4(), frag_t(Bm, 16 * jb, 0, lane), frag_t(Zm, 16 * tb, 0, lane));
+            const int t = 16 * tb + r16, j0 = 16 * jb + 4 * g4;
+            const f32x4 kt = get4(Km, t, j0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = (acc[q] + kt[q]) * glast[j0 + q];
+            gput4(ob + O::M, C * D, t * D + j0, acc);
+        } else {
+            // E[t][j] = Rhat[t][j] + sum_s Mrb[t][s] W1[s][j]; element (j, t)
+            const int jb = (jj - 24) & 3, tb = (jj - 24) >> 2;
+            f32x4 acc = fmma(zero4(), frag_t(W1, 16 * jb, 0, lane), frag_n(Mrb, 16 * tb, 0, lane));
+            const int t = 16 * tb + r16, j0 = 16 * jb + 4 * g4;
+            acc += get4(R, t, j0);
+            gput4(ob + O::E_, C * D, t * D + j0, acc);
+        }
+    }
+}
+
+// --------------------------------------------------------------------- scan
+template <bool SPLIT>
+struct ScanSmem {
+    using F = Fmt<SPLIT>;
+    static constexpr int P = 0;                        // (j, j')
+    static constexpr int M = P + F::bytes(D, D);       // (t, j)
+    static constexpr int E = M + F::bytes(C, D);       // (t, j)
+    static constexpr int Fm = E + F::bytes(C, D);      // (t, u)
+    static constexpr int buf = Fm + F::bytes(C, C);    // one chunk's operands
+    static constexpr int total = 2 * buf;
+};
+
+// One chunk's operand block, global (unpadded) -> registers -> LDS (padded
+// operand rows).  Thread tid moves the 16-byte units tid + NT*u.
+template <bool SPLIT, int NT>
+struct OpsCopy {
+    static constexpr int N16 = kOpsBytes / 16;
+    static constexpr int PER = N16 / NT;
+    static_assert(N16 % NT == 0, "operand block split");
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 v[PER];
+    int off[PER];  // LDS byte offsets inside a buffer
+
+    __device__ __forceinline__ void init(int tid) {
+        using O = OpsLayout<SPLIT>;
+        using Lm = ScanSmem<SPLIT>;
+        constexpr int EPU = SPLIT ? 8 : 4;  // storage elements per 16 bytes
+        constexpr int ESZ = SPLIT ? 2 : 4;
+        constexpr int PAD = Fmt<SPLIT>::pad;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = (tid + NT * u) * EPU;
+            int first, lbase, kshift, rkshift;  // rows * cols = 1 << rkshift, cols = 1 << kshift
+            if (e < O::M) { first = O::P; lbase = Lm::P; kshift = 6; rkshift = 12; }
+            else if (e < O::E_) { first = O::M; lbase = Lm::M; kshift = 6; rkshift = 11; }
+            else if (e < O::F) { first = O::E_; lbase = Lm::E; kshift = 6; rkshift = 11; }
+            else { first = O::F; lbase = Lm::Fm; kshift = 5; rkshift = 10; }
+            const int local = e - first;
+            const int plane = local >> rkshift, rem = local & ((1 << rkshift) - 1);
+            const int row = rem >> kshift, col = rem & ((1 << kshift) - 1);
+            const int rows = 1 << (rkshift - kshift), ld = (1 << kshift) + PAD;
+            off[u] = lbase + ((plane * rows + row) * ld + col) * ESZ;
+        }
+    }
+    __device__ __forceinline__ void load(const char* src, int tid) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) v[u] = reinterpret_cast<const u32x4*>(src)[tid + NT * u];
+    }
+    __device__ __forceinline__ void store(char* buf) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) *reinterpret_cast<u32x4*>(buf + off[u]) = v[u];
+    }
+};
+
+template <typename XT>
+__device__ __forceinline__ float xval(XT x);
+template <>
+__device__ __forceinline__ float xval<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float xval<uint16_t>(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// BWD = false: forward over v (InT), S from h0 -> y, checkpoints, hT.
+// BWD = true : backward over dy (fp32), G from dhT -> dv, dh_ckpt, dh0.
+template <typename InT, bool SPLIT, int NWV, bool BWD>
+__global__ __launch_bounds__(64 * NWV) void scan_kernel(ScanArgs p, int xcd) {
+    constexpr int NT = 64 * NWV, NSUB = 4 / NWV;
+    using XT = typename std::conditional<BWD, float, InT>::type;
+    using L = ScanSmem<SPLIT>;
+    using M = Mat<SPLIT>;
+    using Fr = Frag<SPLIT>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    int head, sub;
+    block_map(blockIdx.x, NSUB, xcd != 0, head, sub);
+    const int n0 = 16 * (sub * NWV + wave);  // this wave's 16 rows of the state
+    const int bb = head / p.H, hh = head % p.H;
+    const int64_t tstride = (int64_t)p.H * D;
+    const int64_t roff = (int64_t)(n0 + r16) * D + 4 * g4;  // this lane's part of a D x D state
+    const int64_t soff = (int64_t)head * D * D + roff;
+    const char* ops = static_cast<const char*>(p.ops) + (int64_t)head * p.NC * kOpsBytes;
+    const XT* gx = static_cast<const XT*>(p.x);
+    const int NC = p.NC;
+
+    // state rows n0 + r: st[m][q] = X[n0 + r][16m + 4g + q]
+    f32x4 st[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st[m] = p.s0 ? *reinterpret_cast<const f32x4*>(p.s0 + soff + 16 * m) : zero4();
+
+    // token values of the chunk for this lane: tokens 16h + 4g + q, column n0 + r
+    XT xraw[8];
+    auto load_x = [&](int c) {
+        const int t0 = c * C, Cc = min(C, p.T - t0);
+        const int64_t b0 = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D + n0 + r16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 16 * (e >> 2) + 4 * g4 + (e & 3);
+            xraw[e] = gx[b0 + min(t, Cc - 1) * tstride];
+        }
+    };
+
+    OpsCopy<SPLIT, NT> cp;
+    cp.init(tid);
+    auto chunk_of = [&](int it) { return BWD ? NC - 1 - it : it; };
+    cp.load(ops + (int64_t)chunk_of(0) * kOpsBytes, tid);
+    load_x(chunk_of(0));
+    cp.store(smem);
+    if (NC > 1) cp.load(ops + (int64_t)chunk_of(1) * kOpsBytes, tid);
+    lds_barrier();
+
+    for (int it = 0; it < NC; ++it) {
+        const int c = chunk_of(it);
+        const int t0 = c * C, Cc = min(C, p.T - t0);
+        // operands of the next chunk into the other buffer (read one chunk
+        // ago by every wave, released by the barrier that ended it)
+        if (it + 1 < NC) {
+            cp.store(smem + ((it + 1) & 1) * L::buf);
+            if (it + 2 < NC) cp.load(ops + (int64_t)chunk_of(it + 2) * kOpsBytes, tid);
+        }
+        f32x4 xa, xb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xa[q] = 4 * g4 + q < Cc ? xval(xraw[q]) : 0.f;
+            xb[q] = 16 + 4 * g4 + q < Cc ? xval(xraw[4 + q]) : 0.f;
+        }
+        if (it + 1 < NC) load_x(chunk_of(it + 1));
+
+        char* lb = smem + (it & 1) * L::buf;
+        const M Pm = make_mat<SPLIT>(lb, L::P, D, D), Mm = make_mat<SPLIT>(lb, L::M, C, D);
+        const M Em = make_mat<SPLIT>(lb, L::E, C, D), Fm = make_mat<SPLIT>(lb, L::Fm, C, C);
+        const Fr s0f = frag_acc<SPLIT>(st[0], st[1]), s1f = frag_acc<SPLIT>(st[2], st[3]);
+        const int64_t obase = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D + n0 + r16;
+        f32x4 nw[4];
+        if constexpr (!BWD) {
+            if (p.ckpt) {
+                float* ck = p.ckpt + ((int64_t)head * NC + c) * D * D + roff;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(ck + 16 * m) = st[m];
+            }
+            const Fr vf = frag_exact<SPLIT>(xa, xb);
+            // S_end^T[j'][i] = sum_j P[j][j'] S[i][j] + sum_t M[t][j'] V[t][i]
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 a = fmma(zero4(), frag_t(Pm, 16 * m, 0, lane), s0f);
+                a = fmma(a, frag_t(Pm, 16 * m, 32, lane), s1f);
+                nw[m] = fmma<false, true>(a, frag_t(Mm, 16 * m, 0, lane), vf);
+            }
+            // Y[t][i] = sum_j E[t][j] S[i][j] + sum_s F[t][s] V[s][i]
+            if (p.out) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    f32x4 a = fmma(zero4(), frag_n(Em, 16 * tb, 0, lane), s0f);
+                    a = fmma(a, frag_n(Em, 16 * tb, 32, lane), s1f);
+                    a = fmma<false, true>(a, frag_n(Fm, 16 * tb, 0, lane), vf);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int t = 16 * tb + 4 * g4 + q;
+                        if (t < Cc) p.out[obase + t * tstride] = a[q];
+                    }
+                }
+            }
+        } else {
+            const Fr df = frag_acc<SPLIT>(xa, xb);
+            // dv[t][i] = sum_j M[t][j] G[i][j] + sum_u F[u][t] DY[u][i]
+            if (p.out) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    f32x4 a = fmma(zero4(), frag_n(Mm, 16 * tb, 0, lane), s0f);
+                    a = fmma(a, frag_n(Mm, 16 * tb, 32, lane), s1f);
+                    a = fmma(a, frag_t(Fm, 16 * tb, 0, lane), df);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int t = 16 * tb + 4 * g4 + q;
+                        if (t < Cc) p.out[obase + t * tstride] = a[q];
+                    }
+                }
+            }
+            // G_start^T[j'][i] = sum_j P[j'][j] G[i][j] + sum_t E[t][j'] DY[t][i]
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 a = fmma(zero4(), frag_n(Pm, 16 * m, 0, lane), s0f);
+                a = fmma(a, frag_n(Pm, 16 * m, 32, lane), s1f);
+                nw[m] = fmma(a, frag_t(Em, 16 * m, 0, lane), df);
+            }
+            if (p.ckpt) {
+                float* ck = p.ckpt + ((int64_t)head * NC + c) * D * D + roff;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(ck + 16 * m) = nw[m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) st[m] = nw[m];
+        lds_barrier();
+    }
+    if (p.sT) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(p.sT + soff + 16 * m) = st[m];
+    }
+}
+
+template <typename F>
+hipError_t set_smem(F kern, int bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               bytes);
+}
+
+template <typename InT, bool SPLIT>
+hipError_t launch_prepare_typed(const PrepArgs& a, hipStream_t s) {
+    using L = PrepSmem<SPLIT>;
+    auto kern = chunk_prepare_kernel<InT, SPLIT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = set_smem(kern, L::total);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int items = a.B * a.H * a.NC;
+    hipLaunchKernelGGL(kern, dim3(items), dim3(256), L::total, s, a);
+    return hipGetLastError();
+}
+
+template <typename InT, bool SPLIT, int NWV, bool BWD>
+hipError_t launch_scan_typed(const ScanArgs& a, hipStream_t s) {
+    using L = ScanSmem<SPLIT>;
+    auto kern = scan_kernel<InT, SPLIT, NWV, BWD>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = set_smem(kern, L::total);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int heads = a.B * a.H;
+    const bool xcd = heads % 8 == 0;
+    hipLaunchKernelGGL(kern, dim3(heads * (4 / NWV)), dim3(64 * NWV), L::total, s, a, xcd ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <typename InT, bool SPLIT, bool BWD>
+hipError_t launch_scan_nwv(const ScanArgs& a, hipStream_t s) {
+    // Fewer heads than CUs: spread each head's 4 waves over 2 workgroups.
+    if (a.B * a.H <= 128) return launch_scan_typed<InT, SPLIT, 2, BWD>(a, s);
+    return launch_scan_typed<InT, SPLIT, 4, BWD>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_chunk_prepare(const PrepArgs& a, bool bf16, hipStream_t s) {
+    if (bf16) return launch_prepare_typed<uint16_t, true>(a, s);
+    return launch_prepare_typed<float, false>(a, s);
+}
+
+hipError_t launch_scan(const ScanArgs& a, bool bf16, bool bwd, hipStream_t s) {
+    if (bf16) return bwd ? launch_scan_nwv<uint16_t, true, true>(a, s) : launch_scan_nwv<uint16_t, true, false>(a, s);
+    return bwd ? launch_scan_nwv<float, false, true>(a, s) : launch_scan_nwv<float, false, false>(a, s);
+}
+
+}  // namespace wkv7

@@ -28,8 +28,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = L.lib()
     names = declared_functions()
-    assert {"wkv7_fwd", "wkv7_bwd", "wkv7_fwd_sequential", "wkv7_bwd_workspace_bytes", "wkv7_chunk_inverse",
-            "wkv7_fwd_chunks", "wkv7_bwd_state", "wkv7_bwd_inputs"} <= set(names)
+    assert {"wkv7_fwd", "wkv7_bwd", "wkv7_fwd_sequential", "wkv7_bwd_workspace_bytes", "wkv7_chunk_prepare",
+            "wkv7_fwd_scan", "wkv7_bwd_scan", "wkv7_bwd_inputs", "wkv7_chunk_ops_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in wkv7.h but not exported"
 
@@ -45,11 +45,13 @@ def test_queries():
     assert lib.wkv7_version() >= 100
     assert lib.wkv7_chunk_len() == 32
     assert [L.num_chunks(t) for t in (0, 1, 31, 32, 33, 64, 1024)] == [0, 1, 1, 1, 2, 2, 32]
-    assert L.chunk_inv_bytes(12, 1024, 6) == 12 * 6 * 32 * 32 * 32 * 4
-    assert L.workspace_bytes(12, 1024, 6) == 12 * 6 * 32 * 64 * 64 * 4 + L.chunk_inv_bytes(12, 1024, 6)
-    assert L.workspace_bytes(1, 1, 1) == 64 * 64 * 4 + 32 * 32 * 4
+    per_chunk = 32 * 32 * 4 + 36864          # (I - L)^-1 in fp32 + the transition operands
+    assert L.chunk_ops_bytes(12, 1024, 6) == 12 * 6 * 32 * per_chunk
+    assert L.workspace_bytes(12, 1024, 6) == 12 * 6 * 32 * 64 * 64 * 4 + L.chunk_ops_bytes(12, 1024, 6)
+    assert L.workspace_bytes(1, 1, 1) == 64 * 64 * 4 + per_chunk
     assert L.fwd_workspace_bytes(1, 1, 1) == 0
-    assert L.fwd_workspace_bytes(2, 33, 3) == 2 * 3 * 2 * 32 * 32 * 4
+    assert L.fwd_workspace_bytes(2, 33, 3) == 2 * 3 * 2 * per_chunk
+    assert L.chunk_ops_bytes(1, 10, 1, 32) == 0
     assert L.workspace_bytes(1, 0, 1) == 0
     assert L.workspace_bytes(1, 10, 1, 32) == 0
     for s in range(8):
@@ -77,7 +79,7 @@ def fake(n):            # distinct non-overlapping fake buffers, 64 MiB apart
 
 def fwd_args(**over):
     a = dict(B=1, T=64, H=1, D=64, dt=1, r=fake(0), w=fake(1), k=fake(2), v=fake(3), a=fake(4),
-             b=fake(5), h0=None, y=fake(6), ck=fake(7), hT=fake(8), inv=fake(10), ws=fake(11), wsb=1 << 20)
+             b=fake(5), h0=None, y=fake(6), ck=fake(7), hT=fake(8), ops=fake(10), ws=fake(11), wsb=1 << 20)
     a.update(over)
     return a
 
@@ -88,13 +90,13 @@ def call_fwd(fn="wkv7_fwd", **over):
     head = (a["B"], a["T"], a["H"], a["D"], a["dt"], a["r"], a["w"], a["k"], a["v"], a["a"], a["b"])
     if fn == "wkv7_fwd":
         return f(*head, a["h0"], a["y"], a["ck"], a["hT"], a["ws"], a["wsb"], None)
-    if fn == "wkv7_fwd_chunks":
-        return f(*head, a["inv"], a["h0"], a["y"], a["ck"], a["hT"], None)
+    if fn == "wkv7_fwd_scan":
+        return f(*head[:5], a["v"], a["ops"], a["h0"], a["y"], a["ck"], a["hT"], None)
     return f(*head, a["h0"], a["y"], a["ck"], a["hT"], None)
 
 
 @needs_no_gpu
-@pytest.mark.parametrize("fn", ["wkv7_fwd", "wkv7_fwd_sequential", "wkv7_fwd_chunks"])
+@pytest.mark.parametrize("fn", ["wkv7_fwd", "wkv7_fwd_sequential", "wkv7_fwd_scan"])
 def test_fwd_rejects_bad_arguments(fn):
     c = lambda **o: call_fwd(fn, **o)
     assert c(D=32) == ERR_SHAPE
@@ -102,39 +104,46 @@ def test_fwd_rejects_bad_arguments(fn):
     assert c(B=0) == ERR_SHAPE
     assert c(H=-1) == ERR_SHAPE
     assert c(dt=7) == ERR_DTYPE
-    assert c(r=None) == ERR_ARG
-    assert c(b=None) == ERR_ARG
+    assert c(v=None) == ERR_ARG
     assert c(y=None, ck=None, hT=None) == ERR_ARG
-    assert c(w=fake(1) + 4) == ERR_ALIGN
+    assert c(v=fake(3) + 4) == ERR_ALIGN
     assert c(h0=fake(9) + 8) == ERR_ALIGN
-    assert c(y=fake(0)) == ERR_ALIAS                 # y on top of r
-    assert c(y=fake(5) + 4096) == ERR_ALIAS          # y overlapping the tail of b
+    assert c(y=fake(3)) == ERR_ALIAS                 # y on top of v
+    assert c(y=fake(3) + 4096) == ERR_ALIAS          # y overlapping the tail of v
     assert c(hT=fake(6)) == ERR_ALIAS                # hT inside y
     assert c(ck=fake(6) + 16) == ERR_ALIAS           # ckpt overlapping y
     assert c(h0=fake(9), hT=fake(9) + 64) == ERR_ALIAS  # hT overlapping h0 but not equal
+    if fn != "wkv7_fwd_scan":
+        assert c(r=None) == ERR_ARG
+        assert c(b=None) == ERR_ARG
+        assert c(w=fake(1) + 4) == ERR_ALIGN
+        assert c(y=fake(0)) == ERR_ALIAS             # y on top of r
+        assert c(y=fake(5) + 4096) == ERR_ALIAS      # y overlapping the tail of b
     if fn == "wkv7_fwd":
         assert c(ws=None) == ERR_WS
         assert c(wsb=1000) == ERR_WS
         assert c(ws=fake(11) + 4) == ERR_ALIGN
         assert c(ws=fake(6)) == ERR_ALIAS                # workspace on top of y
-    if fn == "wkv7_fwd_chunks":
-        assert c(inv=None) == ERR_ARG
-        assert c(inv=fake(10) + 8) == ERR_ALIGN
-        assert c(y=fake(10)) == ERR_ALIAS                # y on top of the inverses
+    if fn == "wkv7_fwd_scan":
+        assert c(ops=None) == ERR_ARG
+        assert c(ops=fake(10) + 8) == ERR_ALIGN
+        assert c(y=fake(10)) == ERR_ALIAS                # y on top of the chunk operands
 
 
 @needs_no_gpu
-def test_chunk_inverse_rejects_bad_arguments():
+def test_chunk_prepare_rejects_bad_arguments():
     lib = L.lib()
-    c = lambda B=1, T=64, H=1, D=64, dt=1, w=fake(0), a=fake(1), b=fake(2), out=fake(3): \
-        lib.wkv7_chunk_inverse(B, T, H, D, dt, w, a, b, out, None)
+    c = lambda B=1, T=64, H=1, D=64, dt=1, r=fake(4), w=fake(0), k=fake(5), a=fake(1), b=fake(2), out=fake(3): \
+        lib.wkv7_chunk_prepare(B, T, H, D, dt, r, w, k, a, b, out, None)
     assert c(D=48) == ERR_SHAPE
     assert c(T=0) == ERR_SHAPE
     assert c(dt=5) == ERR_DTYPE
     assert c(out=None) == ERR_ARG
     assert c(a=None) == ERR_ARG
+    assert c(k=None) == ERR_ARG
     assert c(out=fake(3) + 2) == ERR_ALIGN
     assert c(out=fake(1)) == ERR_ALIAS
+    assert c(out=fake(5) - 64) == ERR_ALIAS          # operands running into k
 
 
 @needs_no_gpu
@@ -153,11 +162,10 @@ def test_bwd_rejects_bad_arguments():
                             a["da"], a["db"], a["dh0"], a["ws"], a["wsb"], None)
 
     def cs(**o):
-        a = dict(dt=1, dy=fake(0), dhT=None, r=fake(1), w=fake(2), k=fake(3), a=fake(5), b=fake(6),
-                 inv=fake(16), dck=fake(17), dv=fake(11), dh0=None, T=T)
+        a = dict(dt=1, dy=fake(0), dhT=None, inv=fake(16), dck=fake(17), dv=fake(11), dh0=None, T=T)
         a.update(o)
-        return lib.wkv7_bwd_state(B, a["T"], H, D, a["dt"], a["dy"], a["dhT"], a["r"], a["w"], a["k"], a["a"],
-                                  a["b"], a["inv"], a["dck"], a["dv"], a["dh0"], None)
+        return lib.wkv7_bwd_scan(B, a["T"], H, D, a["dt"], a["dy"], a["dhT"], a["inv"], a["dck"], a["dv"],
+                                 a["dh0"], None)
 
     def ci(**o):
         a = dict(dt=1, dy=fake(0), dhT=None, r=fake(1), w=fake(2), k=fake(3), v=fake(4), a=fake(5), b=fake(6),
@@ -173,7 +181,8 @@ def test_bwd_rejects_bad_arguments():
     assert cs(inv=None) == ERR_ARG
     assert cs(dck=None) == ERR_ARG
     assert cs(dv=fake(11) + 4) == ERR_ALIGN
-    assert cs(dck=fake(16)) == ERR_ALIAS              # dh_ckpt on the inverses
+    assert cs(dck=fake(16)) == ERR_ALIAS              # dh_ckpt on the chunk operands
+    assert cs(dh0=fake(0) + 64) == ERR_ALIAS          # dh0 inside dy
     assert cs(dv=fake(0)) == ERR_ALIAS                # dv on dy
     assert ci(inv=None) == ERR_ARG
     assert ci(dck=None) == ERR_ARG

@@ -139,9 +139,10 @@ def test_chunk_inverse_matches_direct_solve(dtype, T):
     x = make_inputs(2, T, 3, dtype, seed=300 + T)
     dev = torch.device("cuda:0")
     note(f"chunk inverse {dtype} T{T}")
-    inv = L.chunk_inverse(x.w.to(dev), x.a.to(dev), x.b.to(dev)).double().cpu().numpy()
+    B, _, H, D = x.w.shape
+    ops = L.chunk_prepare(*(t.to(dev) for t in (x.r, x.w, x.k, x.a, x.b)))
+    inv = L.chunk_inverse(ops, B, T, H).double().cpu().numpy()
     w, a, b = (t.double().numpy() for t in (x.w, x.a, x.b))
-    B, _, H, D = w.shape
     worst = 0.0
     for bb in range(B):
         for hh in range(H):
