@@ -609,6 +609,23 @@ __device__ __forceinline__ void tinv_store(const float* tf, Mat<SPLIT> T, bool r
 
 
 // ---------------------------------------------------------------------------
+// Buffer resources: a base address and a size in bytes.  Loads at or past the
+// size return 0 and stores there are dropped by the hardware, so a ragged
+// tail needs no branch (and a wave's counts of outstanding memory operations
+// stay exact).  A size of 0 turns every access off.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bstore(float v, Rsrc r, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void bstore4(f32x4 v, Rsrc r, int voff, int soff) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+}
+
+// ---------------------------------------------------------------------------
 // Fragments with a permuted k order (used by the chunk-operand kernels).
 //
 // A 32-wide block of the contraction index, [c0, c0 + 32), is dealt to the

@@ -217,19 +217,20 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
 }
 
 // --------------------------------------------------------------------- scan
+// LDS image of one chunk's operands (operand rows in the Mat format of
+// wkv7_device.h: padded rows, hi then lo plane for the split format).
 template <bool SPLIT>
-struct ScanSmem {
+struct OpsImage {
     using F = Fmt<SPLIT>;
     static constexpr int P = 0;                        // (j, j')
     static constexpr int M = P + F::bytes(D, D);       // (t, j)
     static constexpr int E = M + F::bytes(C, D);       // (t, j)
     static constexpr int Fm = E + F::bytes(C, D);      // (t, u)
-    static constexpr int buf = Fm + F::bytes(C, C);    // one chunk's operands
-    static constexpr int total = 2 * buf;
+    static constexpr int bytes = Fm + F::bytes(C, C);
 };
 
-// One chunk's operand block, global (unpadded) -> registers -> LDS (padded
-// operand rows).  Thread tid moves the 16-byte units tid + NT*u.
+// One chunk's operand block, global (unpadded) -> registers -> LDS image.
+// Thread tid of NT moves the 16-byte units tid + NT * u.
 template <bool SPLIT, int NT>
 struct OpsCopy {
     static constexpr int N16 = kOpsBytes / 16;
@@ -241,7 +242,7 @@ struct OpsCopy {
 
     __device__ __forceinline__ void init(int tid) {
         using O = OpsLayout<SPLIT>;
-        using Lm = ScanSmem<SPLIT>;
+        using I = OpsImage<SPLIT>;
         constexpr int EPU = SPLIT ? 8 : 4;  // storage elements per 16 bytes
         constexpr int ESZ = SPLIT ? 2 : 4;
         constexpr int PAD = Fmt<SPLIT>::pad;
@@ -249,10 +250,10 @@ struct OpsCopy {
         for (int u = 0; u < PER; ++u) {
             const int e = (tid + NT * u) * EPU;
             int first, lbase, kshift, rkshift;  // rows * cols = 1 << rkshift, cols = 1 << kshift
-            if (e < O::M) { first = O::P; lbase = Lm::P; kshift = 6; rkshift = 12; }
-            else if (e < O::E_) { first = O::M; lbase = Lm::M; kshift = 6; rkshift = 11; }
-            else if (e < O::F) { first = O::E_; lbase = Lm::E; kshift = 6; rkshift = 11; }
-            else { first = O::F; lbase = Lm::Fm; kshift = 5; rkshift = 10; }
+            if (e < O::M) { first = O::P; lbase = I::P; kshift = 6; rkshift = 12; }
+            else if (e < O::E_) { first = O::M; lbase = I::M; kshift = 6; rkshift = 11; }
+            else if (e < O::F) { first = O::E_; lbase = I::E; kshift = 6; rkshift = 11; }
+            else { first = O::F; lbase = I::Fm; kshift = 5; rkshift = 10; }
             const int local = e - first;
             const int plane = local >> rkshift, rem = local & ((1 << rkshift) - 1);
             const int row = rem >> kshift, col = rem & ((1 << kshift) - 1);
@@ -270,20 +271,102 @@ struct OpsCopy {
     }
 };
 
-template <typename XT>
-__device__ __forceinline__ float xval(XT x);
-template <>
-__device__ __forceinline__ float xval<float>(float x) { return x; }
-template <>
-__device__ __forceinline__ float xval<uint16_t>(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+// LDS plan of the scan: double buffers of one chunk's operands, of its
+// token rows (v exact, or dy split) and of its output rows (y or dv, fp32).
+template <bool SPLIT, int NWV>
+struct ScanLds {
+    using F = Fmt<SPLIT>;
+    static constexpr int NI = 16 * NWV;                 // state rows of the workgroup
+    static constexpr int OPS = OpsImage<SPLIT>::bytes;
+    static constexpr int XB = F::bytes(C, NI);          // rows (t, i)
+    static constexpr int LDO = NI + 4;                  // fp32 output row stride
+    static constexpr int OB = C * LDO * 4;
+    static constexpr int X0 = 2 * OPS, O0 = X0 + 2 * XB;
+    static constexpr int total = O0 + 2 * OB;
+    static_assert(total <= 160 * 1024, "scan LDS");
+};
+
+// The token rows of one chunk for a workgroup's NI columns, memory ->
+// registers -> LDS.  Memory thread ct moves 16-byte pieces ct + NTC * u:
+// piece -> (token t, NPR pieces per token row).  Tokens past the end of the
+// sequence read as 0 (buffer resource ending at the head's last token).
+template <typename XT, bool SPLIT, int NWV>
+struct XCopy {
+    static constexpr int NI = 16 * NWV, NTC = 64 * NWV;
+    static constexpr int EPP = 16 / (int)sizeof(XT);            // elements per piece
+    static constexpr int NPR = NI / EPP;                        // pieces per token row
+    static constexpr int PER = C * NPR / NTC;
+    static_assert(C * NPR % NTC == 0 && PER >= 1, "token row split");
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 v[PER];
+
+    __device__ __forceinline__ void load(Rsrc r, int c, int HD, int ct) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * EPP;
+            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 r, (t * HD + e0) * (int)sizeof(XT), c * C * HD * (int)sizeof(XT), 0));
+        }
+    }
+    // rows (t, i) of an operand matrix: exact bf16 (v) or split (dy)
+    __device__ __forceinline__ void store(Mat<SPLIT> X, int ct) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * EPP;
+            if constexpr (sizeof(XT) == 2) {
+                *reinterpret_cast<u32x4*>(reinterpret_cast<__bf16*>(X.p) + t * X.ld + e0) = v[u];
+            } else {
+                put4(X, t, e0, __builtin_bit_cast(f32x4, v[u]));
+            }
+        }
+    }
+};
+
+// Memory waves store one chunk's output rows (fp32, rows t, NI columns)
+// from LDS: 16 bytes per piece.
+template <int NWV>
+__device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD, int ct) {
+    constexpr int NI = 16 * NWV, NTC = 64 * NWV, NPR = NI / 4, PER = C * NPR / NTC, LDO = NI + 4;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * 4;
+        bstore4(*reinterpret_cast<const f32x4*>(ob + t * LDO + e0), r, (t * HD + e0) * 4, c * C * HD * 4);
+    }
+}
+
+// LDS transpose read of exact bf16 values (hi plane only), see frag_t.
+__device__ __forceinline__ Frag<true> frag_t_exact(Mat<true> X, int col0, int c0, int lane) {
+    const int g = lane >> 4, l16 = lane & 15;
+    const __bf16* p = reinterpret_cast<const __bf16*>(X.p) + (c0 + 4 * g + (l16 >> 2)) * X.ld + col0 + 4 * (l16 & 3);
+    Frag<true> f;
+    f.hi = cat8(as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p))),
+                as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * X.ld))));
+    f.lo = f.hi;
+    return f;
+}
+__device__ __forceinline__ Frag<false> frag_t_exact(Mat<false> X, int col0, int c0, int lane) {
+    return frag_t(X, col0, c0, lane);
+}
 
 // BWD = false: forward over v (InT), S from h0 -> y, checkpoints, hT.
 // BWD = true : backward over dy (fp32), G from dhT -> dv, dh_ckpt, dh0.
+//
+// A workgroup has NWV compute waves (16 state rows each) and NWV memory
+// waves.  The memory waves do all the streaming: the operand block and the
+// token rows of chunk it + 1 into LDS while chunk it is computed (loaded two
+// chunks ahead into two register sets), and the output rows of chunk it - 1
+// from LDS to memory.  The compute waves read LDS, run the products and
+// store only the state checkpoints.  Token tensors are addressed through
+// per-head buffer resources that end after the head's last token: tokens
+// past the end of a ragged last chunk read as 0 and their stores are
+// dropped by the hardware, so no branch surrounds a memory access inside the
+// chunk loop.
 template <typename InT, bool SPLIT, int NWV, bool BWD>
-__global__ __launch_bounds__(64 * NWV) void scan_kernel(ScanArgs p, int xcd) {
-    constexpr int NT = 64 * NWV, NSUB = 4 / NWV;
+__global__ __launch_bounds__(128 * NWV) void scan_kernel(ScanArgs p, int xcd) {
+    constexpr int NSUB = 4 / NWV, NTC = 64 * NWV;
     using XT = typename std::conditional<BWD, float, InT>::type;
-    using L = ScanSmem<SPLIT>;
+    using I = OpsImage<SPLIT>;
+    using L = ScanLds<SPLIT, NWV>;
     using M = Mat<SPLIT>;
     using Fr = Frag<SPLIT>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -291,125 +374,137 @@ __global__ __launch_bounds__(64 * NWV) void scan_kernel(ScanArgs p, int xcd) {
     const int r16 = lane & 15, g4 = lane >> 4;
     int head, sub;
     block_map(blockIdx.x, NSUB, xcd != 0, head, sub);
-    const int n0 = 16 * (sub * NWV + wave);  // this wave's 16 rows of the state
-    const int bb = head / p.H, hh = head % p.H;
-    const int64_t tstride = (int64_t)p.H * D;
-    const int64_t roff = (int64_t)(n0 + r16) * D + 4 * g4;  // this lane's part of a D x D state
-    const int64_t soff = (int64_t)head * D * D + roff;
-    const char* ops = static_cast<const char*>(p.ops) + (int64_t)head * p.NC * kOpsBytes;
-    const XT* gx = static_cast<const XT*>(p.x);
     const int NC = p.NC;
+    const int bb = head / p.H, hh = head % p.H;
+    const int HD = p.H * D;                                            // token stride (elements)
+    const int i0 = 16 * sub * NWV;                                     // the workgroup's first state row
+    const int64_t tok0 = (int64_t)bb * p.T * HD + (int64_t)hh * D;     // token 0 of this head
+    const uint32_t head_span = (uint32_t)((int64_t)(p.T - 1) * HD + D);  // elements up to its last token
+    auto chunk_of = [&](int it) { return BWD ? NC - 1 - it : it; };
+    auto xmat = [&](int it) { return make_mat<SPLIT>(smem, L::X0 + (it & 1) * L::XB, C, L::NI); };
+    auto obuf = [&](int it) { return reinterpret_cast<float*>(smem + L::O0 + (it & 1) * L::OB); };
+
+    if (wave >= NWV) {
+        // ---- memory waves
+        const int ct = tid - NTC;
+        const char* ops = static_cast<const char*>(p.ops) + (int64_t)head * NC * kOpsBytes;
+        auto ops_of = [&](int it) { return ops + (int64_t)chunk_of(min(it, NC - 1)) * kOpsBytes; };
+        const Rsrc rx = make_rsrc(static_cast<const XT*>(p.x) + tok0 + i0, head_span * sizeof(XT));
+        const Rsrc ro = make_rsrc(p.out ? p.out + tok0 + i0 : nullptr, p.out ? head_span * 4 : 0);
+        const Rsrc rnull = make_rsrc(nullptr, 0);
+        OpsCopy<SPLIT, NTC> oa, ob;
+        XCopy<XT, SPLIT, NWV> xa, xb;
+        oa.init(ct);
+        ob.init(ct);
+        auto fetch = [&](OpsCopy<SPLIT, NTC>& o, XCopy<XT, SPLIT, NWV>& x, int it) {
+            o.load(ops_of(it), ct);
+            x.load(rx, chunk_of(min(it, NC - 1)), HD, ct);
+        };
+        auto put = [&](const OpsCopy<SPLIT, NTC>& o, const XCopy<XT, SPLIT, NWV>& x, int it) {
+            o.store(smem + (it & 1) * L::OPS);
+            x.store(xmat(it), ct);
+        };
+        // outputs of iteration it - 1 (nothing before the first)
+        auto out = [&](int it) {
+            store_out<NWV>(obuf(it - 1), it > 0 ? ro : rnull, chunk_of(max(it - 1, 0)), HD, ct);
+        };
+        fetch(oa, xa, 0);
+        put(oa, xa, 0);
+        fetch(ob, xb, 1);
+        fetch(oa, xa, 2);
+        lds_barrier();
+        // Two iterations per trip, straight-line code (so that every wait is
+        // counted exactly).  In iteration it: chunk it + 1 goes into the
+        // buffers the compute waves finished reading in iteration it - 1, its
+        // register set is refilled with chunk it + 3 (clamped), and the
+        // outputs of chunk it - 1 go to memory.  Writes past the last chunk
+        // land in buffers nobody reads any more.  An odd NC ends with one
+        // extra barrier, matched by the compute waves.
+        for (int it = 0; it < NC; it += 2) {
+            put(ob, xb, it + 1);
+            fetch(ob, xb, it + 3);
+            out(it);
+            lds_barrier();
+            put(oa, xa, it + 2);
+            fetch(oa, xa, it + 4);
+            out(it + 1);
+            lds_barrier();
+        }
+        if (!(NC & 1)) out(NC);
+        return;
+    }
+
+    // ---- compute waves
+    const int n0 = i0 + 16 * wave;  // this wave's 16 rows of the state
+    const int roff = (n0 + r16) * D + 4 * g4;                          // this lane's part of a D x D state
+    const int64_t soff = (int64_t)head * D * D + roff;
+    const Rsrc rc = make_rsrc(p.ckpt ? p.ckpt + (int64_t)head * NC * D * D : nullptr,
+                              p.ckpt ? (uint32_t)NC * D * D * 4 : 0);
 
     // state rows n0 + r: st[m][q] = X[n0 + r][16m + 4g + q]
     f32x4 st[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) st[m] = p.s0 ? *reinterpret_cast<const f32x4*>(p.s0 + soff + 16 * m) : zero4();
-
-    // token values of the chunk for this lane: tokens 16h + 4g + q, column n0 + r
-    XT xraw[8];
-    auto load_x = [&](int c) {
-        const int t0 = c * C, Cc = min(C, p.T - t0);
-        const int64_t b0 = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D + n0 + r16;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = 16 * (e >> 2) + 4 * g4 + (e & 3);
-            xraw[e] = gx[b0 + min(t, Cc - 1) * tstride];
-        }
-    };
-
-    OpsCopy<SPLIT, NT> cp;
-    cp.init(tid);
-    auto chunk_of = [&](int it) { return BWD ? NC - 1 - it : it; };
-    cp.load(ops + (int64_t)chunk_of(0) * kOpsBytes, tid);
-    load_x(chunk_of(0));
-    cp.store(smem);
-    if (NC > 1) cp.load(ops + (int64_t)chunk_of(1) * kOpsBytes, tid);
     lds_barrier();
 
     for (int it = 0; it < NC; ++it) {
         const int c = chunk_of(it);
-        const int t0 = c * C, Cc = min(C, p.T - t0);
-        // operands of the next chunk into the other buffer (read one chunk
-        // ago by every wave, released by the barrier that ended it)
-        if (it + 1 < NC) {
-            cp.store(smem + ((it + 1) & 1) * L::buf);
-            if (it + 2 < NC) cp.load(ops + (int64_t)chunk_of(it + 2) * kOpsBytes, tid);
-        }
-        f32x4 xa, xb;
+        if constexpr (!BWD) {   // checkpoint c: the state entering the chunk
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            xa[q] = 4 * g4 + q < Cc ? xval(xraw[q]) : 0.f;
-            xb[q] = 16 + 4 * g4 + q < Cc ? xval(xraw[4 + q]) : 0.f;
+            for (int m = 0; m < 4; ++m) bstore4(st[m], rc, (roff + 16 * m) * 4, c * D * D * 4);
         }
-        if (it + 1 < NC) load_x(chunk_of(it + 1));
-
-        char* lb = smem + (it & 1) * L::buf;
-        const M Pm = make_mat<SPLIT>(lb, L::P, D, D), Mm = make_mat<SPLIT>(lb, L::M, C, D);
-        const M Em = make_mat<SPLIT>(lb, L::E, C, D), Fm = make_mat<SPLIT>(lb, L::Fm, C, C);
+        char* lb = smem + (it & 1) * L::OPS;
+        const M Pm = make_mat<SPLIT>(lb, I::P, D, D), Mm = make_mat<SPLIT>(lb, I::M, C, D);
+        const M Em = make_mat<SPLIT>(lb, I::E, C, D), Fm = make_mat<SPLIT>(lb, I::Fm, C, C);
+        const M Xm = xmat(it);
+        float* ob = obuf(it);
         const Fr s0f = frag_acc<SPLIT>(st[0], st[1]), s1f = frag_acc<SPLIT>(st[2], st[3]);
-        const int64_t obase = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D + n0 + r16;
-        f32x4 nw[4];
+        f32x4 ya, yb;
         if constexpr (!BWD) {
-            if (p.ckpt) {
-                float* ck = p.ckpt + ((int64_t)head * NC + c) * D * D + roff;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(ck + 16 * m) = st[m];
-            }
-            const Fr vf = frag_exact<SPLIT>(xa, xb);
+            const Fr vf = frag_t_exact(Xm, 16 * wave, 0, lane);
             // S_end^T[j'][i] = sum_j P[j][j'] S[i][j] + sum_t M[t][j'] V[t][i]
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 a = fmma(zero4(), frag_t(Pm, 16 * m, 0, lane), s0f);
                 a = fmma(a, frag_t(Pm, 16 * m, 32, lane), s1f);
-                nw[m] = fmma<false, true>(a, frag_t(Mm, 16 * m, 0, lane), vf);
+                st[m] = fmma<false, true>(a, frag_t(Mm, 16 * m, 0, lane), vf);
             }
             // Y[t][i] = sum_j E[t][j] S[i][j] + sum_s F[t][s] V[s][i]
-            if (p.out) {
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    f32x4 a = fmma(zero4(), frag_n(Em, 16 * tb, 0, lane), s0f);
-                    a = fmma(a, frag_n(Em, 16 * tb, 32, lane), s1f);
-                    a = fmma<false, true>(a, frag_n(Fm, 16 * tb, 0, lane), vf);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int t = 16 * tb + 4 * g4 + q;
-                        if (t < Cc) p.out[obase + t * tstride] = a[q];
-                    }
-                }
-            }
+            ya = fmma(zero4(), frag_n(Em, 0, 0, lane), s0f);
+            ya = fmma(ya, frag_n(Em, 0, 32, lane), s1f);
+            ya = fmma<false, true>(ya, frag_n(Fm, 0, 0, lane), vf);
+            yb = fmma(zero4(), frag_n(Em, 16, 0, lane), s0f);
+            yb = fmma(yb, frag_n(Em, 16, 32, lane), s1f);
+            yb = fmma<false, true>(yb, frag_n(Fm, 16, 0, lane), vf);
         } else {
-            const Fr df = frag_acc<SPLIT>(xa, xb);
+            const Fr df = frag_t(Xm, 16 * wave, 0, lane);
             // dv[t][i] = sum_j M[t][j] G[i][j] + sum_u F[u][t] DY[u][i]
-            if (p.out) {
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    f32x4 a = fmma(zero4(), frag_n(Mm, 16 * tb, 0, lane), s0f);
-                    a = fmma(a, frag_n(Mm, 16 * tb, 32, lane), s1f);
-                    a = fmma(a, frag_t(Fm, 16 * tb, 0, lane), df);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int t = 16 * tb + 4 * g4 + q;
-                        if (t < Cc) p.out[obase + t * tstride] = a[q];
-                    }
-                }
-            }
+            ya = fmma(zero4(), frag_n(Mm, 0, 0, lane), s0f);
+            ya = fmma(ya, frag_n(Mm, 0, 32, lane), s1f);
+            ya = fmma(ya, frag_t(Fm, 0, 0, lane), df);
+            yb = fmma(zero4(), frag_n(Mm, 16, 0, lane), s0f);
+            yb = fmma(yb, frag_n(Mm, 16, 32, lane), s1f);
+            yb = fmma(yb, frag_t(Fm, 16, 0, lane), df);
             // G_start^T[j'][i] = sum_j P[j'][j] G[i][j] + sum_t E[t][j'] DY[t][i]
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 a = fmma(zero4(), frag_n(Pm, 16 * m, 0, lane), s0f);
                 a = fmma(a, frag_n(Pm, 16 * m, 32, lane), s1f);
-                nw[m] = fmma(a, frag_t(Em, 16 * m, 0, lane), df);
+                st[m] = fmma(a, frag_t(Em, 16 * m, 0, lane), df);
             }
-            if (p.ckpt) {
-                float* ck = p.ckpt + ((int64_t)head * NC + c) * D * D + roff;
+            // gradient w.r.t. the state entering chunk c
 #pragma unroll
-                for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(ck + 16 * m) = nw[m];
-            }
+            for (int m = 0; m < 4; ++m) bstore4(st[m], rc, (roff + 16 * m) * 4, c * D * D * 4);
         }
+        // output rows (t, i) of this chunk for the memory waves
 #pragma unroll
-        for (int m = 0; m < 4; ++m) st[m] = nw[m];
+        for (int q = 0; q < 4; ++q) {
+            ob[(4 * g4 + q) * L::LDO + 16 * wave + r16] = ya[q];
+            ob[(16 + 4 * g4 + q) * L::LDO + 16 * wave + r16] = yb[q];
+        }
         lds_barrier();
     }
+    if (NC & 1) lds_barrier();  // the memory waves' last trip
     if (p.sT) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(p.sT + soff + 16 * m) = st[m];
@@ -439,17 +534,17 @@ hipError_t launch_prepare_typed(const PrepArgs& a, hipStream_t s) {
 
 template <typename InT, bool SPLIT, int NWV, bool BWD>
 hipError_t launch_scan_typed(const ScanArgs& a, hipStream_t s) {
-    using L = ScanSmem<SPLIT>;
+    constexpr int smem_bytes = ScanLds<SPLIT, NWV>::total;
     auto kern = scan_kernel<InT, SPLIT, NWV, BWD>;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = set_smem(kern, L::total);
+        hipError_t e = set_smem(kern, smem_bytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int heads = a.B * a.H;
     const bool xcd = heads % 8 == 0;
-    hipLaunchKernelGGL(kern, dim3(heads * (4 / NWV)), dim3(64 * NWV), L::total, s, a, xcd ? 1 : 0);
+    hipLaunchKernelGGL(kern, dim3(heads * (4 / NWV)), dim3(128 * NWV), smem_bytes, s, a, xcd ? 1 : 0);
     return hipGetLastError();
 }
 
