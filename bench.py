@@ -67,7 +67,7 @@ def kernel_key(name: str):
         return "chunk_prepare"
     if "scan_kernel" in name:
         return "bwd_scan" if ", true>(" in name else "fwd_scan"
-    if "bwd_chunk_kernel" in name:
+    if "grad_kernel" in name:
         return "bwd_inputs"
     return None
 

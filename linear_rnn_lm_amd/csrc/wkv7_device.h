@@ -17,7 +17,7 @@
 //     S_C = (S0 + U^T Btil + V^T Ktil) diag(gamma_last)
 // where Lab = strict_lower(Ahat Btil^T), Lak = strict_lower(Ahat Ktil^T),
 // Mrb = lower(Rhat Btil^T), Mrk = lower(Rhat Ktil^T).  The backward kernels
-// use the same matrices (see wkv7_bwd.hip).
+// use the same matrices (wkv7_grad.hip).
 //
 // Every product is C[m][n] = sum_k X[m][k] Y[n][k] with both operands held in
 // LDS with k contiguous ("Mat").  Two storage formats:
@@ -57,6 +57,14 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // 1/x with v_rcp_f32 (at most 1 ulp off).
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// One MFMA step: 16x16 tile, accumulator c (fp32).
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // LDS matrix formats and handles.
@@ -175,14 +183,14 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, Mat<SPLIT> X, int m0, Mat<SPLIT>
         for (int k0 = 0; k0 < K; k0 += 32) {
             const bf16x8 xh = *reinterpret_cast<const bf16x8*>(xp + k0);
             const bf16x8 yh = *reinterpret_cast<const bf16x8*>(yp + k0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yh, acc, 0, 0, 0);
+            acc = mfma_bf16(xh, yh, acc);
             if constexpr (!YEX) {
                 const bf16x8 yl = *reinterpret_cast<const bf16x8*>(yp + Y.plane + k0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, yl, acc, 0, 0, 0);
+                acc = mfma_bf16(xh, yl, acc);
             }
             if constexpr (!XEX) {
                 const bf16x8 xl = *reinterpret_cast<const bf16x8*>(xp + X.plane + k0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, yh, acc, 0, 0, 0);
+                acc = mfma_bf16(xl, yh, acc);
             }
         }
     } else {
@@ -190,7 +198,7 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, Mat<SPLIT> X, int m0, Mat<SPLIT>
         const float* yp = reinterpret_cast<const float*>(Y.p) + (n0 + r) * Y.ld + g;
 #pragma unroll
         for (int k0 = 0; k0 < K; k0 += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xp[k0], yp[k0], acc, 0, 0, 0);
+            acc = mfma_f32(xp[k0], yp[k0], acc);
     }
     return acc;
 }
@@ -575,7 +583,7 @@ __device__ __forceinline__ void tri_inverse(const float* L, float* tf, float* sc
     f32x4 acc = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < 16; k0 += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(L[(16 + r) * LDF + k0 + g], tf[(k0 + g) * LDF + r], acc, 0, 0, 0);
+        acc = mfma_f32(L[(16 + r) * LDF + k0 + g], tf[(k0 + g) * LDF + r], acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) scr[(4 * g + q) * 20 + r] = acc[q];
     wave_lds_sync();
@@ -583,7 +591,7 @@ __device__ __forceinline__ void tri_inverse(const float* L, float* tf, float* sc
     acc = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < 16; k0 += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tf[(16 + r) * LDF + 16 + k0 + g], scr[(k0 + g) * 20 + r], acc, 0, 0, 0);
+        acc = mfma_f32(tf[(16 + r) * LDF + 16 + k0 + g], scr[(k0 + g) * 20 + r], acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) tf[(16 + 4 * g + q) * LDF + r] = acc[q];
     wave_lds_sync();
@@ -617,12 +625,20 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+//
+// The whole byte offset goes into the per-lane offset and the scalar offset
+// stays the constant 0: the range check covers the per-lane offset, and a
+// 128-bit store with a constant scalar offset is the form for which the
+// compiler keeps the store's data registers untouched for the wait state the
+// hardware needs before they are overwritten.  (Stores with a register
+// scalar offset lost the last dword of the data to the next instruction's
+// write of that register.)
 __device__ __forceinline__ void bstore(float v, Rsrc r, int voff, int soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff + soff, 0, 0);
 }
 __device__ __forceinline__ void bstore4(f32x4 v, Rsrc r, int voff, int soff) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff + soff, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -735,12 +751,26 @@ __device__ __forceinline__ Frag<false> frag_t(Mat<false> X, int col0, int c0, in
     return f;
 }
 
+// LDS transpose read of exact bf16 values (hi plane only), see frag_t.
+__device__ __forceinline__ Frag<true> frag_t_exact(Mat<true> X, int col0, int c0, int lane) {
+    const int g = lane >> 4, l16 = lane & 15;
+    const __bf16* p = reinterpret_cast<const __bf16*>(X.p) + (c0 + 4 * g + (l16 >> 2)) * X.ld + col0 + 4 * (l16 & 3);
+    Frag<true> f;
+    f.hi = cat8(as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p))),
+                as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * X.ld))));
+    f.lo = f.hi;
+    return f;
+}
+__device__ __forceinline__ Frag<false> frag_t_exact(Mat<false> X, int col0, int c0, int lane) {
+    return frag_t(X, col0, c0, lane);
+}
+
 // acc += X Y^T over one 32-wide k block.  XEX / YEX: operand exact in bf16.
 template <bool XEX = false, bool YEX = false>
 __device__ __forceinline__ f32x4 fmma(f32x4 acc, const Frag<true>& x, const Frag<true>& y) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, y.hi, acc, 0, 0, 0);
-    if constexpr (!YEX) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.hi, y.lo, acc, 0, 0, 0);
-    if constexpr (!XEX) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.lo, y.hi, acc, 0, 0, 0);
+    acc = mfma_bf16(x.hi, y.hi, acc);
+    if constexpr (!YEX) acc = mfma_bf16(x.hi, y.lo, acc);
+    if constexpr (!XEX) acc = mfma_bf16(x.lo, y.hi, acc);
     return acc;
 }
 template <bool XEX = false, bool YEX = false>
@@ -748,7 +778,7 @@ __device__ __forceinline__ f32x4 fmma(f32x4 acc, const Frag<false>& x, const Fra
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.v[h][q], y.v[h][q], acc, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) acc = mfma_f32(x.v[h][q], y.v[h][q], acc);
     return acc;
 }
 

@@ -1,0 +1,356 @@
+// wkv7_grad.hip -- per-token input gradients of the WKV7 backward (gfx950).
+//
+// Reverse-mode of the per-token update (rwkv-mlx page, "Metal kernel
+// architecture", backward block: chunks in reverse, from checkpoints).  With
+// X_t = dL/dS_t (all later uses of S_t, including y_t) the gradient state
+// obeys X_{t-1} = X_t (diag w_t + b_t a_t^T) + dy_{t-1} r_{t-1}^T.  The scan
+// kernel (wkv7_scan.hip) walks that recurrence over the chunks and leaves the
+// gradient w.r.t. the state entering every chunk in dh_ckpt.  This kernel
+// takes it from there, one workgroup per (head, chunk), all chunks at once.
+// With the chunk matrices of wkv7_device.h, Ge' = Ge diag(gamma_last) for the
+// gradient Ge at the chunk's end and T = (I - Lab)^-1 (from the prepare
+// kernel), it recomputes from the checkpoint S0 -- never by dividing the
+// state by w --
+//     U   = T (Ahat S0^T + Lak V)                       u_t   = S_{t-1} a_t
+//     DSA = T^T (Btil Ge'^T + Mrb^T DY)                 dsa_t = X_t b_t
+// and then, with P1 = tril(DY U^T), P2 = tril(DY V^T), P3 = stril(DSA U^T),
+// P4 = stril(DSA V^T),
+//     dr = Gamma    * (DY S0  + P1 Btil   + P2 Ktil)
+//     da = Gamma_-1 * (DSA S0 + P3 Btil   + P4 Ktil)
+//     dk = Gamma^-1 * (V Ge'  + P4^T Ahat + P2^T Rhat)
+//     db = Gamma^-1 * (U Ge'  + P3^T Ahat + P1^T Rhat)
+// and dw from an identity that follows from the update rule: with
+// phi_t = w_t * dw_t and Gs = dL/dS0,
+//     phi_t = sum_i Gs[i][j] S0[i][j] - sum_{s<=t} a_s da_s
+//             + sum_{s<t} (k_s dk_s + b_s db_s - r_s dr_s),
+//     dw_t  = phi_t / w_t.
+// Every operand is staged once, in rows; products that need the other
+// orientation read it with the LDS transpose (frag_t).  The outputs are
+// computed transposed, (j, t), so that each lane stores four consecutive j.
+#include "wkv7_device.h"
+#include "wkv7_internal.h"
+
+namespace wkv7 {
+namespace {
+
+constexpr int GNT = 512;  // threads per workgroup (8 waves)
+constexpr int GNW = GNT / 64;
+
+// LDS plan (byte offsets).  Region Q holds T, Lak, Mrb, RHS_U, RHS_D until U
+// and DSA exist, then P1..P4 and the dw ingredients.
+template <bool SPLIT>
+struct GradSmem {
+    using F = Fmt<SPLIT>;
+    static constexpr int RM = F::bytes(C, D), SM = F::bytes(D, D), CM = F::bytes(C, C);
+    static constexpr int A = 0;                      // Ahat rows (t, j)
+    static constexpr int R = A + RM;                 // Rhat rows
+    static constexpr int Bm = R + RM;                // Btil rows
+    static constexpr int Km = Bm + RM;               // Ktil rows
+    static constexpr int V = Km + RM;                // v rows (t, i), exact: one plane
+    static constexpr int DY = V + C * F::ld(D) * (SPLIT ? 2 : 4);  // dy rows (t, i)
+    static constexpr int S0 = DY + RM;               // S0 rows (i, j)
+    static constexpr int Ge = S0 + SM;               // Ge' rows (i, j)
+    static constexpr int Gam = Ge + SM;              // fp32 gamma [t][j], stride LDG
+    static constexpr int glast = Gam + C * LDG * 4;
+    static constexpr int qp = glast + D * 4;         // fp32 16 x 64
+    static constexpr int red = qp + 16 * D * 4;      // fp32 8 x 64
+    static constexpr int Q = red + 8 * D * 4;
+    // region Q, phases 0-3
+    static constexpr int Tm = Q;                     // T rows (t, s)
+    static constexpr int Lak = Tm + CM;              // Lak rows (t, s)
+    static constexpr int Mrb = Lak + CM;             // Mrb rows (t, s)
+    static constexpr int RU = Mrb + CM;              // RHS_U rows (s, i)
+    static constexpr int RD = RU + RM;               // RHS_D rows (s, i)
+    static constexpr int QEND1 = RD + RM;
+    // region Q, phases 4-6
+    static constexpr int P1 = Q;                     // P1..P4 rows (t, s)
+    static constexpr int HH = P1 + 4 * CM;           // fp32 [t][j]: k dk + b db - r dr - a da
+    static constexpr int FA = HH + C * LDG * 4;      // fp32 [t][j]: a da
+    static constexpr int QEND2 = FA + C * LDG * 4;
+    static constexpr int U = QEND1 > QEND2 ? QEND1 : QEND2;   // U rows (t, i)
+    static constexpr int DSA = U + RM;               // DSA rows (t, i)
+    static constexpr int total = DSA + RM;
+    static_assert(total <= 160 * 1024, "gradient kernel LDS exceeds 160 KiB");
+};
+
+template <bool SPLIT>
+__device__ __forceinline__ Mat<SPLIT> exact_mat(char* smem, int off, int K) {
+    return Mat<SPLIT>{smem + off, Fmt<SPLIT>::ld(K), 0};   // one plane: lo reads see hi
+}
+
+template <typename InT, bool SPLIT>
+__global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using L = GradSmem<SPLIT>;
+    using M = Mat<SPLIT>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
+
+    int head, c;
+    block_map(blockIdx.x, p.NC, xcd != 0, head, c);
+    const int bb = head / p.H, hh = head % p.H;
+    const int HD = p.H * D;
+    const int64_t tstride = HD;
+    const int t0 = c * C;
+    const int Cc = min(C, p.T - t0);
+    const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
+    const int64_t hoff = (int64_t)head * D * D;
+    // the head's tokens: outputs past the sequence's end are dropped
+    const int64_t tok0 = (int64_t)bb * p.T * HD + (int64_t)hh * D;
+    const uint32_t span = (uint32_t)(((int64_t)(p.T - 1) * HD + D) * 4);
+
+    // ---- phase 0: loads, gamma and the scaled rows
+    RawChunk<GNT, InT> raw;
+    raw.load(static_cast<const InT*>(p.w), static_cast<const InT*>(p.a), static_cast<const InT*>(p.r),
+             static_cast<const InT*>(p.b), static_cast<const InT*>(p.k), base, tstride, Cc, tid);
+    RawCols<GNT, D, InT> rv;
+    RawCols<GNT, D, float> rdy;
+    rv.load(static_cast<const InT*>(p.v), base, tstride, Cc, 0, tid);
+    rdy.load(p.dy, base, tstride, Cc, 0, tid);
+    // state-sized inputs: thread holds row si = tid / 8, columns sj0 .. sj0 + 7
+    const int si = tid >> 3, sj0 = (tid & 7) * 8;
+    const float* s0g = p.ckpt + ((int64_t)head * p.NC + c) * D * D;
+    const float* geg = (c + 1 < p.NC) ? p.gbuf + ((int64_t)head * p.NC + c + 1) * D * D
+                                      : (p.dhT ? p.dhT + hoff : nullptr);
+    f32x4 s0v[2], gev[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        s0v[q] = *reinterpret_cast<const f32x4*>(s0g + si * D + sj0 + 4 * q);
+        gev[q] = geg ? *reinterpret_cast<const f32x4*>(geg + si * D + sj0 + 4 * q) : zero4();
+    }
+    // two entries of the chunk's T = (I - Lab)^-1: row tid / 16, columns 2 (tid % 16) ..
+    const float2 tv = *reinterpret_cast<const float2*>(p.inv + ((int64_t)head * p.NC + c) * C * C + tid * 2);
+    // partial sums of diag(Gs^T S0): thread column rj, rows 8 * rgrp .. + 7
+    {
+        const float* gsg = p.gbuf + ((int64_t)head * p.NC + c) * D * D;
+        const int rj = tid & 63, rgrp = tid >> 6;
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = rgrp * 8 + i;
+            acc = fmaf(gsg[row * D + rj], s0g[row * D + rj], acc);
+        }
+        reinterpret_cast<float*>(smem + L::red)[rgrp * 64 + rj] = acc;
+    }
+
+    const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
+    const M Bm = make_mat<SPLIT>(smem, L::Bm, C, D), Km = make_mat<SPLIT>(smem, L::Km, C, D);
+    const M Vm = exact_mat<SPLIT>(smem, L::V, D), DYm = make_mat<SPLIT>(smem, L::DY, C, D);
+    const M S0m = make_mat<SPLIT>(smem, L::S0, D, D), Gem = make_mat<SPLIT>(smem, L::Ge, D, D);
+    const M Tm = make_mat<SPLIT>(smem, L::Tm, C, C), Lak = make_mat<SPLIT>(smem, L::Lak, C, C);
+    const M Mrb = make_mat<SPLIT>(smem, L::Mrb, C, C);
+    const M RU = make_mat<SPLIT>(smem, L::RU, C, D), RD = make_mat<SPLIT>(smem, L::RD, C, D);
+    const M Um = make_mat<SPLIT>(smem, L::U, C, D), DSAm = make_mat<SPLIT>(smem, L::DSA, C, D);
+    auto Pm = [&](int m) { return make_mat<SPLIT>(smem, L::P1 + m * L::CM, C, C); };
+    float* gam = reinterpret_cast<float*>(smem + L::Gam);
+    float* glast = reinterpret_cast<float*>(smem + L::glast);
+    float* qp = reinterpret_cast<float*>(smem + L::qp);
+    float* red = reinterpret_cast<float*>(smem + L::red);
+    float* hh_ = reinterpret_cast<float*>(smem + L::HH);
+    float* fa_ = reinterpret_cast<float*>(smem + L::FA);
+
+    const PrepOut<SPLIT> po{A, R, Bm, Km, A, A, A, A, true, true, true, true, false, false, false, false,
+                            gam, glast};
+    chunk_prep<GNT, SPLIT>(raw, po, qp, tid);
+    rv.template store_rows<SPLIT, true>(Vm, tid);
+    rdy.template store_rows<SPLIT, false>(DYm, tid);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) put4(S0m, si, sj0 + 4 * q, s0v[q]);
+    put2(Tm, tid >> 4, 2 * (tid & 15), tv.x, tv.y);
+    lds_barrier();
+
+    // ---- phase 1: Lak = stril(Ahat Ktil^T), Mrb = tril(Rhat Btil^T) (rows); Ge' = Ge diag(gamma_last)
+    if (wave < 6) {
+        const int mat = wave / 3, tile = wave % 3;
+        const int ti = tile == 0 ? 0 : 1, tj = tile == 2 ? 1 : 0;
+        if (mat == 0) {
+            const f32x4 acc = mma<SPLIT, D>(zero4(), A, ti * 16, Km, tj * 16, lane);
+            store_rows<MASK_STRICT>(Lak, acc, ti * 16, tj * 16, lane);
+        } else {
+            const f32x4 acc = mma<SPLIT, D>(zero4(), R, ti * 16, Bm, tj * 16, lane);
+            store_rows<MASK_LOWER>(Mrb, acc, ti * 16, tj * 16, lane);
+        }
+    } else {
+        zero_block(wave == 6 ? Lak : Mrb, 0, 16, lane);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gev[q][e] *= glast[sj0 + 4 * q + e];
+        put4(Gem, si, sj0 + 4 * q, gev[q]);
+    }
+    lds_barrier();
+
+    // ---- phase 2: RHS_U[s][i] = sum_j S0[i][j] Ahat[s][j] + sum_u V[u][i] Lak[s][u]
+    //               RHS_D[s][i] = sum_j Ge'[i][j] Btil[s][j] + sum_u DY[u][i] Mrb[u][s]
+    // (accumulator element (i, s); rows s stored with four consecutive i per lane)
+    for (int job = wave; job < 16; job += GNW) {
+        const int which = job >> 3, ib = job & 3, sb = (job >> 2) & 1;
+        f32x4 acc;
+        if (which == 0) {
+            acc = fmma(zero4(), frag_n(S0m, 16 * ib, 0, lane), frag_n(A, 16 * sb, 0, lane));
+            acc = fmma(acc, frag_n(S0m, 16 * ib, 32, lane), frag_n(A, 16 * sb, 32, lane));
+            acc = fmma<true, false>(acc, frag_t_exact(Vm, 16 * ib, 0, lane), frag_n(Lak, 16 * sb, 0, lane));
+            put4(RU, 16 * sb + r16, 16 * ib + 4 * g4, acc);
+        } else {
+            acc = fmma(zero4(), frag_n(Gem, 16 * ib, 0, lane), frag_n(Bm, 16 * sb, 0, lane));
+            acc = fmma(acc, frag_n(Gem, 16 * ib, 32, lane), frag_n(Bm, 16 * sb, 32, lane));
+            acc = fmma(acc, frag_t(DYm, 16 * ib, 0, lane), frag_t(Mrb, 16 * sb, 0, lane));
+            put4(RD, 16 * sb + r16, 16 * ib + 4 * g4, acc);
+        }
+    }
+    lds_barrier();
+
+    // ---- phase 3: U[t][i] = sum_s T[t][s] RHS_U[s][i], DSA[t][i] = sum_s T[s][t] RHS_D[s][i]
+    for (int job = wave; job < 16; job += GNW) {
+        const int which = job >> 3, ib = job & 3, tb = (job >> 2) & 1;
+        if (which == 0) {
+            const f32x4 acc = fmma(zero4(), frag_t(RU, 16 * ib, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
+            put4(Um, 16 * tb + r16, 16 * ib + 4 * g4, acc);
+        } else {
+            const f32x4 acc = fmma(zero4(), frag_t(RD, 16 * ib, 0, lane), frag_t(Tm, 16 * tb, 0, lane));
+            put4(DSAm, 16 * tb + r16, 16 * ib + 4 * g4, acc);
+        }
+    }
+    lds_barrier();
+
+    // ---- phase 4: P1 = tril(DY U^T), P2 = tril(DY V^T), P3 = stril(DSA U^T), P4 = stril(DSA V^T),
+    // rows (t, s); accumulator element (s, t)
+    for (int job = wave; job < 16; job += GNW) {
+        const int mat = job >> 2, tile = job & 3;
+        if (tile == 3) {   // s in 16..31, t in 0..15: zero
+            put4(Pm(mat), r16, 16 + 4 * g4, zero4());
+            continue;
+        }
+        const int sb = tile == 2 ? 1 : 0, tb = tile == 0 ? 0 : 1;
+        const M X = mat < 2 ? DYm : DSAm;
+        f32x4 acc;
+        if (mat & 1) {
+            acc = fmma<true, false>(zero4(), frag_n(Vm, 16 * sb, 0, lane), frag_n(X, 16 * tb, 0, lane));
+            acc = fmma<true, false>(acc, frag_n(Vm, 16 * sb, 32, lane), frag_n(X, 16 * tb, 32, lane));
+        } else {
+            acc = fmma(zero4(), frag_n(Um, 16 * sb, 0, lane), frag_n(X, 16 * tb, 0, lane));
+            acc = fmma(acc, frag_n(Um, 16 * sb, 32, lane), frag_n(X, 16 * tb, 32, lane));
+        }
+        const int t = 16 * tb + r16, s0_ = 16 * sb + 4 * g4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int s = s0_ + q;
+            if (mat < 2 ? s > t : s >= t) acc[q] = 0.f;
+        }
+        put4(Pm(mat), t, s0_, acc);
+    }
+    lds_barrier();
+
+    // ---- phase 5: outputs, accumulator element (j, t); one (j block, t block) per wave
+    {
+        const Rsrc rdr = make_rsrc(p.dr + tok0, span), rda = make_rsrc(p.da + tok0, span);
+        const Rsrc rdk = make_rsrc(p.dk + tok0, span), rdb = make_rsrc(p.db + tok0, span);
+        const int jb = wave & 3, tb = wave >> 2;
+        const M P1 = Pm(0), P2 = Pm(1), P3 = Pm(2), P4 = Pm(3);
+        f32x4 aR = fmma(zero4(), frag_t(S0m, 16 * jb, 0, lane), frag_n(DYm, 16 * tb, 0, lane));
+        aR = fmma(aR, frag_t(S0m, 16 * jb, 32, lane), frag_n(DYm, 16 * tb, 32, lane));
+        aR = fmma(aR, frag_t(Bm, 16 * jb, 0, lane), frag_n(P1, 16 * tb, 0, lane));
+        aR = fmma(aR, frag_t(Km, 16 * jb, 0, lane), frag_n(P2, 16 * tb, 0, lane));
+        f32x4 aA = fmma(zero4(), frag_t(S0m, 16 * jb, 0, lane), frag_n(DSAm, 16 * tb, 0, lane));
+        aA = fmma(aA, frag_t(S0m, 16 * jb, 32, lane), frag_n(DSAm, 16 * tb, 32, lane));
+        aA = fmma(aA, frag_t(Bm, 16 * jb, 0, lane), frag_n(P3, 16 * tb, 0, lane));
+        aA = fmma(aA, frag_t(Km, 16 * jb, 0, lane), frag_n(P4, 16 * tb, 0, lane));
+        f32x4 aK = fmma<false, true>(zero4(), frag_t(Gem, 16 * jb, 0, lane), frag_n(Vm, 16 * tb, 0, lane));
+        aK = fmma<false, true>(aK, frag_t(Gem, 16 * jb, 32, lane), frag_n(Vm, 16 * tb, 32, lane));
+        aK = fmma(aK, frag_t(A, 16 * jb, 0, lane), frag_t(P4, 16 * tb, 0, lane));
+        aK = fmma(aK, frag_t(R, 16 * jb, 0, lane), frag_t(P2, 16 * tb, 0, lane));
+        f32x4 aB = fmma(zero4(), frag_t(Gem, 16 * jb, 0, lane), frag_n(Um, 16 * tb, 0, lane));
+        aB = fmma(aB, frag_t(Gem, 16 * jb, 32, lane), frag_n(Um, 16 * tb, 32, lane));
+        aB = fmma(aB, frag_t(A, 16 * jb, 0, lane), frag_t(P3, 16 * tb, 0, lane));
+        aB = fmma(aB, frag_t(R, 16 * jb, 0, lane), frag_t(P1, 16 * tb, 0, lane));
+
+        const int t = 16 * tb + r16, j0 = 16 * jb + 4 * g4;
+        const f32x4 g = *reinterpret_cast<const f32x4*>(gam + t * LDG + j0);
+        const f32x4 gp = t > 0 ? *reinterpret_cast<const f32x4*>(gam + (t - 1) * LDG + j0) : f32x4{1.f, 1.f, 1.f, 1.f};
+        f32x4 ig;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ig[q] = rcp(g[q]);
+        const int voff = (t * HD + j0) * 4, soff_ = t0 * HD * 4;
+        bstore4(aR * g, rdr, voff, soff_);
+        bstore4(aA * gp, rda, voff, soff_);
+        bstore4(aK * ig, rdk, voff, soff_);
+        bstore4(aB * ig, rdb, voff, soff_);
+        // k dk = Ktil aK, b db = Btil aB, r dr = Rhat aR, a da = Ahat aA
+        const f32x4 fa = get4(A, t, j0) * aA;
+        const f32x4 ev = get4(Km, t, j0) * aK + get4(Bm, t, j0) * aB - get4(R, t, j0) * aR;
+        *reinterpret_cast<f32x4*>(hh_ + t * LDG + j0) = ev - fa;
+        *reinterpret_cast<f32x4*>(fa_ + t * LDG + j0) = fa;
+    }
+    lds_barrier();
+
+    // ---- phase 6: dw: phi_t = diag(Gs^T S0) - sum_{s<=t} a da + sum_{s<t} (k dk + b db - r dr),
+    //      dw_t = phi_t / w_t.  Thread (jp, q) scans tokens TPG q .. of columns 2jp, 2jp+1.
+    {
+        constexpr int TPG = RawChunk<GNT, InT>::TPG, NG = RawChunk<GNT, InT>::NG;
+        const int jp = tid & 31, q = tid >> 5, j0 = 2 * jp;
+        float2 hx[TPG], fx[TPG];
+        float2 tot = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int tt = 0; tt < TPG; ++tt) {
+            const int t = q * TPG + tt;
+            hx[tt] = *reinterpret_cast<const float2*>(hh_ + t * LDG + j0);
+            fx[tt] = *reinterpret_cast<const float2*>(fa_ + t * LDG + j0);
+            tot.x += hx[tt].x;
+            tot.y += hx[tt].y;
+        }
+        qp[q * 64 + j0] = tot.x;
+        qp[q * 64 + j0 + 1] = tot.y;
+        lds_barrier();
+        float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int g = 0; g < GNW; ++g) {
+            acc.x += red[g * 64 + j0];
+            acc.y += red[g * 64 + j0 + 1];
+        }
+#pragma unroll
+        for (int q2 = 0; q2 < NG; ++q2) {
+            if (q2 < q) {
+                acc.x += qp[q2 * 64 + j0];
+                acc.y += qp[q2 * 64 + j0 + 1];
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPG; ++tt) {
+            const int t = q * TPG + tt;
+            if (t < Cc) {
+                const float2 wv = Pair<InT>::f(raw.w[tt]);
+                *reinterpret_cast<float2*>(p.dw + base + t * tstride + j0) =
+                    make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y));
+            }
+            acc.x += hx[tt].x;
+            acc.y += hx[tt].y;
+        }
+    }
+}
+
+template <typename InT, bool SPLIT>
+hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
+    using L = GradSmem<SPLIT>;
+    auto kern = grad_kernel<InT, SPLIT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int heads = a.B * a.H;
+    const int xcd = (heads % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(kern, dim3(heads * a.NC), dim3(GNT), L::total, s, a, xcd);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, hipStream_t s) {
+    if (bf16) return launch_typed<uint16_t, true>(a, s);
+    return launch_typed<float, false>(a, s);
+}
+
+}  // namespace wkv7

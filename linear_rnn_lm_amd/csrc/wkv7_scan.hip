@@ -305,7 +305,7 @@ struct XCopy {
         for (int u = 0; u < PER; ++u) {
             const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * EPP;
             v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 r, (t * HD + e0) * (int)sizeof(XT), c * C * HD * (int)sizeof(XT), 0));
+                                                 r, (t * HD + e0 + c * C * HD) * (int)sizeof(XT), 0, 0));
         }
     }
     // rows (t, i) of an operand matrix: exact bf16 (v) or split (dy)
@@ -332,20 +332,6 @@ __device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD
         const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * 4;
         bstore4(*reinterpret_cast<const f32x4*>(ob + t * LDO + e0), r, (t * HD + e0) * 4, c * C * HD * 4);
     }
-}
-
-// LDS transpose read of exact bf16 values (hi plane only), see frag_t.
-__device__ __forceinline__ Frag<true> frag_t_exact(Mat<true> X, int col0, int c0, int lane) {
-    const int g = lane >> 4, l16 = lane & 15;
-    const __bf16* p = reinterpret_cast<const __bf16*>(X.p) + (c0 + 4 * g + (l16 >> 2)) * X.ld + col0 + 4 * (l16 & 3);
-    Frag<true> f;
-    f.hi = cat8(as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p))),
-                as_bf16x4(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * X.ld))));
-    f.lo = f.hi;
-    return f;
-}
-__device__ __forceinline__ Frag<false> frag_t_exact(Mat<false> X, int col0, int c0, int lane) {
-    return frag_t(X, col0, c0, lane);
 }
 
 // BWD = false: forward over v (InT), S from h0 -> y, checkpoints, hT.
