@@ -78,59 +78,166 @@ __device__ __forceinline__ Mat<SPLIT> exact_mat(char* smem, int off, int K) {
     return Mat<SPLIT>{smem + off, Fmt<SPLIT>::ld(K), 0};   // one plane: lo reads see hi
 }
 
+// Where one chunk's inputs live.  `on == false` (no next chunk) gives every
+// buffer resource size 0, so the loads return zeros without touching memory.
+struct ChunkSrc {
+    int64_t tok0;   // element offset of the head's token 0
+    int64_t cs;     // element offset of the chunk's D x D state blocks
+    int64_t ci;     // element offset of the chunk's C x C inverse
+    int t0, cc;     // first token, tokens in the chunk
+    bool on, has_ge;
+    const float* ge;   // gradient at the chunk's end: next checkpoint's, dhT, or none
+
+    __device__ __forceinline__ ChunkSrc(const BwdArgs& p, int head, int c, bool on_) {
+        const int bb = head / p.H, hh = head % p.H;
+        const int HD = p.H * D;
+        tok0 = (int64_t)bb * p.T * HD + (int64_t)hh * D;
+        cs = ((int64_t)head * p.NC + c) * D * D;
+        ci = ((int64_t)head * p.NC + c) * C * C;
+        t0 = c * C;
+        cc = min(C, p.T - t0);
+        on = on_;
+        has_ge = c + 1 < p.NC || p.dhT != nullptr;
+        ge = (c + 1 < p.NC) ? p.gbuf + cs + D * D : (p.dhT ? p.dhT + (int64_t)head * D * D : p.gbuf);
+    }
+};
+
+// Everything one chunk reads from global memory, held in registers so that
+// the next chunk's loads are in flight while the current chunk computes.  The
+// loads are issued in six parts, one per compute phase, so that no wave
+// stalls on a full memory queue; buffer loads without branches keep the
+// wave's count of outstanding loads exact.
+template <typename InT>
+struct GradIn {
+    using W = typename Pair<InT>::T;
+    static constexpr int ES = sizeof(InT);
+    RawChunk<GNT, InT> raw;          // w, a, r, b, k
+    RawCols<GNT, D, InT> rv;         // v
+    RawCols<GNT, D, float> rdy;      // dy
+    f32x4 s0v[2], gsv[2], gev[2];    // S0, Gs (gradient entering), Ge (gradient at the end): row si, 8 columns
+    float2 tv;                       // two entries of T = (I - Lab)^-1
+
+    template <typename X>
+    static __device__ __forceinline__ X ld(Rsrc r, int off) {
+        if constexpr (sizeof(X) == 4) {
+            return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        } else {
+            return __builtin_bit_cast(X, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        }
+    }
+    static __device__ __forceinline__ f32x4 ld4(Rsrc r, int off) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+    static __device__ __forceinline__ Rsrc tok(const void* base, const BwdArgs& p, const ChunkSrc& s, int es) {
+        const uint32_t span = s.on ? (uint32_t)(((int64_t)(p.T - 1) * p.H * D + D) * es) : 0u;
+        return make_rsrc(static_cast<const char*>(base) + s.tok0 * es, span);
+    }
+    // w, a, r, b, k: columns 2 jp, 2 jp + 1 of tokens q TPG + tt
+    __device__ __forceinline__ void raw_part(W* dst, const void* src, const BwdArgs& p, const ChunkSrc& s, int tid) {
+        constexpr int TPG = RawChunk<GNT, InT>::TPG;
+        const Rsrc r = tok(src, p, s, ES);
+        const int jp = tid & 31, q = tid >> 5, HD = p.H * D;
+#pragma unroll
+        for (int tt = 0; tt < TPG; ++tt) dst[tt] = ld<W>(r, ((s.t0 + q * TPG + tt) * HD + 2 * jp) * ES);
+    }
+    template <int PART>
+    __device__ __forceinline__ void issue(const BwdArgs& p, const ChunkSrc& s, int tid) {
+        using RC = RawCols<GNT, D, InT>;
+        const int si = tid >> 3, sj0 = (tid & 7) * 8, soff = (si * D + sj0) * 4;
+        const uint32_t sbytes = s.on ? D * D * 4 : 0u;
+        if constexpr (PART == 0) {
+            raw.cc = rv.cc = rdy.cc = s.cc;
+            raw_part(raw.w, p.w, p, s, tid);
+            raw_part(raw.a, p.a, p, s, tid);
+            raw_part(raw.r, p.r, p, s, tid);
+        } else if constexpr (PART == 1) {
+            raw_part(raw.b, p.b, p, s, tid);
+            raw_part(raw.k, p.k, p, s, tid);
+            const Rsrc r = tok(p.v, p, s, ES);
+            const int ip = tid % RC::PAIRS, t1 = tid / RC::PAIRS, HD = p.H * D;
+#pragma unroll
+            for (int u = 0; u < RC::PER; ++u) rv.v[u] = ld<W>(r, ((s.t0 + t1 + u * RC::TSTEP) * HD + 2 * ip) * ES);
+        } else if constexpr (PART == 2) {
+            const Rsrc r = tok(p.dy, p, s, 4);
+            const int ip = tid % RC::PAIRS, t1 = tid / RC::PAIRS, HD = p.H * D;
+#pragma unroll
+            for (int u = 0; u < RC::PER; ++u) rdy.v[u] = ld<float2>(r, ((s.t0 + t1 + u * RC::TSTEP) * HD + 2 * ip) * 4);
+            tv = ld<float2>(make_rsrc(p.inv + s.ci, s.on ? C * C * 4 : 0u), tid * 8);
+        } else if constexpr (PART == 3) {
+            const Rsrc r = make_rsrc(p.ckpt + s.cs, sbytes);
+            s0v[0] = ld4(r, soff);
+            s0v[1] = ld4(r, soff + 16);
+        } else if constexpr (PART == 4) {
+            const Rsrc r = make_rsrc(p.gbuf + s.cs, sbytes);
+            gsv[0] = ld4(r, soff);
+            gsv[1] = ld4(r, soff + 16);
+        } else {
+            const Rsrc r = make_rsrc(s.ge, s.has_ge ? sbytes : 0u);
+            gev[0] = ld4(r, soff);
+            gev[1] = ld4(r, soff + 16);
+        }
+    }
+    __device__ __forceinline__ void issue_all(const BwdArgs& p, const ChunkSrc& s, int tid) {
+        issue<0>(p, s, tid);
+        issue<1>(p, s, tid);
+        issue<2>(p, s, tid);
+        issue<3>(p, s, tid);
+        issue<4>(p, s, tid);
+        issue<5>(p, s, tid);
+    }
+};
+
+// Persistent: each workgroup takes chunks blockIdx.x, + gridDim.x, ... of the
+// total; while it works on one chunk the next chunk's inputs are loading.
 template <typename InT, bool SPLIT>
-__global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
+__global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using L = GradSmem<SPLIT>;
     using M = Mat<SPLIT>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g4 = lane >> 4;
-
-    int head, c;
-    block_map(blockIdx.x, p.NC, xcd != 0, head, c);
-    const int bb = head / p.H, hh = head % p.H;
     const int HD = p.H * D;
     const int64_t tstride = HD;
+    const uint32_t span = (uint32_t)(((int64_t)(p.T - 1) * HD + D) * 4);
+    // state-sized inputs: thread holds row si = tid / 8, columns sj0 .. sj0 + 7
+    const int si = tid >> 3, sj0 = (tid & 7) * 8;
+
+    int idx = blockIdx.x, head, c;
+    block_map(idx, p.NC, xcd != 0, head, c);
+    GradIn<InT> cur, nxt;
+    cur.issue_all(p, ChunkSrc(p, head, c, true), tid);
+
+  for (;;) {
+    const int nidx = idx + (int)gridDim.x;
+    const bool more = nidx < total;
+    int nhead, ncc;
+    block_map(more ? nidx : idx, p.NC, xcd != 0, nhead, ncc);
+    const ChunkSrc nsrc(p, nhead, ncc, more);
+    nxt.template issue<0>(p, nsrc, tid);
+    const int bb = head / p.H, hh = head % p.H;
     const int t0 = c * C;
     const int Cc = min(C, p.T - t0);
     const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
-    const int64_t hoff = (int64_t)head * D * D;
     // the head's tokens: outputs past the sequence's end are dropped
     const int64_t tok0 = (int64_t)bb * p.T * HD + (int64_t)hh * D;
-    const uint32_t span = (uint32_t)(((int64_t)(p.T - 1) * HD + D) * 4);
 
-    // ---- phase 0: loads, gamma and the scaled rows
-    RawChunk<GNT, InT> raw;
-    raw.load(static_cast<const InT*>(p.w), static_cast<const InT*>(p.a), static_cast<const InT*>(p.r),
-             static_cast<const InT*>(p.b), static_cast<const InT*>(p.k), base, tstride, Cc, tid);
-    RawCols<GNT, D, InT> rv;
-    RawCols<GNT, D, float> rdy;
-    rv.load(static_cast<const InT*>(p.v), base, tstride, Cc, 0, tid);
-    rdy.load(p.dy, base, tstride, Cc, 0, tid);
-    // state-sized inputs: thread holds row si = tid / 8, columns sj0 .. sj0 + 7
-    const int si = tid >> 3, sj0 = (tid & 7) * 8;
-    const float* s0g = p.ckpt + ((int64_t)head * p.NC + c) * D * D;
-    const float* geg = (c + 1 < p.NC) ? p.gbuf + ((int64_t)head * p.NC + c + 1) * D * D
-                                      : (p.dhT ? p.dhT + hoff : nullptr);
-    f32x4 s0v[2], gev[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        s0v[q] = *reinterpret_cast<const f32x4*>(s0g + si * D + sj0 + 4 * q);
-        gev[q] = geg ? *reinterpret_cast<const f32x4*>(geg + si * D + sj0 + 4 * q) : zero4();
-    }
-    // two entries of the chunk's T = (I - Lab)^-1: row tid / 16, columns 2 (tid % 16) ..
-    const float2 tv = *reinterpret_cast<const float2*>(p.inv + ((int64_t)head * p.NC + c) * C * C + tid * 2);
-    // partial sums of diag(Gs^T S0): thread column rj, rows 8 * rgrp .. + 7
+    // ---- phase 0: gamma and the scaled rows; partial sums of diag(Gs^T S0)
     {
-        const float* gsg = p.gbuf + ((int64_t)head * p.NC + c) * D * D;
-        const int rj = tid & 63, rgrp = tid >> 6;
-        float acc = 0.f;
+        // this wave's 8 rows: lanes with equal tid % 8 hold the same 8 columns
+        f32x4 d0 = cur.gsv[0] * cur.s0v[0], d1 = cur.gsv[1] * cur.s0v[1];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = rgrp * 8 + i;
-            acc = fmaf(gsg[row * D + rj], s0g[row * D + rj], acc);
+        for (int m = 8; m < 64; m <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d0[e] += __shfl_xor(d0[e], m);
+                d1[e] += __shfl_xor(d1[e], m);
+            }
         }
-        reinterpret_cast<float*>(smem + L::red)[rgrp * 64 + rj] = acc;
+        if (lane < 8) {
+            float* red = reinterpret_cast<float*>(smem + L::red) + wave * 64 + sj0;
+            *reinterpret_cast<f32x4*>(red) = d0;
+            *reinterpret_cast<f32x4*>(red + 4) = d1;
+        }
     }
 
     const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
@@ -151,14 +258,15 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
 
     const PrepOut<SPLIT> po{A, R, Bm, Km, A, A, A, A, true, true, true, true, false, false, false, false,
                             gam, glast};
-    chunk_prep<GNT, SPLIT>(raw, po, qp, tid);
-    rv.template store_rows<SPLIT, true>(Vm, tid);
-    rdy.template store_rows<SPLIT, false>(DYm, tid);
+    chunk_prep<GNT, SPLIT>(cur.raw, po, qp, tid);
+    cur.rv.template store_rows<SPLIT, true>(Vm, tid);
+    cur.rdy.template store_rows<SPLIT, false>(DYm, tid);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) put4(S0m, si, sj0 + 4 * q, s0v[q]);
-    put2(Tm, tid >> 4, 2 * (tid & 15), tv.x, tv.y);
+    for (int q = 0; q < 2; ++q) put4(S0m, si, sj0 + 4 * q, cur.s0v[q]);
+    put2(Tm, tid >> 4, 2 * (tid & 15), cur.tv.x, cur.tv.y);
     lds_barrier();
 
+    nxt.template issue<1>(p, nsrc, tid);
     // ---- phase 1: Lak = stril(Ahat Ktil^T), Mrb = tril(Rhat Btil^T) (rows); Ge' = Ge diag(gamma_last)
     if (wave < 6) {
         const int mat = wave / 3, tile = wave % 3;
@@ -176,11 +284,12 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gev[q][e] *= glast[sj0 + 4 * q + e];
-        put4(Gem, si, sj0 + 4 * q, gev[q]);
+        for (int e = 0; e < 4; ++e) cur.gev[q][e] *= glast[sj0 + 4 * q + e];
+        put4(Gem, si, sj0 + 4 * q, cur.gev[q]);
     }
     lds_barrier();
 
+    nxt.template issue<2>(p, nsrc, tid);
     // ---- phase 2: RHS_U[s][i] = sum_j S0[i][j] Ahat[s][j] + sum_u V[u][i] Lak[s][u]
     //               RHS_D[s][i] = sum_j Ge'[i][j] Btil[s][j] + sum_u DY[u][i] Mrb[u][s]
     // (accumulator element (i, s); rows s stored with four consecutive i per lane)
@@ -201,6 +310,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
     }
     lds_barrier();
 
+    nxt.template issue<3>(p, nsrc, tid);
     // ---- phase 3: U[t][i] = sum_s T[t][s] RHS_U[s][i], DSA[t][i] = sum_s T[s][t] RHS_D[s][i]
     for (int job = wave; job < 16; job += GNW) {
         const int which = job >> 3, ib = job & 3, tb = (job >> 2) & 1;
@@ -214,6 +324,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
     }
     lds_barrier();
 
+    nxt.template issue<4>(p, nsrc, tid);
     // ---- phase 4: P1 = tril(DY U^T), P2 = tril(DY V^T), P3 = stril(DSA U^T), P4 = stril(DSA V^T),
     // rows (t, s); accumulator element (s, t)
     for (int job = wave; job < 16; job += GNW) {
@@ -242,6 +353,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
     }
     lds_barrier();
 
+    nxt.template issue<5>(p, nsrc, tid);
     // ---- phase 5: outputs, accumulator element (j, t); one (j block, t block) per wave
     {
         const Rsrc rdr = make_rsrc(p.dr + tok0, span), rda = make_rsrc(p.da + tok0, span);
@@ -319,7 +431,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
         for (int tt = 0; tt < TPG; ++tt) {
             const int t = q * TPG + tt;
             if (t < Cc) {
-                const float2 wv = Pair<InT>::f(raw.w[tt]);
+                const float2 wv = Pair<InT>::f(cur.raw.w[tt]);
                 *reinterpret_cast<float2*>(p.dw + base + t * tstride + j0) =
                     make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y));
             }
@@ -327,6 +439,13 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd) {
             acc.y += hx[tt].y;
         }
     }
+    if (!more) break;
+    cur = nxt;
+    idx = nidx;
+    head = nhead;
+    c = ncc;
+    lds_barrier();   // this chunk's last LDS reads before the next chunk's writes
+  }
 }
 
 template <typename InT, bool SPLIT>
@@ -340,9 +459,20 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
+    // one workgroup per CU (the LDS plan takes most of a CU's 160 KiB)
+    static int n_cu = 0;
+    if (n_cu == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
     const int heads = a.B * a.H;
+    const int total = heads * a.NC;
     const int xcd = (heads % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3(heads * a.NC), dim3(GNT), L::total, s, a, xcd);
+    int grid = total < n_cu ? total : n_cu;
+    if (xcd && grid > 8) grid -= grid % 8;   // a workgroup's chunks stay on one XCD
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(GNT), L::total, s, a, xcd, total);
     return hipGetLastError();
 }
 
