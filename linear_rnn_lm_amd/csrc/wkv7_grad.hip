@@ -293,63 +293,63 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     // ---- phase 2: RHS_U[s][i] = sum_j S0[i][j] Ahat[s][j] + sum_u V[u][i] Lak[s][u]
     //               RHS_D[s][i] = sum_j Ge'[i][j] Btil[s][j] + sum_u DY[u][i] Mrb[u][s]
     // (accumulator element (i, s); rows s stored with four consecutive i per lane)
-    for (int job = wave; job < 16; job += GNW) {
-        const int which = job >> 3, ib = job & 3, sb = (job >> 2) & 1;
-        f32x4 acc;
-        if (which == 0) {
-            acc = fmma(zero4(), frag_n(S0m, 16 * ib, 0, lane), frag_n(A, 16 * sb, 0, lane));
-            acc = fmma(acc, frag_n(S0m, 16 * ib, 32, lane), frag_n(A, 16 * sb, 32, lane));
-            acc = fmma<true, false>(acc, frag_t_exact(Vm, 16 * ib, 0, lane), frag_n(Lak, 16 * sb, 0, lane));
-            put4(RU, 16 * sb + r16, 16 * ib + 4 * g4, acc);
-        } else {
-            acc = fmma(zero4(), frag_n(Gem, 16 * ib, 0, lane), frag_n(Bm, 16 * sb, 0, lane));
-            acc = fmma(acc, frag_n(Gem, 16 * ib, 32, lane), frag_n(Bm, 16 * sb, 32, lane));
-            acc = fmma(acc, frag_t(DYm, 16 * ib, 0, lane), frag_t(Mrb, 16 * sb, 0, lane));
-            put4(RD, 16 * sb + r16, 16 * ib + 4 * g4, acc);
-        }
+    {   // wave: tile (ib, sb) of both; the two chains interleave
+        const int ib = wave & 3, sb = wave >> 2;
+        f32x4 au = fmma(zero4(), frag_n(S0m, 16 * ib, 0, lane), frag_n(A, 16 * sb, 0, lane));
+        f32x4 ad = fmma(zero4(), frag_n(Gem, 16 * ib, 0, lane), frag_n(Bm, 16 * sb, 0, lane));
+        au = fmma(au, frag_n(S0m, 16 * ib, 32, lane), frag_n(A, 16 * sb, 32, lane));
+        ad = fmma(ad, frag_n(Gem, 16 * ib, 32, lane), frag_n(Bm, 16 * sb, 32, lane));
+        au = fmma<true, false>(au, frag_t_exact(Vm, 16 * ib, 0, lane), frag_n(Lak, 16 * sb, 0, lane));
+        ad = fmma(ad, frag_t(DYm, 16 * ib, 0, lane), frag_t(Mrb, 16 * sb, 0, lane));
+        put4(RU, 16 * sb + r16, 16 * ib + 4 * g4, au);
+        put4(RD, 16 * sb + r16, 16 * ib + 4 * g4, ad);
     }
     lds_barrier();
 
     nxt.template issue<3>(p, nsrc, tid);
     // ---- phase 3: U[t][i] = sum_s T[t][s] RHS_U[s][i], DSA[t][i] = sum_s T[s][t] RHS_D[s][i]
-    for (int job = wave; job < 16; job += GNW) {
-        const int which = job >> 3, ib = job & 3, tb = (job >> 2) & 1;
-        if (which == 0) {
-            const f32x4 acc = fmma(zero4(), frag_t(RU, 16 * ib, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
-            put4(Um, 16 * tb + r16, 16 * ib + 4 * g4, acc);
-        } else {
-            const f32x4 acc = fmma(zero4(), frag_t(RD, 16 * ib, 0, lane), frag_t(Tm, 16 * tb, 0, lane));
-            put4(DSAm, 16 * tb + r16, 16 * ib + 4 * g4, acc);
-        }
+    {
+        const int ib = wave & 3, tb = wave >> 2;
+        const f32x4 au = fmma(zero4(), frag_t(RU, 16 * ib, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
+        const f32x4 ad = fmma(zero4(), frag_t(RD, 16 * ib, 0, lane), frag_t(Tm, 16 * tb, 0, lane));
+        put4(Um, 16 * tb + r16, 16 * ib + 4 * g4, au);
+        put4(DSAm, 16 * tb + r16, 16 * ib + 4 * g4, ad);
     }
     lds_barrier();
 
     nxt.template issue<4>(p, nsrc, tid);
     // ---- phase 4: P1 = tril(DY U^T), P2 = tril(DY V^T), P3 = stril(DSA U^T), P4 = stril(DSA V^T),
     // rows (t, s); accumulator element (s, t)
-    for (int job = wave; job < 16; job += GNW) {
-        const int mat = job >> 2, tile = job & 3;
-        if (tile == 3) {   // s in 16..31, t in 0..15: zero
-            put4(Pm(mat), r16, 16 + 4 * g4, zero4());
-            continue;
-        }
-        const int sb = tile == 2 ? 1 : 0, tb = tile == 0 ? 0 : 1;
-        const M X = mat < 2 ? DYm : DSAm;
-        f32x4 acc;
-        if (mat & 1) {
-            acc = fmma<true, false>(zero4(), frag_n(Vm, 16 * sb, 0, lane), frag_n(X, 16 * tb, 0, lane));
-            acc = fmma<true, false>(acc, frag_n(Vm, 16 * sb, 32, lane), frag_n(X, 16 * tb, 32, lane));
+    {   // wave: tile (wave % 4) of P(wave / 4) and P(wave / 4 + 2); tile 3 (s >= 16 > t) is zero
+        const int tile = wave & 3, m0 = wave >> 2;
+        if (tile == 3) {
+            put4(Pm(m0), r16, 16 + 4 * g4, zero4());
+            put4(Pm(m0 + 2), r16, 16 + 4 * g4, zero4());
         } else {
-            acc = fmma(zero4(), frag_n(Um, 16 * sb, 0, lane), frag_n(X, 16 * tb, 0, lane));
-            acc = fmma(acc, frag_n(Um, 16 * sb, 32, lane), frag_n(X, 16 * tb, 32, lane));
-        }
-        const int t = 16 * tb + r16, s0_ = 16 * sb + 4 * g4;
+            const int sb = tile == 2 ? 1 : 0, tb = tile == 0 ? 0 : 1;
+            // m0 = 0: P1 (DY U^T), P3 (DSA U^T); m0 = 1: P2 (DY V^T), P4 (DSA V^T)
+            f32x4 a0, a1;
+            if (m0 == 0) {
+                a0 = fmma(zero4(), frag_n(Um, 16 * sb, 0, lane), frag_n(DYm, 16 * tb, 0, lane));
+                a1 = fmma(zero4(), frag_n(Um, 16 * sb, 0, lane), frag_n(DSAm, 16 * tb, 0, lane));
+                a0 = fmma(a0, frag_n(Um, 16 * sb, 32, lane), frag_n(DYm, 16 * tb, 32, lane));
+                a1 = fmma(a1, frag_n(Um, 16 * sb, 32, lane), frag_n(DSAm, 16 * tb, 32, lane));
+            } else {
+                a0 = fmma<true, false>(zero4(), frag_n(Vm, 16 * sb, 0, lane), frag_n(DYm, 16 * tb, 0, lane));
+                a1 = fmma<true, false>(zero4(), frag_n(Vm, 16 * sb, 0, lane), frag_n(DSAm, 16 * tb, 0, lane));
+                a0 = fmma<true, false>(a0, frag_n(Vm, 16 * sb, 32, lane), frag_n(DYm, 16 * tb, 32, lane));
+                a1 = fmma<true, false>(a1, frag_n(Vm, 16 * sb, 32, lane), frag_n(DSAm, 16 * tb, 32, lane));
+            }
+            const int t = 16 * tb + r16, s0_ = 16 * sb + 4 * g4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int s = s0_ + q;
-            if (mat < 2 ? s > t : s >= t) acc[q] = 0.f;
+            for (int q = 0; q < 4; ++q) {
+                const int s = s0_ + q;
+                if (s > t) a0[q] = 0.f;    // P1, P2: s <= t
+                if (s >= t) a1[q] = 0.f;   // P3, P4: s < t
+            }
+            put4(Pm(m0), t, s0_, a0);
+            put4(Pm(m0 + 2), t, s0_, a1);
         }
-        put4(Pm(mat), t, s0_, acc);
     }
     lds_barrier();
 

@@ -30,6 +30,11 @@ SMALL = [
     (8, 40, 16, BF16, True, True),
     (16, 40, 16, BF16, False, True),
     (1, 257, 8, F32, True, True),
+    # more chunks than CUs: the gradient kernel's workgroups take several
+    # chunks each (uneven counts), on the XCD-grouped (40 heads) and the
+    # plain (300 heads) block order
+    (3, 300, 40, BF16, True, True),
+    (1, 200, 300, F32, False, True),
 ]
 
 
