@@ -194,7 +194,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using L = GradSmem<SPLIT>;
     using M = Mat<SPLIT>;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int r16 = lane & 15, g4 = lane >> 4;
     const int HD = p.H * D;
     const int64_t tstride = HD;
@@ -354,45 +354,95 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     lds_barrier();
 
     nxt.template issue<5>(p, nsrc, tid);
-    // ---- phase 5: outputs, accumulator element (j, t); one (j block, t block) per wave
+    // ---- phase 5: outputs, accumulator element (j, t).  Waves 0-3 form dr and da, waves 4-7 dk and
+    // db; each wave one t block and two j blocks, so the t-side operands are read once for both.
+    // The dw ingredients: waves 4-7 store k dk + b db to hh_, waves 0-3 store a da to fa_ and, after
+    // the next barrier, add -r dr - a da to hh_.
     {
-        const Rsrc rdr = make_rsrc(p.dr + tok0, span), rda = make_rsrc(p.da + tok0, span);
-        const Rsrc rdk = make_rsrc(p.dk + tok0, span), rdb = make_rsrc(p.db + tok0, span);
-        const int jb = wave & 3, tb = wave >> 2;
+        using Fr = Frag<SPLIT>;
+        const int pr = wave >> 2, tb = (wave >> 1) & 1, jb0 = (wave & 1) * 2;
+        const int t = 16 * tb + r16;
         const M P1 = Pm(0), P2 = Pm(1), P3 = Pm(2), P4 = Pm(3);
-        f32x4 aR = fmma(zero4(), frag_t(S0m, 16 * jb, 0, lane), frag_n(DYm, 16 * tb, 0, lane));
-        aR = fmma(aR, frag_t(S0m, 16 * jb, 32, lane), frag_n(DYm, 16 * tb, 32, lane));
-        aR = fmma(aR, frag_t(Bm, 16 * jb, 0, lane), frag_n(P1, 16 * tb, 0, lane));
-        aR = fmma(aR, frag_t(Km, 16 * jb, 0, lane), frag_n(P2, 16 * tb, 0, lane));
-        f32x4 aA = fmma(zero4(), frag_t(S0m, 16 * jb, 0, lane), frag_n(DSAm, 16 * tb, 0, lane));
-        aA = fmma(aA, frag_t(S0m, 16 * jb, 32, lane), frag_n(DSAm, 16 * tb, 32, lane));
-        aA = fmma(aA, frag_t(Bm, 16 * jb, 0, lane), frag_n(P3, 16 * tb, 0, lane));
-        aA = fmma(aA, frag_t(Km, 16 * jb, 0, lane), frag_n(P4, 16 * tb, 0, lane));
-        f32x4 aK = fmma<false, true>(zero4(), frag_t(Gem, 16 * jb, 0, lane), frag_n(Vm, 16 * tb, 0, lane));
-        aK = fmma<false, true>(aK, frag_t(Gem, 16 * jb, 32, lane), frag_n(Vm, 16 * tb, 32, lane));
-        aK = fmma(aK, frag_t(A, 16 * jb, 0, lane), frag_t(P4, 16 * tb, 0, lane));
-        aK = fmma(aK, frag_t(R, 16 * jb, 0, lane), frag_t(P2, 16 * tb, 0, lane));
-        f32x4 aB = fmma(zero4(), frag_t(Gem, 16 * jb, 0, lane), frag_n(Um, 16 * tb, 0, lane));
-        aB = fmma(aB, frag_t(Gem, 16 * jb, 32, lane), frag_n(Um, 16 * tb, 32, lane));
-        aB = fmma(aB, frag_t(A, 16 * jb, 0, lane), frag_t(P3, 16 * tb, 0, lane));
-        aB = fmma(aB, frag_t(R, 16 * jb, 0, lane), frag_t(P1, 16 * tb, 0, lane));
-
-        const int t = 16 * tb + r16, j0 = 16 * jb + 4 * g4;
-        const f32x4 g = *reinterpret_cast<const f32x4*>(gam + t * LDG + j0);
-        const f32x4 gp = t > 0 ? *reinterpret_cast<const f32x4*>(gam + (t - 1) * LDG + j0) : f32x4{1.f, 1.f, 1.f, 1.f};
-        f32x4 ig;
+        f32x4 ac[2][2];   // [first / second output][j block]
+        if (pr == 0) {
+            const Fr dy0 = frag_n(DYm, 16 * tb, 0, lane), dy1 = frag_n(DYm, 16 * tb, 32, lane);
+            const Fr ds0 = frag_n(DSAm, 16 * tb, 0, lane), ds1 = frag_n(DSAm, 16 * tb, 32, lane);
+            const Fr p1 = frag_n(P1, 16 * tb, 0, lane), p2 = frag_n(P2, 16 * tb, 0, lane);
+            const Fr p3 = frag_n(P3, 16 * tb, 0, lane), p4 = frag_n(P4, 16 * tb, 0, lane);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ig[q] = rcp(g[q]);
-        const int voff = (t * HD + j0) * 4, soff_ = t0 * HD * 4;
-        bstore4(aR * g, rdr, voff, soff_);
-        bstore4(aA * gp, rda, voff, soff_);
-        bstore4(aK * ig, rdk, voff, soff_);
-        bstore4(aB * ig, rdb, voff, soff_);
-        // k dk = Ktil aK, b db = Btil aB, r dr = Rhat aR, a da = Ahat aA
-        const f32x4 fa = get4(A, t, j0) * aA;
-        const f32x4 ev = get4(Km, t, j0) * aK + get4(Bm, t, j0) * aB - get4(R, t, j0) * aR;
-        *reinterpret_cast<f32x4*>(hh_ + t * LDG + j0) = ev - fa;
-        *reinterpret_cast<f32x4*>(fa_ + t * LDG + j0) = fa;
+            for (int jj = 0; jj < 2; ++jj) {
+                const int jb = jb0 + jj;
+                const Fr s0a = frag_t(S0m, 16 * jb, 0, lane), s0b = frag_t(S0m, 16 * jb, 32, lane);
+                const Fr bt = frag_t(Bm, 16 * jb, 0, lane), kt = frag_t(Km, 16 * jb, 0, lane);
+                f32x4 aR = fmma(zero4(), s0a, dy0), aA = fmma(zero4(), s0a, ds0);
+                aR = fmma(aR, s0b, dy1);
+                aA = fmma(aA, s0b, ds1);
+                aR = fmma(aR, bt, p1);
+                aA = fmma(aA, bt, p3);
+                aR = fmma(aR, kt, p2);
+                aA = fmma(aA, kt, p4);
+                ac[0][jj] = aR;
+                ac[1][jj] = aA;
+            }
+        } else {
+            const Fr v0 = frag_n(Vm, 16 * tb, 0, lane), v1 = frag_n(Vm, 16 * tb, 32, lane);
+            const Fr u0 = frag_n(Um, 16 * tb, 0, lane), u1 = frag_n(Um, 16 * tb, 32, lane);
+            const Fr p1 = frag_t(P1, 16 * tb, 0, lane), p2 = frag_t(P2, 16 * tb, 0, lane);
+            const Fr p3 = frag_t(P3, 16 * tb, 0, lane), p4 = frag_t(P4, 16 * tb, 0, lane);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int jb = jb0 + jj;
+                const Fr g0 = frag_t(Gem, 16 * jb, 0, lane), g1 = frag_t(Gem, 16 * jb, 32, lane);
+                const Fr at = frag_t(A, 16 * jb, 0, lane), rt = frag_t(R, 16 * jb, 0, lane);
+                f32x4 aK = fmma<false, true>(zero4(), g0, v0), aB = fmma(zero4(), g0, u0);
+                aK = fmma<false, true>(aK, g1, v1);
+                aB = fmma(aB, g1, u1);
+                aK = fmma(aK, at, p4);
+                aB = fmma(aB, at, p3);
+                aK = fmma(aK, rt, p2);
+                aB = fmma(aB, rt, p1);
+                ac[0][jj] = aK;
+                ac[1][jj] = aB;
+            }
+        }
+        const Rsrc r0 = make_rsrc((pr == 0 ? p.dr : p.dk) + tok0, span);
+        const Rsrc r1 = make_rsrc((pr == 0 ? p.da : p.db) + tok0, span);
+        const int soff_ = t0 * HD * 4;
+        const int tp = t > 0 ? t - 1 : 0;
+        f32x4 evr[2];   // waves 0-3: -r dr - a da, added to hh_ after the barrier
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j0 = 16 * (jb0 + jj) + 4 * g4;
+            const int voff = (t * HD + j0) * 4;
+            const f32x4 g = *reinterpret_cast<const f32x4*>(gam + t * LDG + j0);
+            if (pr == 0) {
+                // dr = gamma_t aR, da = gamma_{t-1} aA; r dr = Rhat aR, a da = Ahat aA
+                const f32x4 gpl = *reinterpret_cast<const f32x4*>(gam + tp * LDG + j0);
+                const f32x4 gp = t > 0 ? gpl : f32x4{1.f, 1.f, 1.f, 1.f};
+                bstore4(ac[0][jj] * g, r0, voff, soff_);
+                bstore4(ac[1][jj] * gp, r1, voff, soff_);
+                const f32x4 fa = get4(A, t, j0) * ac[1][jj];
+                evr[jj] = -(get4(R, t, j0) * ac[0][jj]) - fa;
+                *reinterpret_cast<f32x4*>(fa_ + t * LDG + j0) = fa;
+            } else {
+                // dk = aK / gamma_t, db = aB / gamma_t; k dk = Ktil aK, b db = Btil aB
+                f32x4 ig;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ig[q] = rcp(g[q]);
+                bstore4(ac[0][jj] * ig, r0, voff, soff_);
+                bstore4(ac[1][jj] * ig, r1, voff, soff_);
+                *reinterpret_cast<f32x4*>(hh_ + t * LDG + j0) =
+                    get4(Km, t, j0) * ac[0][jj] + get4(Bm, t, j0) * ac[1][jj];
+            }
+        }
+        lds_barrier();
+        if (pr == 0) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                f32x4* h = reinterpret_cast<f32x4*>(hh_ + t * LDG + 16 * (jb0 + jj) + 4 * g4);
+                *h = *h + evr[jj];
+            }
+        }
     }
     lds_barrier();
 
