@@ -368,11 +368,10 @@ __device__ __forceinline__ void chunk_prep(const RawChunk<NT, InT>& raw, const P
     lds_barrier();
     float2 pre = make_float2(1.f, 1.f);
 #pragma unroll
-    for (int q2 = 0; q2 < NG; ++q2) {
-        if (q2 < q) {
-            pre.x *= qp[q2 * 64 + j0];
-            pre.y *= qp[q2 * 64 + j0 + 1];
-        }
+    for (int q2 = 0; q2 < NG; ++q2) {   // selects, not branches: a factor 1 leaves the product unchanged
+        const float2 v = *reinterpret_cast<const float2*>(qp + q2 * 64 + j0);
+        pre.x *= q2 < q ? v.x : 1.f;
+        pre.y *= q2 < q ? v.y : 1.f;
     }
     float2 gprev = pre;
     float gt[2][TPG], at[2][TPG], rt[2][TPG], bt[2][TPG], kt[2][TPG];
@@ -635,6 +634,10 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 // write of that register.)
 __device__ __forceinline__ void bstore(float v, Rsrc r, int voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff + soff, 0, 0);
+}
+__device__ __forceinline__ void bstore2(float2 v, Rsrc r, int voff, int soff) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff + soff, 0, 0);
 }
 __device__ __forceinline__ void bstore4(f32x4 v, Rsrc r, int voff, int soff) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

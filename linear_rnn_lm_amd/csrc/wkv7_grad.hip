@@ -80,6 +80,43 @@ __device__ __forceinline__ Mat<SPLIT> exact_mat(char* smem, int off, int K) {
 
 // Where one chunk's inputs live.  `on == false` (no next chunk) gives every
 // buffer resource size 0, so the loads return zeros without touching memory.
+// The chunks of one workgroup: blockIdx.x, + gridDim.x, ... in the block_map
+// order, walked without divisions (the steps are divided out once).
+struct ChunkWalk {
+    int head, c, bb, hh;               // position: head = bb * H + hh, chunk c
+    int NC, H, dc, dh, hs, qa, ra, qb, rb;
+
+    __device__ __forceinline__ ChunkWalk(const BwdArgs& p, int blk, int grid, bool xcd) {
+        block_map(blk, p.NC, xcd, head, c);
+        NC = p.NC;
+        H = p.H;
+        bb = head / H;
+        hh = head % H;
+        hs = xcd ? 8 : 1;                       // head step of one carry out of c
+        const int gs = xcd ? grid >> 3 : grid;  // chunk-index step (grid % 8 == 0 with xcd)
+        dc = gs % NC;
+        dh = (gs / NC) * hs;
+        qa = dh / H;
+        ra = dh % H;
+        qb = (dh + hs) / H;
+        rb = (dh + hs) % H;
+    }
+    __device__ __forceinline__ void advance() {
+        c += dc;
+        const bool carry = c >= NC;
+        if (carry) c -= NC;
+        head += dh + (carry ? hs : 0);
+        hh += carry ? rb : ra;
+        bb += carry ? qb : qa;
+        if (hh >= H) {
+            hh -= H;
+            bb += 1;
+        }
+    }
+};
+
+// Where one chunk's inputs live.  `on == false` (no next chunk) gives every
+// buffer resource size 0, so the loads return zeros without touching memory.
 struct ChunkSrc {
     int64_t tok0;   // element offset of the head's token 0
     int64_t cs;     // element offset of the chunk's D x D state blocks
@@ -88,17 +125,16 @@ struct ChunkSrc {
     bool on, has_ge;
     const float* ge;   // gradient at the chunk's end: next checkpoint's, dhT, or none
 
-    __device__ __forceinline__ ChunkSrc(const BwdArgs& p, int head, int c, bool on_) {
-        const int bb = head / p.H, hh = head % p.H;
+    __device__ __forceinline__ ChunkSrc(const BwdArgs& p, const ChunkWalk& w, bool on_) {
         const int HD = p.H * D;
-        tok0 = (int64_t)bb * p.T * HD + (int64_t)hh * D;
-        cs = ((int64_t)head * p.NC + c) * D * D;
-        ci = ((int64_t)head * p.NC + c) * C * C;
-        t0 = c * C;
+        tok0 = (int64_t)w.bb * p.T * HD + (int64_t)w.hh * D;
+        cs = ((int64_t)w.head * p.NC + w.c) * D * D;
+        ci = ((int64_t)w.head * p.NC + w.c) * C * C;
+        t0 = w.c * C;
         cc = min(C, p.T - t0);
         on = on_;
-        has_ge = c + 1 < p.NC || p.dhT != nullptr;
-        ge = (c + 1 < p.NC) ? p.gbuf + cs + D * D : (p.dhT ? p.dhT + (int64_t)head * D * D : p.gbuf);
+        has_ge = w.c + 1 < p.NC || p.dhT != nullptr;
+        ge = (w.c + 1 < p.NC) ? p.gbuf + cs + D * D : (p.dhT ? p.dhT + (int64_t)w.head * D * D : p.gbuf);
     }
 };
 
@@ -197,27 +233,24 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int r16 = lane & 15, g4 = lane >> 4;
     const int HD = p.H * D;
-    const int64_t tstride = HD;
     const uint32_t span = (uint32_t)(((int64_t)(p.T - 1) * HD + D) * 4);
     // state-sized inputs: thread holds row si = tid / 8, columns sj0 .. sj0 + 7
     const int si = tid >> 3, sj0 = (tid & 7) * 8;
 
-    int idx = blockIdx.x, head, c;
-    block_map(idx, p.NC, xcd != 0, head, c);
+    int idx = blockIdx.x;
+    ChunkWalk cw(p, idx, gridDim.x, xcd != 0);
     GradIn<InT> cur, nxt;
-    cur.issue_all(p, ChunkSrc(p, head, c, true), tid);
+    cur.issue_all(p, ChunkSrc(p, cw, true), tid);
 
   for (;;) {
+    const int head = cw.head, c = cw.c, bb = cw.bb, hh = cw.hh;
     const int nidx = idx + (int)gridDim.x;
     const bool more = nidx < total;
-    int nhead, ncc;
-    block_map(more ? nidx : idx, p.NC, xcd != 0, nhead, ncc);
-    const ChunkSrc nsrc(p, nhead, ncc, more);
+    ChunkWalk nw = cw;
+    nw.advance();
+    const ChunkSrc nsrc(p, nw, more);
     nxt.template issue<0>(p, nsrc, tid);
-    const int bb = head / p.H, hh = head % p.H;
     const int t0 = c * C;
-    const int Cc = min(C, p.T - t0);
-    const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
     // the head's tokens: outputs past the sequence's end are dropped
     const int64_t tok0 = (int64_t)bb * p.T * HD + (int64_t)hh * D;
 
@@ -364,13 +397,17 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         const int t = 16 * tb + r16;
         const M P1 = Pm(0), P2 = Pm(1), P3 = Pm(2), P4 = Pm(3);
         f32x4 ac[2][2];   // [first / second output][j block]
+        // t-side fragments are read inside the j-block loop: for the split format the two unrolled
+        // iterations share them; fp32 fragments take twice the registers, so a compiler barrier makes
+        // each iteration read them again instead of keeping them live.
         if (pr == 0) {
-            const Fr dy0 = frag_n(DYm, 16 * tb, 0, lane), dy1 = frag_n(DYm, 16 * tb, 32, lane);
-            const Fr ds0 = frag_n(DSAm, 16 * tb, 0, lane), ds1 = frag_n(DSAm, 16 * tb, 32, lane);
-            const Fr p1 = frag_n(P1, 16 * tb, 0, lane), p2 = frag_n(P2, 16 * tb, 0, lane);
-            const Fr p3 = frag_n(P3, 16 * tb, 0, lane), p4 = frag_n(P4, 16 * tb, 0, lane);
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
+                if constexpr (!SPLIT) asm volatile("" ::: "memory");
+                const Fr dy0 = frag_n(DYm, 16 * tb, 0, lane), dy1 = frag_n(DYm, 16 * tb, 32, lane);
+                const Fr ds0 = frag_n(DSAm, 16 * tb, 0, lane), ds1 = frag_n(DSAm, 16 * tb, 32, lane);
+                const Fr p1 = frag_n(P1, 16 * tb, 0, lane), p2 = frag_n(P2, 16 * tb, 0, lane);
+                const Fr p3 = frag_n(P3, 16 * tb, 0, lane), p4 = frag_n(P4, 16 * tb, 0, lane);
                 const int jb = jb0 + jj;
                 const Fr s0a = frag_t(S0m, 16 * jb, 0, lane), s0b = frag_t(S0m, 16 * jb, 32, lane);
                 const Fr bt = frag_t(Bm, 16 * jb, 0, lane), kt = frag_t(Km, 16 * jb, 0, lane);
@@ -385,12 +422,13 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
                 ac[1][jj] = aA;
             }
         } else {
-            const Fr v0 = frag_n(Vm, 16 * tb, 0, lane), v1 = frag_n(Vm, 16 * tb, 32, lane);
-            const Fr u0 = frag_n(Um, 16 * tb, 0, lane), u1 = frag_n(Um, 16 * tb, 32, lane);
-            const Fr p1 = frag_t(P1, 16 * tb, 0, lane), p2 = frag_t(P2, 16 * tb, 0, lane);
-            const Fr p3 = frag_t(P3, 16 * tb, 0, lane), p4 = frag_t(P4, 16 * tb, 0, lane);
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
+                if constexpr (!SPLIT) asm volatile("" ::: "memory");
+                const Fr v0 = frag_n(Vm, 16 * tb, 0, lane), v1 = frag_n(Vm, 16 * tb, 32, lane);
+                const Fr u0 = frag_n(Um, 16 * tb, 0, lane), u1 = frag_n(Um, 16 * tb, 32, lane);
+                const Fr p1 = frag_t(P1, 16 * tb, 0, lane), p2 = frag_t(P2, 16 * tb, 0, lane);
+                const Fr p3 = frag_t(P3, 16 * tb, 0, lane), p4 = frag_t(P4, 16 * tb, 0, lane);
                 const int jb = jb0 + jj;
                 const Fr g0 = frag_t(Gem, 16 * jb, 0, lane), g1 = frag_t(Gem, 16 * jb, 32, lane);
                 const Fr at = frag_t(A, 16 * jb, 0, lane), rt = frag_t(R, 16 * jb, 0, lane);
@@ -471,20 +509,18 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
             acc.y += red[g * 64 + j0 + 1];
         }
 #pragma unroll
-        for (int q2 = 0; q2 < NG; ++q2) {
-            if (q2 < q) {
-                acc.x += qp[q2 * 64 + j0];
-                acc.y += qp[q2 * 64 + j0 + 1];
-            }
+        for (int q2 = 0; q2 < NG; ++q2) {   // selects, not branches: adding 0 leaves the sum unchanged
+            const float2 v = *reinterpret_cast<const float2*>(qp + q2 * 64 + j0);
+            acc.x += q2 < q ? v.x : 0.f;
+            acc.y += q2 < q ? v.y : 0.f;
         }
+        const Rsrc rdw = make_rsrc(p.dw + tok0, span);   // tokens past the end are dropped
 #pragma unroll
         for (int tt = 0; tt < TPG; ++tt) {
             const int t = q * TPG + tt;
-            if (t < Cc) {
-                const float2 wv = Pair<InT>::f(cur.raw.w[tt]);
-                *reinterpret_cast<float2*>(p.dw + base + t * tstride + j0) =
-                    make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y));
-            }
+            const float2 wv = Pair<InT>::f(cur.raw.w[tt]);
+            bstore2(make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y)), rdw,
+                    (t * HD + j0) * 4, t0 * HD * 4);
             acc.x += hx[tt].x;
             acc.y += hx[tt].y;
         }
@@ -492,8 +528,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     if (!more) break;
     cur = nxt;
     idx = nidx;
-    head = nhead;
-    c = ncc;
+    cw = nw;
     lds_barrier();   // this chunk's last LDS reads before the next chunk's writes
   }
 }
