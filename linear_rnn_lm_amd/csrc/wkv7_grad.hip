@@ -53,8 +53,8 @@ struct GradSmem {
     static constexpr int Gam = Ge + SM;              // fp32 gamma [t][j], stride LDG
     static constexpr int glast = Gam + C * LDG * 4;
     static constexpr int qp = glast + D * 4;         // fp32 16 x 64
-    static constexpr int red = qp + 16 * D * 4;      // fp32 8 x 64
-    static constexpr int Q = red + 8 * D * 4;
+    static constexpr int red = qp + 16 * D * 4;      // fp32 10 x 64: parts of diag(Gs^T S0)
+    static constexpr int Q = red + 10 * D * 4;
     // region Q, phases 0-3
     static constexpr int Tm = Q;                     // T rows (t, s)
     static constexpr int Lak = Tm + CM;              // Lak rows (t, s)
@@ -140,7 +140,7 @@ struct ChunkSrc {
 
 // Everything one chunk reads from global memory, held in registers so that
 // the next chunk's loads are in flight while the current chunk computes.  The
-// loads are issued in six parts, one per compute phase, so that no wave
+// loads are issued in five parts, one per compute phase, so that no wave
 // stalls on a full memory queue; buffer loads without branches keep the
 // wave's count of outstanding loads exact.
 template <typename InT>
@@ -150,7 +150,7 @@ struct GradIn {
     RawChunk<GNT, InT> raw;          // w, a, r, b, k
     RawCols<GNT, D, InT> rv;         // v
     RawCols<GNT, D, float> rdy;      // dy
-    f32x4 s0v[2], gsv[2], gev[2];    // S0, Gs (gradient entering), Ge (gradient at the end): row si, 8 columns
+    f32x4 s0v[2], gev[2];            // S0, Ge (gradient at the chunk's end): row si, 8 columns
     float2 tv;                       // two entries of T = (I - Lab)^-1
 
     template <typename X>
@@ -203,10 +203,6 @@ struct GradIn {
             const Rsrc r = make_rsrc(p.ckpt + s.cs, sbytes);
             s0v[0] = ld4(r, soff);
             s0v[1] = ld4(r, soff + 16);
-        } else if constexpr (PART == 4) {
-            const Rsrc r = make_rsrc(p.gbuf + s.cs, sbytes);
-            gsv[0] = ld4(r, soff);
-            gsv[1] = ld4(r, soff + 16);
         } else {
             const Rsrc r = make_rsrc(s.ge, s.has_ge ? sbytes : 0u);
             gev[0] = ld4(r, soff);
@@ -219,7 +215,6 @@ struct GradIn {
         issue<2>(p, s, tid);
         issue<3>(p, s, tid);
         issue<4>(p, s, tid);
-        issue<5>(p, s, tid);
     }
 };
 
@@ -254,25 +249,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     // the head's tokens: outputs past the sequence's end are dropped
     const int64_t tok0 = (int64_t)bb * p.T * HD + (int64_t)hh * D;
 
-    // ---- phase 0: gamma and the scaled rows; partial sums of diag(Gs^T S0)
-    {
-        // this wave's 8 rows: lanes with equal tid % 8 hold the same 8 columns
-        f32x4 d0 = cur.gsv[0] * cur.s0v[0], d1 = cur.gsv[1] * cur.s0v[1];
-#pragma unroll
-        for (int m = 8; m < 64; m <<= 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                d0[e] += __shfl_xor(d0[e], m);
-                d1[e] += __shfl_xor(d1[e], m);
-            }
-        }
-        if (lane < 8) {
-            float* red = reinterpret_cast<float*>(smem + L::red) + wave * 64 + sj0;
-            *reinterpret_cast<f32x4*>(red) = d0;
-            *reinterpret_cast<f32x4*>(red + 4) = d1;
-        }
-    }
-
+    // ---- phase 0: gamma and the scaled rows
     const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
     const M Bm = make_mat<SPLIT>(smem, L::Bm, C, D), Km = make_mat<SPLIT>(smem, L::Km, C, D);
     const M Vm = exact_mat<SPLIT>(smem, L::V, D), DYm = make_mat<SPLIT>(smem, L::DY, C, D);
@@ -319,6 +296,21 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
 #pragma unroll
         for (int e = 0; e < 4; ++e) cur.gev[q][e] *= glast[sj0 + 4 * q + e];
         put4(Gem, si, sj0 + 4 * q, cur.gev[q]);
+    }
+    {   // sum_i G'[i][j] S0[i][j] over this wave's 8 rows (lanes with equal tid % 8 share columns)
+        f32x4 d0 = cur.gev[0] * cur.s0v[0], d1 = cur.gev[1] * cur.s0v[1];
+#pragma unroll
+        for (int m = 8; m < 64; m <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d0[e] += __shfl_xor(d0[e], m);
+                d1[e] += __shfl_xor(d1[e], m);
+            }
+        }
+        if (lane < 8) {
+            *reinterpret_cast<f32x4*>(red + wave * 64 + sj0) = d0;
+            *reinterpret_cast<f32x4*>(red + wave * 64 + sj0 + 4) = d1;
+        }
     }
     lds_barrier();
 
@@ -386,17 +378,19 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     }
     lds_barrier();
 
-    nxt.template issue<5>(p, nsrc, tid);
     // ---- phase 5: outputs, accumulator element (j, t).  Waves 0-3 form dr and da, waves 4-7 dk and
     // db; each wave one t block and two j blocks, so the t-side operands are read once for both.
     // The dw ingredients: waves 4-7 store k dk + b db to hh_, waves 0-3 store a da to fa_ and, after
-    // the next barrier, add -r dr - a da to hh_.
+    // the next barrier, add -r dr - a da to hh_.  Waves 0-3 also complete diag(Gs^T S0): with
+    // Gs = G' + DY^T Rhat + DSA^T Ahat it is sum_i G' S0 (phase 1) plus the column sums over t of
+    // Rhat * (DY S0) and Ahat * (DSA S0), the first terms of the dr and da accumulators.
     {
         using Fr = Frag<SPLIT>;
         const int pr = wave >> 2, tb = (wave >> 1) & 1, jb0 = (wave & 1) * 2;
         const int t = 16 * tb + r16;
         const M P1 = Pm(0), P2 = Pm(1), P3 = Pm(2), P4 = Pm(3);
         f32x4 ac[2][2];   // [first / second output][j block]
+        f32x4 xs[2][2];   // waves 0-3: DY S0 and DSA S0 tiles
         // t-side fragments are read inside the j-block loop: for the split format the two unrolled
         // iterations share them; fp32 fragments take twice the registers, so a compiler barrier makes
         // each iteration read them again instead of keeping them live.
@@ -414,6 +408,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
                 f32x4 aR = fmma(zero4(), s0a, dy0), aA = fmma(zero4(), s0a, ds0);
                 aR = fmma(aR, s0b, dy1);
                 aA = fmma(aA, s0b, ds1);
+                xs[0][jj] = aR;
+                xs[1][jj] = aA;
                 aR = fmma(aR, bt, p1);
                 aA = fmma(aA, bt, p3);
                 aR = fmma(aR, kt, p2);
@@ -459,9 +455,15 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
                 const f32x4 gp = t > 0 ? gpl : f32x4{1.f, 1.f, 1.f, 1.f};
                 bstore4(ac[0][jj] * g, r0, voff, soff_);
                 bstore4(ac[1][jj] * gp, r1, voff, soff_);
-                const f32x4 fa = get4(A, t, j0) * ac[1][jj];
-                evr[jj] = -(get4(R, t, j0) * ac[0][jj]) - fa;
+                const f32x4 ah = get4(A, t, j0), rh = get4(R, t, j0);
+                const f32x4 fa = ah * ac[1][jj];
+                evr[jj] = -(rh * ac[0][jj]) - fa;
                 *reinterpret_cast<f32x4*>(fa_ + t * LDG + j0) = fa;
+                // this wave's 16 tokens of sum_t Rhat (DY S0) + Ahat (DSA S0); lane r16 = 15 holds the sum
+                f32x4 dg = rh * xs[0][jj] + ah * xs[1][jj];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dg[q] = row_sum16(dg[q]);
+                if (r16 == 15) *reinterpret_cast<f32x4*>(red + (8 + tb) * 64 + j0) = dg;
             } else {
                 // dk = aK / gamma_t, db = aB / gamma_t; k dk = Ktil aK, b db = Btil aB
                 f32x4 ig;
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         lds_barrier();
         float2 acc = make_float2(0.f, 0.f);
 #pragma unroll
-        for (int g = 0; g < GNW; ++g) {
+        for (int g = 0; g < GNW + 2; ++g) {   // diag(Gs^T S0): 8 waves' G' S0 rows, 2 token blocks
             acc.x += red[g * 64 + j0];
             acc.y += red[g * 64 + j0 + 1];
         }
