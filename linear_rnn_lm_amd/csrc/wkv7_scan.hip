@@ -316,7 +316,12 @@ struct XCopy {
             if constexpr (sizeof(XT) == 2) {
                 *reinterpret_cast<u32x4*>(reinterpret_cast<__bf16*>(X.p) + t * X.ld + e0) = v[u];
             } else {
-                put4(X, t, e0, __builtin_bit_cast(f32x4, v[u]));
+                // The split of the fp32 values is register arithmetic: pin it here, after the
+                // preceding barrier, or it is hoisted to where the load was just issued and the
+                // wave waits for it there.
+                u32x4 w = v[u];
+                asm volatile("" : "+v"(w));
+                put4(X, t, e0, __builtin_bit_cast(f32x4, w));
             }
         }
     }
@@ -397,6 +402,10 @@ __global__ __launch_bounds__(128 * NWV) void scan_kernel(ScanArgs p, int xcd) {
         fetch(oa, xa, 0);
         put(oa, xa, 0);
         fetch(ob, xb, 1);
+        // Keep chunk 1's loads ahead of chunk 2's: entering the loop with chunk
+        // 1 issued last would make the compiler's count at the loop top (where
+        // chunk 1 is consumed) a full drain in every iteration.
+        __builtin_amdgcn_sched_barrier(0);
         fetch(oa, xa, 2);
         lds_barrier();
         // Two iterations per trip, straight-line code (so that every wait is
