@@ -819,4 +819,12 @@ __device__ __forceinline__ void gput4(float* X, int64_t, int64_t idx, f32x4 v) {
     *reinterpret_cast<f32x4*>(X + idx) = v;
 }
 
+// Accumulator tile (lane (g, r) holds row r, columns 4g .. 4g + 3) stored as
+// tile `tile` of a plane-major sequence of row-major 16 x 16 tiles: the wave's
+// stores fill one contiguous 512-byte (bf16) or 1 KiB (fp32) block per plane.
+template <typename X>
+__device__ __forceinline__ void tput4(X* base, int64_t plane, int tile, int lane, f32x4 v) {
+    gput4(base, plane, (int64_t)tile * 256 + (lane & 15) * 16 + 4 * (lane >> 4), v);
+}
+
 }  // namespace wkv7

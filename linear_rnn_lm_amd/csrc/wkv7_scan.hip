@@ -37,7 +37,9 @@ namespace {
 
 // Element offsets of P, M, E, F inside one chunk's operand block, in storage
 // elements (bf16 for the split format, which keeps the hi plane of a matrix
-// followed by its lo plane; fp32 otherwise).  Rows are unpadded.
+// followed by its lo plane; fp32 otherwise).  Each plane is a sequence of
+// 16 x 16 tiles, row-major over the tiles and row-major inside a tile (256
+// elements), so that one wave stores a whole tile as one contiguous block.
 template <bool SPLIT>
 struct OpsLayout {
     using E = typename std::conditional<SPLIT, __bf16, float>::type;
@@ -180,10 +182,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
         const f32x4 f00 = fmma(mk0, frag_t(Zm, 0, 0, lane), frag_n(Mrb, 0, 0, lane));
         const f32x4 f01 = fmma(mk1, frag_t(Zm, 0, 0, lane), frag_n(Mrb, 16, 0, lane));
         const f32x4 f11 = fmma(mk2, frag_t(Zm, 16, 0, lane), frag_n(Mrb, 16, 0, lane));
-        gput4(ob + O::F, C * C, r16 * C + 4 * g4, f00);
-        gput4(ob + O::F, C * C, (16 + r16) * C + 4 * g4, f01);
-        gput4(ob + O::F, C * C, (16 + r16) * C + 16 + 4 * g4, f11);
-        gput4(ob + O::F, C * C, r16 * C + 16 + 4 * g4, zero4());
+        // F tiles (row block, column block): (0, 0), (1, 0), (1, 1) and the zero tile (0, 1)
+        tput4(ob + O::F, C * C, 0, lane, f00);
+        tput4(ob + O::F, C * C, 2, lane, f01);
+        tput4(ob + O::F, C * C, 3, lane, f11);
+        tput4(ob + O::F, C * C, 1, lane, zero4());
     }
     const int w3 = wave == 3 ? 2 : wave;
     const int jlo = wave == 2 ? 27 : 9 * w3, jhi = wave == 2 ? 32 : 9 * w3 + 9;
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
             const int j = 16 * qb + r16, jp0 = 16 * pb + 4 * g4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[q] = (acc[q] + (jp0 + q == j ? 1.f : 0.f)) * glast[jp0 + q];
-            gput4(ob + O::P, D * D, j * D + jp0, acc);
+            tput4(ob + O::P, D * D, qb * 4 + pb, lane, acc);
         } else if (jj < 24) {
             // M[t][j] = (sum_s Z[s][t] Btil[s][j] + Ktil[t][j]) gamma_last[j]; element (j, t)
             const int jb = (jj - 16) & 3, tb = (jj - 16) >> 2;
@@ -204,14 +207,14 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
             const f32x4 kt = get4(Km, t, j0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[q] = (acc[q] + kt[q]) * glast[j0 + q];
-            gput4(ob + O::M, C * D, t * D + j0, acc);
+            tput4(ob + O::M, C * D, tb * 4 + jb, lane, acc);
         } else {
             // E[t][j] = Rhat[t][j] + sum_s Mrb[t][s] W1[s][j]; element (j, t)
             const int jb = (jj - 24) & 3, tb = (jj - 24) >> 2;
             f32x4 acc = fmma(zero4(), frag_t(W1, 16 * jb, 0, lane), frag_n(Mrb, 16 * tb, 0, lane));
             const int t = 16 * tb + r16, j0 = 16 * jb + 4 * g4;
             acc += get4(R, t, j0);
-            gput4(ob + O::E_, C * D, t * D + j0, acc);
+            tput4(ob + O::E_, C * D, tb * 4 + jb, lane, acc);
         }
     }
 }
@@ -249,16 +252,18 @@ struct OpsCopy {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int e = (tid + NT * u) * EPU;
-            int first, lbase, kshift, rkshift;  // rows * cols = 1 << rkshift, cols = 1 << kshift
-            if (e < O::M) { first = O::P; lbase = I::P; kshift = 6; rkshift = 12; }
-            else if (e < O::E_) { first = O::M; lbase = I::M; kshift = 6; rkshift = 11; }
-            else if (e < O::F) { first = O::E_; lbase = I::E; kshift = 6; rkshift = 11; }
-            else { first = O::F; lbase = I::Fm; kshift = 5; rkshift = 10; }
+            int first, lbase, cols, rows;
+            if (e < O::M) { first = O::P; lbase = I::P; cols = D; rows = D; }
+            else if (e < O::E_) { first = O::M; lbase = I::M; cols = D; rows = C; }
+            else if (e < O::F) { first = O::E_; lbase = I::E; cols = D; rows = C; }
+            else { first = O::F; lbase = I::Fm; cols = C; rows = C; }
+            // local -> (plane, tile, row and column inside the tile) -> image row, column
             const int local = e - first;
-            const int plane = local >> rkshift, rem = local & ((1 << rkshift) - 1);
-            const int row = rem >> kshift, col = rem & ((1 << kshift) - 1);
-            const int rows = 1 << (rkshift - kshift), ld = (1 << kshift) + PAD;
-            off[u] = lbase + ((plane * rows + row) * ld + col) * ESZ;
+            const int plane = local / (rows * cols), rem = local % (rows * cols);
+            const int tile = rem >> 8, in = rem & 255;
+            const int tr = tile / (cols / 16), tc = tile % (cols / 16);
+            const int row = 16 * tr + (in >> 4), col = 16 * tc + (in & 15);
+            off[u] = lbase + ((plane * rows + row) * (cols + PAD) + col) * ESZ;
         }
     }
     __device__ __forceinline__ void load(const char* src, int tid) {
