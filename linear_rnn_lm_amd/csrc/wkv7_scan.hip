@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
     using O = OpsLayout<SPLIT>;
     using E = typename O::E;
     constexpr int NT = 256;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
     const int item = blockIdx.x;  // (head, chunk)
     const int head = item / p.NC, c = item % p.NC;
@@ -156,65 +156,78 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
     }
     lds_barrier();
 
-    // ---- W1 = T Ahat (rows t, columns j) and Z = T Lak (rows t, columns u)
-    for (int job = wave; job < 12; job += 4) {
-        if (job < 8) {
-            const int jb = job & 3, tb = job >> 2;
-            // element (j, t) = sum_s Ahat[s][j] T[t][s]
-            const f32x4 acc = fmma(zero4(), frag_t(A, 16 * jb, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
-            put4(W1, 16 * tb + r16, 16 * jb + 4 * g4, acc);
-        } else if (job < 11) {
-            const int ub = job == 10 ? 1 : 0, tb = job == 8 ? 0 : 1;
+    // ---- W1 = T Ahat (rows t, columns j) and Z = T Lak (rows t, columns u).  Wave w: W1 tiles
+    // (t blocks 0, 1; j block w) and Z tile w of (u block, t block) = (0, 0), (0, 1), (1, 1); wave 3
+    // the zero Z tile (t < 16 <= u).
+    {
+        const Frag<SPLIT> aw = frag_t(A, 16 * wave, 0, lane);
+        // element (j, t) = sum_s Ahat[s][j] T[t][s]
+        const f32x4 w0 = fmma(zero4(), aw, frag_n(Tm, 0, 0, lane));
+        const f32x4 w1 = fmma(zero4(), aw, frag_n(Tm, 16, 0, lane));
+        if (wave < 3) {
+            const int ub = wave == 2 ? 1 : 0, tb = wave == 0 ? 0 : 1;
             // element (u, t) = sum_s Lak[s][u] T[t][s]
-            const f32x4 acc = fmma(zero4(), frag_t(Lak, 16 * ub, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
-            put4(Zm, 16 * tb + r16, 16 * ub + 4 * g4, acc);
+            const f32x4 z = fmma(zero4(), frag_t(Lak, 16 * ub, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
+            put4(Zm, 16 * tb + r16, 16 * ub + 4 * g4, z);
         } else {
-            put4(Zm, r16, 16 + 4 * g4, zero4());  // t < 16 <= u
+            put4(Zm, r16, 16 + 4 * g4, zero4());
         }
+        put4(W1, r16, 16 * wave + 4 * g4, w0);
+        put4(W1, 16 + r16, 16 * wave + 4 * g4, w1);
     }
     lds_barrier();
 
     // ---- P, M, E, F to the chunk's operand block; every lane writes four
     // consecutive columns of one row per tile
     E* ob = reinterpret_cast<E*>(static_cast<char*>(p.ops) + (int64_t)item * kOpsBytes);
-    if (wave == 2) {
-        // F[t][u] = Mrk[t][u] + sum_s Mrb[t][s] Z[s][u]; accumulator element (u, t)
-        const f32x4 f00 = fmma(mk0, frag_t(Zm, 0, 0, lane), frag_n(Mrb, 0, 0, lane));
-        const f32x4 f01 = fmma(mk1, frag_t(Zm, 0, 0, lane), frag_n(Mrb, 16, 0, lane));
-        const f32x4 f11 = fmma(mk2, frag_t(Zm, 16, 0, lane), frag_n(Mrb, 16, 0, lane));
-        // F tiles (row block, column block): (0, 0), (1, 0), (1, 1) and the zero tile (0, 1)
-        tput4(ob + O::F, C * C, 0, lane, f00);
-        tput4(ob + O::F, C * C, 2, lane, f01);
-        tput4(ob + O::F, C * C, 3, lane, f11);
-        tput4(ob + O::F, C * C, 1, lane, zero4());
-    }
-    const int w3 = wave == 3 ? 2 : wave;
-    const int jlo = wave == 2 ? 27 : 9 * w3, jhi = wave == 2 ? 32 : 9 * w3 + 9;
-    for (int jj = jlo; jj < jhi; ++jj) {
-        if (jj < 16) {
-            // P[j][j'] = (delta + sum_t W1[t][j] Btil[t][j']) gamma_last[j']; element (j', j)
-            const int pb = jj & 3, qb = jj >> 2;
-            f32x4 acc = fmma(zero4(), frag_t(Bm, 16 * pb, 0, lane), frag_t(W1, 16 * qb, 0, lane));
-            const int j = 16 * qb + r16, jp0 = 16 * pb + 4 * g4;
+    // Wave w: P tiles (row block w, column blocks 0..3), M and E tiles (column block w, row
+    // blocks 0, 1); wave 2 also F, wave 3 F's zero tile.  The W1 and Btil fragments of column
+    // block w serve several tiles; all tiles of a wave are independent chains.
+    {
+        using Fr = Frag<SPLIT>;
+        const Fr w1w = frag_t(W1, 16 * wave, 0, lane);   // W1 columns 16w ..
+        const Fr bw = frag_t(Bm, 16 * wave, 0, lane);    // Btil columns 16w ..
+        f32x4 pa[4], ma[2], ea[2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] = (acc[q] + (jp0 + q == j ? 1.f : 0.f)) * glast[jp0 + q];
-            tput4(ob + O::P, D * D, qb * 4 + pb, lane, acc);
-        } else if (jj < 24) {
-            // M[t][j] = (sum_s Z[s][t] Btil[s][j] + Ktil[t][j]) gamma_last[j]; element (j, t)
-            const int jb = (jj - 16) & 3, tb = (jj - 16) >> 2;
-            f32x4 acc = fmma(zero4(), frag_t(Bm, 16 * jb, 0, lane), frag_t(Zm, 16 * tb, 0, lane));
-            const int t = 16 * tb + r16, j0 = 16 * jb + 4 * g4;
+        for (int pb = 0; pb < 4; ++pb)
+            pa[pb] = fmma(zero4(), pb == wave ? bw : frag_t(Bm, 16 * pb, 0, lane), w1w);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            ma[tb] = fmma(zero4(), bw, frag_t(Zm, 16 * tb, 0, lane));
+            ea[tb] = fmma(zero4(), w1w, frag_n(Mrb, 16 * tb, 0, lane));
+        }
+        // P[j][j'] = (delta + sum_t W1[t][j] Btil[t][j']) gamma_last[j']; element (j', j), j = 16w + r
+        const int j = 16 * wave + r16;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+            const int jp0 = 16 * pb + 4 * g4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pa[pb][q] = (pa[pb][q] + (jp0 + q == j ? 1.f : 0.f)) * glast[jp0 + q];
+            tput4(ob + O::P, D * D, wave * 4 + pb, lane, pa[pb]);
+        }
+        // M[t][j] = (sum_s Z[s][t] Btil[s][j] + Ktil[t][j]) gamma_last[j]; element (j, t), j = 16w + 4g + q
+        // E[t][j] = Rhat[t][j] + sum_s Mrb[t][s] W1[s][j]; element (j, t)
+        const int j0 = 16 * wave + 4 * g4;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int t = 16 * tb + r16;
             const f32x4 kt = get4(Km, t, j0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] = (acc[q] + kt[q]) * glast[j0 + q];
-            tput4(ob + O::M, C * D, tb * 4 + jb, lane, acc);
-        } else {
-            // E[t][j] = Rhat[t][j] + sum_s Mrb[t][s] W1[s][j]; element (j, t)
-            const int jb = (jj - 24) & 3, tb = (jj - 24) >> 2;
-            f32x4 acc = fmma(zero4(), frag_t(W1, 16 * jb, 0, lane), frag_n(Mrb, 16 * tb, 0, lane));
-            const int t = 16 * tb + r16, j0 = 16 * jb + 4 * g4;
-            acc += get4(R, t, j0);
-            tput4(ob + O::E_, C * D, tb * 4 + jb, lane, acc);
+            for (int q = 0; q < 4; ++q) ma[tb][q] = (ma[tb][q] + kt[q]) * glast[j0 + q];
+            tput4(ob + O::M, C * D, tb * 4 + wave, lane, ma[tb]);
+            tput4(ob + O::E_, C * D, tb * 4 + wave, lane, ea[tb] + get4(R, t, j0));
+        }
+        if (wave == 2) {
+            // F[t][u] = Mrk[t][u] + sum_s Mrb[t][s] Z[s][u]; accumulator element (u, t)
+            const f32x4 f00 = fmma(mk0, frag_t(Zm, 0, 0, lane), frag_n(Mrb, 0, 0, lane));
+            const f32x4 f01 = fmma(mk1, frag_t(Zm, 0, 0, lane), frag_n(Mrb, 16, 0, lane));
+            const f32x4 f11 = fmma(mk2, frag_t(Zm, 16, 0, lane), frag_n(Mrb, 16, 0, lane));
+            // F tiles (row block, column block): (0, 0), (1, 0), (1, 1)
+            tput4(ob + O::F, C * C, 0, lane, f00);
+            tput4(ob + O::F, C * C, 2, lane, f01);
+            tput4(ob + O::F, C * C, 3, lane, f11);
+        } else if (wave == 3) {
+            tput4(ob + O::F, C * C, 1, lane, zero4());   // (0, 1): u >= 16 > t
         }
     }
 }
