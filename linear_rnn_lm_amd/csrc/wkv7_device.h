@@ -246,6 +246,16 @@ __device__ __forceinline__ void store_cols(Mat<SPLIT> M, f32x4 acc, int m0, int 
     put4(M, n0 + r, m0 + 4 * g, v);
 }
 
+// fp32 tile store, transposed: M[n][m] = element (m, n) (stride ld floats)
+template <int MASK>
+__device__ __forceinline__ void store_f32_t(float* M, int ld, f32x4 acc, int m0, int n0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    f32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = masked<MASK>(acc[q], m0 + 4 * g + q, n0 + r);
+    *reinterpret_cast<f32x4*>(M + (n0 + r) * ld + m0 + 4 * g) = v;
+}
+
 // fp32 tile store into a plain row-major LDS array (stride ld floats)
 template <int MASK>
 __device__ __forceinline__ void store_f32(float* M, int ld, f32x4 acc, int m0, int n0, int lane) {
@@ -561,25 +571,29 @@ __device__ __forceinline__ void chunk_cc(Mat<SPLIT> A, Mat<SPLIT> R, Mat<SPLIT> 
 }
 
 // ---------------------------------------------------------------------------
-// T = (I - L)^-1 for the strictly lower C x C matrix L (fp32, stride LDF), by
-// 16 x 16 blocks: T11 = (I - L11)^-1 and T22 = (I - L22)^-1 by forward
-// substitution (lanes 0..15 and 16..31, one column each), then
-// T21 = T22 (L21 T11) with two fp32 MFMA products.  One wave.  `tf` (fp32,
-// stride LDF) receives T; `scr` is 16 x 20 floats of scratch.
-__device__ __forceinline__ void tri_inverse(const float* L, float* tf, float* scr, int lane) {
+// T = (I - L)^-1 for the strictly lower C x C matrix L, given transposed
+// (LT[s][t] = L[t][s], fp32, stride LDF), by 16 x 16 blocks: T11 = (I - L11)^-1
+// and T22 = (I - L22)^-1 by forward substitution (lanes 0..15 and 16..31, one
+// column each), then T21 = T22 (L21 T11) with two fp32 MFMA products.  One
+// wave.  `tf` (fp32, stride LDF) receives T; `scr` is 16 x 20 floats of scratch.
+__device__ __forceinline__ void tri_inverse(const float* LT, float* tf, float* scr, int lane) {
     if (lane < 32) {
         const int k = lane & 15, base = lane & 16;
+        // right-looking: once x[s] is final, every later row t takes L[t][s] x[s]; column s of
+        // L is row s of LT, read in 16-byte pieces (the updates of one step are independent)
         float x[16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const float* Lrow = L + (base + t) * LDF + base;
-            float acc0 = (t == k) ? 1.f : 0.f, acc1 = 0.f;
+        for (int t = 0; t < 16; ++t) x[t] = (t == k) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < t; s += 2) {
-                acc0 = fmaf(Lrow[s], x[s], acc0);
-                if (s + 1 < t) acc1 = fmaf(Lrow[s + 1], x[s + 1], acc1);
+        for (int s = 0; s < 15; ++s) {
+            const float* col = LT + (base + s) * LDF + base;
+#pragma unroll
+            for (int q0 = ((s + 1) >> 2) << 2; q0 < 16; q0 += 4) {
+                const f32x4 l = *reinterpret_cast<const f32x4*>(col + q0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (q0 + e > s) x[q0 + e] = fmaf(l[e], x[s], x[q0 + e]);
             }
-            x[t] = acc0 + acc1;
         }
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
@@ -588,12 +602,12 @@ __device__ __forceinline__ void tri_inverse(const float* L, float* tf, float* sc
         }
     }
     wave_lds_sync();
-    // P = L21 T11  (row t-16, column n)
+    // P = L21 T11  (row t-16, column n); L21[r][c] = LT[c][16 + r]
     const int r = lane & 15, g = lane >> 4;
     f32x4 acc = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < 16; k0 += 4)
-        acc = mfma_f32(L[(16 + r) * LDF + k0 + g], tf[(k0 + g) * LDF + r], acc);
+        acc = mfma_f32(LT[(k0 + g) * LDF + 16 + r], tf[(k0 + g) * LDF + r], acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) scr[(4 * g + q) * 20 + r] = acc[q];
     wave_lds_sync();

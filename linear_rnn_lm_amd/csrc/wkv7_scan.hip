@@ -65,7 +65,7 @@ struct PrepSmem {
     static constexpr int Mrb = Lak + F::bytes(C, C);   // Mrb rows (t, s)
     static constexpr int W1 = Mrb + F::bytes(C, C);    // W1 rows (t, j)
     static constexpr int Zm = W1 + F::bytes(C, D);     // Z rows (t, u)
-    static constexpr int LabF = Zm + F::bytes(C, C);   // fp32 Lab, stride LDF
+    static constexpr int LabF = Zm + F::bytes(C, C);   // fp32 Lab^T, stride LDF
     static constexpr int TF = LabF + C * LDF * 4;      // fp32 T, stride LDF
     static constexpr int Scr = TF + C * LDF * 4;       // 16 x 20 fp32
     static constexpr int glast = Scr + 16 * 20 * 4;    // fp32 [64]
@@ -112,17 +112,19 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
     chunk_prep<NT, SPLIT>(raw, po, qp, tid);
     lds_barrier();
 
-    // ---- C x C matrices and T (one wave each)
+    // ---- Lab^T (fp32, for the inverse): one lower tile per wave 0-2, wave 3 the zero tile
+    if (wave < 3) {
+        const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
+        const f32x4 t = mma<SPLIT, D>(zero4(), A, 16 * ti, Bm, 16 * tj, lane);
+        store_f32_t<MASK_STRICT>(labf, LDF, t, 16 * ti, 16 * tj, lane);
+    } else {
+        for (int e = lane; e < 256; e += 64) labf[(16 + (e >> 4)) * LDF + (e & 15)] = 0.f;
+    }
+    lds_barrier();
+
+    // ---- T = (I - Lab)^-1 (wave 3) while waves 0-2 form Lak, Mrb and Mrk
     f32x4 mk0 = zero4(), mk1 = zero4(), mk2 = zero4();
     if (wave == 3) {
-        const f32x4 t00 = mma<SPLIT, D>(zero4(), A, 0, Bm, 0, lane);
-        const f32x4 t10 = mma<SPLIT, D>(zero4(), A, 16, Bm, 0, lane);
-        const f32x4 t11 = mma<SPLIT, D>(zero4(), A, 16, Bm, 16, lane);
-        store_f32<MASK_STRICT>(labf, LDF, t00, 0, 0, lane);
-        store_f32<MASK_STRICT>(labf, LDF, t10, 16, 0, lane);
-        store_f32<MASK_STRICT>(labf, LDF, t11, 16, 16, lane);
-        for (int e = lane; e < 256; e += 64) labf[(e >> 4) * LDF + 16 + (e & 15)] = 0.f;
-        wave_lds_sync();
         tri_inverse(labf, tf, scr, lane);
         tinv_store<SPLIT>(tf, Tm, true, Tm, false, lane);
         float* out = p.inv + (int64_t)item * C * C;
