@@ -27,6 +27,8 @@
 // Every operand is staged once, in rows; products that need the other
 // orientation read it with the LDS transpose (frag_t).  The outputs are
 // computed transposed, (j, t), so that each lane stores four consecutive j.
+#include <type_traits>
+
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
 
@@ -236,6 +238,11 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     ChunkWalk cw(p, idx, gridDim.x, xcd != 0);
     GradIn<InT> cur, nxt;
     cur.issue_all(p, ChunkSrc(p, cw, true), tid);
+    // The first chunk needs these at once.  Waiting here also leaves nothing
+    // pending on entry to the loop, so the compiler sizes the loop's waits for
+    // the steady state (where the previous chunk's stores are still in flight)
+    // instead of for this entry.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   for (;;) {
     const int head = cw.head, c = cw.c, bb = cw.bb, hh = cw.hh;
@@ -388,56 +395,49 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         using Fr = Frag<SPLIT>;
         const int pr = wave >> 2, tb = (wave >> 1) & 1, jb0 = (wave & 1) * 2;
         const int t = 16 * tb + r16;
-        const M P1 = Pm(0), P2 = Pm(1), P3 = Pm(2), P4 = Pm(3);
         f32x4 ac[2][2];   // [first / second output][j block]
         f32x4 xs[2][2];   // waves 0-3: DY S0 and DSA S0 tiles
-        // t-side fragments are read inside the j-block loop: for the split format the two unrolled
-        // iterations share them; fp32 fragments take twice the registers, so a compiler barrier makes
-        // each iteration read them again instead of keeping them live.
+        // k-step-major: each step reads two j-side and two t-side fragments and advances four
+        // independent accumulators (two outputs x two j blocks).  fp32 fragments take twice the
+        // registers; a compiler barrier between steps keeps only one step's fragments live.
+        auto kstep = [&](f32x4 (&a)[2][2], const Fr& x0, const Fr& x1, const Fr& y0, const Fr& y1, auto ex) {
+            constexpr bool YEX = decltype(ex)::value;
+            a[0][0] = fmma<false, YEX>(a[0][0], x0, y0);
+            a[0][1] = fmma<false, YEX>(a[0][1], x1, y0);
+            a[1][0] = fmma(a[1][0], x0, y1);
+            a[1][1] = fmma(a[1][1], x1, y1);
+            if constexpr (!SPLIT) asm volatile("" ::: "memory");
+        };
+        using exact_t = std::integral_constant<bool, true>;
+        using split_t = std::integral_constant<bool, false>;
+#pragma unroll
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) ac[o][jj] = zero4();
         if (pr == 0) {
+            // aR = S0 DY + Btil P1 + Ktil P2, aA = S0 DSA + Btil P3 + Ktil P4 (j side first)
+            kstep(ac, frag_t(S0m, 16 * jb0, 0, lane), frag_t(S0m, 16 * jb0 + 16, 0, lane),
+                  frag_n(DYm, 16 * tb, 0, lane), frag_n(DSAm, 16 * tb, 0, lane), split_t{});
+            kstep(ac, frag_t(S0m, 16 * jb0, 32, lane), frag_t(S0m, 16 * jb0 + 16, 32, lane),
+                  frag_n(DYm, 16 * tb, 32, lane), frag_n(DSAm, 16 * tb, 32, lane), split_t{});
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                if constexpr (!SPLIT) asm volatile("" ::: "memory");
-                const Fr dy0 = frag_n(DYm, 16 * tb, 0, lane), dy1 = frag_n(DYm, 16 * tb, 32, lane);
-                const Fr ds0 = frag_n(DSAm, 16 * tb, 0, lane), ds1 = frag_n(DSAm, 16 * tb, 32, lane);
-                const Fr p1 = frag_n(P1, 16 * tb, 0, lane), p2 = frag_n(P2, 16 * tb, 0, lane);
-                const Fr p3 = frag_n(P3, 16 * tb, 0, lane), p4 = frag_n(P4, 16 * tb, 0, lane);
-                const int jb = jb0 + jj;
-                const Fr s0a = frag_t(S0m, 16 * jb, 0, lane), s0b = frag_t(S0m, 16 * jb, 32, lane);
-                const Fr bt = frag_t(Bm, 16 * jb, 0, lane), kt = frag_t(Km, 16 * jb, 0, lane);
-                f32x4 aR = fmma(zero4(), s0a, dy0), aA = fmma(zero4(), s0a, ds0);
-                aR = fmma(aR, s0b, dy1);
-                aA = fmma(aA, s0b, ds1);
-                xs[0][jj] = aR;
-                xs[1][jj] = aA;
-                aR = fmma(aR, bt, p1);
-                aA = fmma(aA, bt, p3);
-                aR = fmma(aR, kt, p2);
-                aA = fmma(aA, kt, p4);
-                ac[0][jj] = aR;
-                ac[1][jj] = aA;
-            }
+            for (int o = 0; o < 2; ++o)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) xs[o][jj] = ac[o][jj];
+            kstep(ac, frag_t(Bm, 16 * jb0, 0, lane), frag_t(Bm, 16 * jb0 + 16, 0, lane),
+                  frag_n(Pm(0), 16 * tb, 0, lane), frag_n(Pm(2), 16 * tb, 0, lane), split_t{});
+            kstep(ac, frag_t(Km, 16 * jb0, 0, lane), frag_t(Km, 16 * jb0 + 16, 0, lane),
+                  frag_n(Pm(1), 16 * tb, 0, lane), frag_n(Pm(3), 16 * tb, 0, lane), split_t{});
         } else {
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                if constexpr (!SPLIT) asm volatile("" ::: "memory");
-                const Fr v0 = frag_n(Vm, 16 * tb, 0, lane), v1 = frag_n(Vm, 16 * tb, 32, lane);
-                const Fr u0 = frag_n(Um, 16 * tb, 0, lane), u1 = frag_n(Um, 16 * tb, 32, lane);
-                const Fr p1 = frag_t(P1, 16 * tb, 0, lane), p2 = frag_t(P2, 16 * tb, 0, lane);
-                const Fr p3 = frag_t(P3, 16 * tb, 0, lane), p4 = frag_t(P4, 16 * tb, 0, lane);
-                const int jb = jb0 + jj;
-                const Fr g0 = frag_t(Gem, 16 * jb, 0, lane), g1 = frag_t(Gem, 16 * jb, 32, lane);
-                const Fr at = frag_t(A, 16 * jb, 0, lane), rt = frag_t(R, 16 * jb, 0, lane);
-                f32x4 aK = fmma<false, true>(zero4(), g0, v0), aB = fmma(zero4(), g0, u0);
-                aK = fmma<false, true>(aK, g1, v1);
-                aB = fmma(aB, g1, u1);
-                aK = fmma(aK, at, p4);
-                aB = fmma(aB, at, p3);
-                aK = fmma(aK, rt, p2);
-                aB = fmma(aB, rt, p1);
-                ac[0][jj] = aK;
-                ac[1][jj] = aB;
-            }
+            // aK = Ge' V + Ahat P4^T + Rhat P2^T, aB = Ge' U + Ahat P3^T + Rhat P1^T
+            kstep(ac, frag_t(Gem, 16 * jb0, 0, lane), frag_t(Gem, 16 * jb0 + 16, 0, lane),
+                  frag_n(Vm, 16 * tb, 0, lane), frag_n(Um, 16 * tb, 0, lane), exact_t{});
+            kstep(ac, frag_t(Gem, 16 * jb0, 32, lane), frag_t(Gem, 16 * jb0 + 16, 32, lane),
+                  frag_n(Vm, 16 * tb, 32, lane), frag_n(Um, 16 * tb, 32, lane), exact_t{});
+            kstep(ac, frag_t(A, 16 * jb0, 0, lane), frag_t(A, 16 * jb0 + 16, 0, lane),
+                  frag_t(Pm(3), 16 * tb, 0, lane), frag_t(Pm(2), 16 * tb, 0, lane), split_t{});
+            kstep(ac, frag_t(R, 16 * jb0, 0, lane), frag_t(R, 16 * jb0 + 16, 0, lane),
+                  frag_t(Pm(1), 16 * tb, 0, lane), frag_t(Pm(0), 16 * tb, 0, lane), split_t{});
         }
         const Rsrc r0 = make_rsrc((pr == 0 ? p.dr : p.dk) + tok0, span);
         const Rsrc r1 = make_rsrc((pr == 0 ? p.da : p.db) + tok0, span);
