@@ -161,6 +161,97 @@ def cpu_baseline(wl, budget_s: float) -> dict:
                       f"{reps} pass(es) in {el:.1f} s; tokens scaled by {H}/{wl.H} heads"}
 
 
+STEP_METRIC = "WKV7 recurrent step tokens/s and % HBM peak, 32 layers x B256 T1 H64 D64 (1 MI355X)"
+
+
+def step_bytes(wl, in_bytes: int) -> int:
+    """Bytes one layer call of the one-token step must move: the state read and
+    written once (in place), six input rows read, y written."""
+    heads = wl.B * wl.H
+    return 2 * heads * D * D * 4 + 6 * heads * D * in_bytes + heads * D * 4
+
+
+def bench_step(args, wl) -> int:
+    """The one-token recurrent step (forward only): one call per layer, each
+    updating that layer's (B,H,64,64) fp32 state in place.  A step is all
+    layers; tokens/s counts the B sequences' tokens per step."""
+    import torch
+    import linear_rnn_lm_amd as L
+    from linear_rnn_lm_amd.inputs import make_inputs
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    in_bytes = 2 if wl.dtype == torch.bfloat16 else 4
+    layers = []
+    gen = torch.Generator(device=dev)
+    for layer in range(wl.layers):
+        x = make_inputs(wl.B, 1, wl.H, wl.dtype, wl.seed + layer, with_h0=False)
+        gen.manual_seed(wl.seed + layer)
+        # the states: N(0, 0.1), drawn on the device (8.6 GB for 32 layers)
+        state = torch.randn(wl.B, wl.H, D, D, generator=gen, device=dev, dtype=torch.float32) * 0.1
+        layers.append(([t.to(dev) for t in x.tensors()], state,
+                       torch.empty(wl.B, 1, wl.H, D, device=dev, dtype=torch.float32)))
+    lib = L.lib()
+    code = 1 if wl.dtype == torch.bfloat16 else 0
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    calls = [([t.data_ptr() for t in ins], st.data_ptr(), y.data_ptr()) for ins, st, y in layers]
+
+    def call(c):
+        p, ps, py = c
+        st = lib.wkv7_fwd(wl.B, 1, wl.H, D, code, *p, ps, py, None, ps, None, 0, sh)
+        assert st == 0, lib.wkv7_status_str(st)
+
+    def step():
+        for c in calls:
+            call(c)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    # per-launch duration of the layer kernel, from events around each call
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+    launch_ms = []
+    for _ in range(args.steps):
+        evs[0].record(stream)
+        for i, c in enumerate(calls):
+            call(c)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        launch_ms += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(calls))]
+    per_launch_ms = sum(launch_ms) / len(launch_ms)
+    kb = step_bytes(wl, in_bytes)
+    achieved = kb / (per_launch_ms * 1e-3) / 1e9
+    out = {
+        "metric": STEP_METRIC,
+        "value": wl.B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.description}", "B": wl.B, "T": 1, "H": wl.H, "D": D,
+                   "layers": wl.layers, "in_dtype": "bf16" if in_bytes == 2 else "f32", "state_dtype": "f32"},
+        "layer_tokens_per_s": wl.B * wl.layers / (ms_per_step * 1e-3),
+        "kernel_ms": {"fwd_sequential": per_launch_ms},
+        "roofline": {"kernel": "fwd_sequential", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,9 +291,7 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(torch.device("cuda:0"))
     if wl.T == 1:
-        print("bench.py: the one-token recurrent-step workload is measured by its own benchmark "
-              "(forward only); pick a training workload", file=sys.stderr)
-        return 2
+        return bench_step(args, wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = workload_inputs(wl)
