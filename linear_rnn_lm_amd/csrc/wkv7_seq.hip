@@ -88,10 +88,82 @@ __global__ __launch_bounds__(SEQ_NT) void fwd_sequential_kernel(FwdArgs p) {
     }
 }
 
+// Sum over the 16 lanes of a DPP row, the same value in every lane: a butterfly
+// of lane pairs l ^ 1, l ^ 2 (quad permutes), l ^ 7 (half-row mirror) and
+// l ^ 15 (row mirror); each step adds a pair in both lanes, so the lanes agree.
+__device__ __forceinline__ float row16_allsum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));  // row_mirror
+    return x;
+}
+
+template <typename InT>
+__device__ __forceinline__ f32x4 load4(const InT* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+template <>
+__device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                 __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
+
+// One token (T = 1), the recurrent step: the same update as above, with the
+// state accessed as one contiguous 16 KiB block per head.  Thread tid holds
+// the four 4-column pieces at flat offsets 1024 q + 4 tid of the head's state:
+// rows tid / 16 + 16 q, columns 4 (tid % 16) .. + 3.  The 16 threads of a row
+// are one DPP row, so the row dot products need no LDS.
+template <typename InT>
+__global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
+    const int tid = threadIdx.x;
+    const int head = blockIdx.x;
+    const int bb = head / p.H, hh = head % p.H;
+    const int64_t base = ((int64_t)bb * p.H + hh) * D;      // this head's token row (T = 1)
+    const int c0 = 4 * (tid & 15), r0 = tid >> 4;
+    const int64_t hoff = (int64_t)head * D * D + 4 * tid;
+    f32x4 st[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st[q] = p.h0 ? *reinterpret_cast<const f32x4*>(p.h0 + hoff + 1024 * q) : zero4();
+    if (p.ckpt) {   // checkpoint 0: the state entering the (only) chunk
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(p.ckpt + hoff + 1024 * q) = st[q];
+    }
+    const f32x4 w = load4(static_cast<const InT*>(p.w) + base + c0), k = load4(static_cast<const InT*>(p.k) + base + c0);
+    const f32x4 a = load4(static_cast<const InT*>(p.a) + base + c0), b = load4(static_cast<const InT*>(p.b) + base + c0);
+    const f32x4 r = load4(static_cast<const InT*>(p.r) + base + c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float vi = load1(static_cast<const InT*>(p.v) + base + r0 + 16 * q);
+        float sa = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sa = fmaf(st[q][c], a[c], sa);
+        sa = row16_allsum(sa);
+        float y = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            st[q][c] = fmaf(w[c], st[q][c], fmaf(vi, k[c], sa * b[c]));
+            y = fmaf(st[q][c], r[c], y);
+        }
+        y = row16_allsum(y);
+        if (p.y && (tid & 15) == 0) p.y[base + r0 + 16 * q] = y;
+    }
+    if (p.hT) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(p.hT + hoff + 1024 * q) = st[q];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, hipStream_t s) {
     const int heads = a.B * a.H;
+    if (a.T == 1) {   // the recurrent step: coalesced state access
+        if (bf16) hipLaunchKernelGGL(step_kernel<uint16_t>, dim3(heads), dim3(SEQ_NT), 0, s, a);
+        else hipLaunchKernelGGL(step_kernel<float>, dim3(heads), dim3(SEQ_NT), 0, s, a);
+        return hipGetLastError();
+    }
     if (bf16) hipLaunchKernelGGL(fwd_sequential_kernel<uint16_t>, dim3(heads), dim3(SEQ_NT), 0, s, a);
     else hipLaunchKernelGGL(fwd_sequential_kernel<float>, dim3(heads), dim3(SEQ_NT), 0, s, a);
     return hipGetLastError();
