@@ -125,7 +125,8 @@ __global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
     const int64_t hoff = (int64_t)head * D * D + 4 * tid;
     f32x4 st[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st[q] = p.h0 ? *reinterpret_cast<const f32x4*>(p.h0 + hoff + 1024 * q) : zero4();
+    for (int q = 0; q < 4; ++q)   // streamed once: non-temporal
+        st[q] = p.h0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.h0 + hoff + 1024 * q)) : zero4();
     if (p.ckpt) {   // checkpoint 0: the state entering the (only) chunk
 #pragma unroll
         for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(p.ckpt + hoff + 1024 * q) = st[q];
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
     }
     if (p.hT) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(p.hT + hoff + 1024 * q) = st[q];
+        for (int q = 0; q < 4; ++q) __builtin_nontemporal_store(st[q], reinterpret_cast<f32x4*>(p.hT + hoff + 1024 * q));
     }
 }
 
