@@ -657,16 +657,24 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 // hardware needs before they are overwritten.  (Stores with a register
 // scalar offset lost the last dword of the data to the next instruction's
 // write of that register.)
+//
+// CP selects the cache policy: kCached for data the next kernel reads back
+// (checkpoints, state gradients), kStream (non-temporal) for outputs that
+// leave the library.
+constexpr int kCached = 0, kStream = 2;
+template <int CP = kCached>
 __device__ __forceinline__ void bstore(float v, Rsrc r, int voff, int soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff + soff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff + soff, 0, CP);
 }
+template <int CP = kCached>
 __device__ __forceinline__ void bstore2(float2 v, Rsrc r, int voff, int soff) {
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff + soff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff + soff, 0, CP);
 }
+template <int CP = kCached>
 __device__ __forceinline__ void bstore4(f32x4 v, Rsrc r, int voff, int soff) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff + soff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff + soff, 0, CP);
 }
 
 // ---------------------------------------------------------------------------

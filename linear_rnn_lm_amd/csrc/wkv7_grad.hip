@@ -453,8 +453,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
                 // dr = gamma_t aR, da = gamma_{t-1} aA; r dr = Rhat aR, a da = Ahat aA
                 const f32x4 gpl = *reinterpret_cast<const f32x4*>(gam + tp * LDG + j0);
                 const f32x4 gp = t > 0 ? gpl : f32x4{1.f, 1.f, 1.f, 1.f};
-                bstore4(ac[0][jj] * g, r0, voff, soff_);
-                bstore4(ac[1][jj] * gp, r1, voff, soff_);
+                bstore4<kStream>(ac[0][jj] * g, r0, voff, soff_);
+                bstore4<kStream>(ac[1][jj] * gp, r1, voff, soff_);
                 const f32x4 ah = get4(A, t, j0), rh = get4(R, t, j0);
                 const f32x4 fa = ah * ac[1][jj];
                 evr[jj] = -(rh * ac[0][jj]) - fa;
@@ -469,8 +469,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
                 f32x4 ig;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) ig[q] = rcp(g[q]);
-                bstore4(ac[0][jj] * ig, r0, voff, soff_);
-                bstore4(ac[1][jj] * ig, r1, voff, soff_);
+                bstore4<kStream>(ac[0][jj] * ig, r0, voff, soff_);
+                bstore4<kStream>(ac[1][jj] * ig, r1, voff, soff_);
                 *reinterpret_cast<f32x4*>(hh_ + t * LDG + j0) =
                     get4(Km, t, j0) * ac[0][jj] + get4(Bm, t, j0) * ac[1][jj];
             }
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         for (int tt = 0; tt < TPG; ++tt) {
             const int t = q * TPG + tt;
             const float2 wv = Pair<InT>::f(cur.raw.w[tt]);
-            bstore2(make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y)), rdw,
+            bstore2<kStream>(make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y)), rdw,
                     (t * HD + j0) * 4, t0 * HD * 4);
             acc.x += hx[tt].x;
             acc.y += hx[tt].y;

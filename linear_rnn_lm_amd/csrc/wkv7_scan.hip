@@ -355,7 +355,7 @@ __device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * 4;
-        bstore4(*reinterpret_cast<const f32x4*>(ob + t * LDO + e0), r, (t * HD + e0) * 4, c * C * HD * 4);
+        bstore4<kStream>(*reinterpret_cast<const f32x4*>(ob + t * LDO + e0), r, (t * HD + e0) * 4, c * C * HD * 4);
     }
 }
 
