@@ -307,23 +307,27 @@ struct ScanLds {
 };
 
 // The token rows of one chunk for a workgroup's NI columns, memory ->
-// registers -> LDS.  Memory thread ct moves 16-byte pieces ct + NTC * u:
-// piece -> (token t, NPR pieces per token row).  Tokens past the end of the
-// sequence read as 0 (buffer resource ending at the head's last token).
-template <typename XT, bool SPLIT, int NWV>
+// registers -> LDS.  Memory thread ct of NT moves the 16-byte pieces
+// (ct + NT * u) mod NPC: piece -> (token t, NPR pieces per token row).  With
+// fewer pieces than threads, two threads move the same piece to the same
+// place.  Tokens past the end of the sequence read as 0 (buffer resource
+// ending at the head's last token).
+template <typename XT, bool SPLIT, int NWV, int NT>
 struct XCopy {
-    static constexpr int NI = 16 * NWV, NTC = 64 * NWV;
+    static constexpr int NI = 16 * NWV;
     static constexpr int EPP = 16 / (int)sizeof(XT);            // elements per piece
     static constexpr int NPR = NI / EPP;                        // pieces per token row
-    static constexpr int PER = C * NPR / NTC;
-    static_assert(C * NPR % NTC == 0 && PER >= 1, "token row split");
+    static constexpr int NPC = C * NPR;                         // pieces per chunk
+    static constexpr int PER = NPC >= NT ? NPC / NT : 1;
+    static_assert(NPC % NT == 0 || NT % NPC == 0, "token row split");
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     u32x4 v[PER];
 
+    static __device__ __forceinline__ int piece(int ct, int u) { return (ct + NT * u) % NPC; }
     __device__ __forceinline__ void load(Rsrc r, int c, int HD, int ct) {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * EPP;
+            const int pc = piece(ct, u), t = pc / NPR, e0 = (pc % NPR) * EPP;
             v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  r, (t * HD + e0 + c * C * HD) * (int)sizeof(XT), 0, 0));
         }
@@ -332,7 +336,7 @@ struct XCopy {
     __device__ __forceinline__ void store(Mat<SPLIT> X, int ct) const {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * EPP;
+            const int pc = piece(ct, u), t = pc / NPR, e0 = (pc % NPR) * EPP;
             if constexpr (sizeof(XT) == 2) {
                 *reinterpret_cast<u32x4*>(reinterpret_cast<__bf16*>(X.p) + t * X.ld + e0) = v[u];
             } else {
@@ -348,13 +352,14 @@ struct XCopy {
 };
 
 // Memory waves store one chunk's output rows (fp32, rows t, NI columns)
-// from LDS: 16 bytes per piece.
-template <int NWV>
+// from LDS: 16 bytes per piece, NT threads.
+template <int NWV, int NT>
 __device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD, int ct) {
-    constexpr int NI = 16 * NWV, NTC = 64 * NWV, NPR = NI / 4, PER = C * NPR / NTC, LDO = NI + 4;
+    constexpr int NI = 16 * NWV, NPR = NI / 4, PER = C * NPR / NT, LDO = NI + 4;
+    static_assert(C * NPR % NT == 0 && PER >= 1, "output row split");
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int pc = ct + NTC * u, t = pc / NPR, e0 = (pc % NPR) * 4;
+        const int pc = ct + NT * u, t = pc / NPR, e0 = (pc % NPR) * 4;
         bstore4<kStream>(*reinterpret_cast<const f32x4*>(ob + t * LDO + e0), r, (t * HD + e0) * 4, c * C * HD * 4);
     }
 }
@@ -362,7 +367,7 @@ __device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD
 // BWD = false: forward over v (InT), S from h0 -> y, checkpoints, hT.
 // BWD = true : backward over dy (fp32), G from dhT -> dv, dh_ckpt, dh0.
 //
-// A workgroup has NWV compute waves (16 state rows each) and NWV memory
+// A workgroup has NWV compute waves (16 state rows each) and NMW memory
 // waves.  The memory waves do all the streaming: the operand block and the
 // token rows of chunk it + 1 into LDS while chunk it is computed (loaded two
 // chunks ahead into two register sets), and the output rows of chunk it - 1
@@ -372,9 +377,9 @@ __device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD
 // past the end of a ragged last chunk read as 0 and their stores are
 // dropped by the hardware, so no branch surrounds a memory access inside the
 // chunk loop.
-template <typename InT, bool SPLIT, int NWV, bool BWD>
-__global__ __launch_bounds__(128 * NWV) void scan_kernel(ScanArgs p, int xcd) {
-    constexpr int NSUB = 4 / NWV, NTC = 64 * NWV;
+template <typename InT, bool SPLIT, int NWV, int NMW, bool BWD>
+__global__ __launch_bounds__(64 * (NWV + NMW)) void scan_kernel(ScanArgs p, int xcd) {
+    constexpr int NSUB = 4 / NWV, NTC = 64 * NWV, NTM = 64 * NMW;
     using XT = typename std::conditional<BWD, float, InT>::type;
     using I = OpsImage<SPLIT>;
     using L = ScanLds<SPLIT, NWV>;
@@ -403,21 +408,21 @@ __global__ __launch_bounds__(128 * NWV) void scan_kernel(ScanArgs p, int xcd) {
         const Rsrc rx = make_rsrc(static_cast<const XT*>(p.x) + tok0 + i0, head_span * sizeof(XT));
         const Rsrc ro = make_rsrc(p.out ? p.out + tok0 + i0 : nullptr, p.out ? head_span * 4 : 0);
         const Rsrc rnull = make_rsrc(nullptr, 0);
-        OpsCopy<SPLIT, NTC> oa, ob;
-        XCopy<XT, SPLIT, NWV> xa, xb;
+        OpsCopy<SPLIT, NTM> oa, ob;
+        XCopy<XT, SPLIT, NWV, NTM> xa, xb;
         oa.init(ct);
         ob.init(ct);
-        auto fetch = [&](OpsCopy<SPLIT, NTC>& o, XCopy<XT, SPLIT, NWV>& x, int it) {
+        auto fetch = [&](OpsCopy<SPLIT, NTM>& o, XCopy<XT, SPLIT, NWV, NTM>& x, int it) {
             o.load(ops_of(it), ct);
             x.load(rx, chunk_of(min(it, NC - 1)), HD, ct);
         };
-        auto put = [&](const OpsCopy<SPLIT, NTC>& o, const XCopy<XT, SPLIT, NWV>& x, int it) {
+        auto put = [&](const OpsCopy<SPLIT, NTM>& o, const XCopy<XT, SPLIT, NWV, NTM>& x, int it) {
             o.store(smem + (it & 1) * L::OPS);
             x.store(xmat(it), ct);
         };
         // outputs of iteration it - 1 (nothing before the first)
         auto out = [&](int it) {
-            store_out<NWV>(obuf(it - 1), it > 0 ? ro : rnull, chunk_of(max(it - 1, 0)), HD, ct);
+            store_out<NWV, NTM>(obuf(it - 1), it > 0 ? ro : rnull, chunk_of(max(it - 1, 0)), HD, ct);
         };
         fetch(oa, xa, 0);
         put(oa, xa, 0);
@@ -547,10 +552,10 @@ hipError_t launch_prepare_typed(const PrepArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename InT, bool SPLIT, int NWV, bool BWD>
+template <typename InT, bool SPLIT, int NWV, int NMW, bool BWD>
 hipError_t launch_scan_typed(const ScanArgs& a, hipStream_t s) {
     constexpr int smem_bytes = ScanLds<SPLIT, NWV>::total;
-    auto kern = scan_kernel<InT, SPLIT, NWV, BWD>;
+    auto kern = scan_kernel<InT, SPLIT, NWV, NMW, BWD>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = set_smem(kern, smem_bytes);
@@ -559,15 +564,15 @@ hipError_t launch_scan_typed(const ScanArgs& a, hipStream_t s) {
     }
     const int heads = a.B * a.H;
     const bool xcd = heads % 8 == 0;
-    hipLaunchKernelGGL(kern, dim3(heads * (4 / NWV)), dim3(128 * NWV), smem_bytes, s, a, xcd ? 1 : 0);
+    hipLaunchKernelGGL(kern, dim3(heads * (4 / NWV)), dim3(64 * (NWV + NMW)), smem_bytes, s, a, xcd ? 1 : 0);
     return hipGetLastError();
 }
 
 template <typename InT, bool SPLIT, bool BWD>
 hipError_t launch_scan_nwv(const ScanArgs& a, hipStream_t s) {
     // Fewer heads than CUs: spread each head's 4 waves over 2 workgroups.
-    if (a.B * a.H <= 128) return launch_scan_typed<InT, SPLIT, 2, BWD>(a, s);
-    return launch_scan_typed<InT, SPLIT, 4, BWD>(a, s);
+    if (a.B * a.H <= 128) return launch_scan_typed<InT, SPLIT, 2, 4, BWD>(a, s);
+    return launch_scan_typed<InT, SPLIT, 4, 4, BWD>(a, s);
 }
 
 }  // namespace
