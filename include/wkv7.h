@@ -61,7 +61,10 @@ extern "C" {
 typedef enum {
     WKV7_OK = 0,
     WKV7_ERR_ARG = 1,       /* NULL where a pointer is required, bad enum   */
-    WKV7_ERR_SHAPE = 2,     /* D != 64, B/T/H < 1, sizes overflowing int64  */
+    WKV7_ERR_SHAPE = 2,     /* D != 64, B/T/H < 1, sizes overflowing int64,
+                               or B*T*H*D*4 > 0xFFFFFF00: token tensors are
+                               addressed with 32-bit byte offsets (at D = 64,
+                               B*T*H below 2^24); split larger batches      */
     WKV7_ERR_DTYPE = 3,     /* in_dtype not a wkv7_dtype                    */
     WKV7_ERR_ALIGN = 4,     /* a pointer not 16-byte aligned                */
     WKV7_ERR_ALIAS = 5,     /* an output overlaps an input or another output */

@@ -39,6 +39,8 @@ wkv7_status check_shape(int B, int T, int H, int D, Sizes* sz) {
     const int64_t tok = heads * (int64_t)T * kD;
     if (tok / T != heads * kD) return WKV7_ERR_SHAPE;
     if (tok > (INT64_MAX / 8)) return WKV7_ERR_SHAPE;
+    // every token tensor, taken as fp32, is addressed with 32-bit byte offsets
+    if (tok * 4 > (int64_t)wkv7::kMaxTensorBytes) return WKV7_ERR_SHAPE;
     sz->heads = heads;
     sz->nc = nc;
     sz->tok_elems = tok;

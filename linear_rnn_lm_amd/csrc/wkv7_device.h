@@ -66,6 +66,19 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Sum over the lanes l, l ^ 8, l ^ 16, ..., l ^ 56 (the eight lanes with equal
+// l % 8), returned in all of them; VALU only.  The rotation by 8 inside a row
+// of 16 pairs lane l with l ^ 8.  permlane16_swap(x, x) returns rows
+// (x0, x0, x2, x2) and (x1, x1, x3, x3), whose sum pairs each row with its
+// neighbour; permlane32_swap does the same for the two halves of the wave.
+__device__ __forceinline__ float sum_stride8(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(w[0]) + __uint_as_float(w[1]);
+}
+
 // 1/x with v_rcp_f32 (at most 1 ulp off).
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 

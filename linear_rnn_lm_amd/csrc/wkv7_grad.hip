@@ -117,10 +117,16 @@ struct ChunkWalk {
     }
 };
 
+// Byte offset of element e of a token tensor (below 4 GiB, so unsigned 32 bit).
+__device__ __forceinline__ int tok_bytes(int e, int es) { return (int)((uint32_t)e * (uint32_t)es); }
+
 // Where one chunk's inputs live.  `on == false` (no next chunk) gives every
 // buffer resource size 0, so the loads return zeros without touching memory.
+// Token tensors (B, T, H, D) are addressed whole, with 32-bit byte offsets
+// (the entry points keep them below 4 GiB): one scalar per chunk, tokc, and a
+// per-lane part that does not change from chunk to chunk.
 struct ChunkSrc {
-    int64_t tok0;   // element offset of the head's token 0
+    int tokc;       // element offset of the chunk's first token (head bb, hh)
     int64_t cs;     // element offset of the chunk's D x D state blocks
     int64_t ci;     // element offset of the chunk's C x C inverse
     int t0, cc;     // first token, tokens in the chunk
@@ -129,7 +135,7 @@ struct ChunkSrc {
 
     __device__ __forceinline__ ChunkSrc(const BwdArgs& p, const ChunkWalk& w, bool on_) {
         const int HD = p.H * D;
-        tok0 = (int64_t)w.bb * p.T * HD + (int64_t)w.hh * D;
+        tokc = (w.bb * p.T + w.c * C) * HD + w.hh * D;
         cs = ((int64_t)w.head * p.NC + w.c) * D * D;
         ci = ((int64_t)w.head * p.NC + w.c) * C * C;
         t0 = w.c * C;
@@ -166,9 +172,10 @@ struct GradIn {
     static __device__ __forceinline__ f32x4 ld4(Rsrc r, int off) {
         return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     }
+    // A whole token tensor.  Tokens past the head's end in a ragged last chunk
+    // read the next head's rows (or 0 past the tensor); the consumers mask them.
     static __device__ __forceinline__ Rsrc tok(const void* base, const BwdArgs& p, const ChunkSrc& s, int es) {
-        const uint32_t span = s.on ? (uint32_t)(((int64_t)(p.T - 1) * p.H * D + D) * es) : 0u;
-        return make_rsrc(static_cast<const char*>(base) + s.tok0 * es, span);
+        return make_rsrc(base, s.on ? (uint32_t)p.B * (uint32_t)(p.T * p.H * D * es) : 0u);
     }
     // w, a, r, b, k: columns 2 jp, 2 jp + 1 of tokens q TPG + tt
     __device__ __forceinline__ void raw_part(W* dst, const void* src, const BwdArgs& p, const ChunkSrc& s, int tid) {
@@ -176,7 +183,7 @@ struct GradIn {
         const Rsrc r = tok(src, p, s, ES);
         const int jp = tid & 31, q = tid >> 5, HD = p.H * D;
 #pragma unroll
-        for (int tt = 0; tt < TPG; ++tt) dst[tt] = ld<W>(r, ((s.t0 + q * TPG + tt) * HD + 2 * jp) * ES);
+        for (int tt = 0; tt < TPG; ++tt) dst[tt] = ld<W>(r, tok_bytes(s.tokc + (q * TPG + tt) * HD + 2 * jp, ES));
     }
     template <int PART>
     __device__ __forceinline__ void issue(const BwdArgs& p, const ChunkSrc& s, int tid) {
@@ -194,12 +201,12 @@ struct GradIn {
             const Rsrc r = tok(p.v, p, s, ES);
             const int ip = tid % RC::PAIRS, t1 = tid / RC::PAIRS, HD = p.H * D;
 #pragma unroll
-            for (int u = 0; u < RC::PER; ++u) rv.v[u] = ld<W>(r, ((s.t0 + t1 + u * RC::TSTEP) * HD + 2 * ip) * ES);
+            for (int u = 0; u < RC::PER; ++u) rv.v[u] = ld<W>(r, tok_bytes(s.tokc + (t1 + u * RC::TSTEP) * HD + 2 * ip, ES));
         } else if constexpr (PART == 2) {
             const Rsrc r = tok(p.dy, p, s, 4);
             const int ip = tid % RC::PAIRS, t1 = tid / RC::PAIRS, HD = p.H * D;
 #pragma unroll
-            for (int u = 0; u < RC::PER; ++u) rdy.v[u] = ld<float2>(r, ((s.t0 + t1 + u * RC::TSTEP) * HD + 2 * ip) * 4);
+            for (int u = 0; u < RC::PER; ++u) rdy.v[u] = ld<float2>(r, tok_bytes(s.tokc + (t1 + u * RC::TSTEP) * HD + 2 * ip, 4));
             tv = ld<float2>(make_rsrc(p.inv + s.ci, s.on ? C * C * 4 : 0u), tid * 8);
         } else if constexpr (PART == 3) {
             const Rsrc r = make_rsrc(p.ckpt + s.cs, sbytes);
@@ -230,7 +237,6 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int r16 = lane & 15, g4 = lane >> 4;
     const int HD = p.H * D;
-    const uint32_t span = (uint32_t)(((int64_t)(p.T - 1) * HD + D) * 4);
     // state-sized inputs: thread holds row si = tid / 8, columns sj0 .. sj0 + 7
     const int si = tid >> 3, sj0 = (tid & 7) * 8;
 
@@ -252,9 +258,12 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     nw.advance();
     const ChunkSrc nsrc(p, nw, more);
     nxt.template issue<0>(p, nsrc, tid);
-    const int t0 = c * C;
-    // the head's tokens: outputs past the sequence's end are dropped
-    const int64_t tok0 = (int64_t)bb * p.T * HD + (int64_t)hh * D;
+    const int t0 = c * C, cc = min(C, p.T - t0);
+    // fp32 outputs: whole tensors; a token past the sequence's end gets an
+    // offset beyond every tensor, so the hardware drops its store
+    const int tokc = (bb * p.T + t0) * HD + hh * D;
+    const uint32_t out_bytes = (uint32_t)p.B * (uint32_t)(p.T * HD * 4);
+    auto out_off = [&](int t, int j) { return t < cc ? tok_bytes(tokc + t * HD + j, 4) : (int)kDropOffset; };
 
     // ---- phase 0: gamma and the scaled rows
     const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
@@ -307,12 +316,9 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     {   // sum_i G'[i][j] S0[i][j] over this wave's 8 rows (lanes with equal tid % 8 share columns)
         f32x4 d0 = cur.gev[0] * cur.s0v[0], d1 = cur.gev[1] * cur.s0v[1];
 #pragma unroll
-        for (int m = 8; m < 64; m <<= 1) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                d0[e] += __shfl_xor(d0[e], m);
-                d1[e] += __shfl_xor(d1[e], m);
-            }
+        for (int e = 0; e < 4; ++e) {
+            d0[e] = sum_stride8(d0[e]);
+            d1[e] = sum_stride8(d1[e]);
         }
         if (lane < 8) {
             *reinterpret_cast<f32x4*>(red + wave * 64 + sj0) = d0;
@@ -439,22 +445,21 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
             kstep(ac, frag_t(R, 16 * jb0, 0, lane), frag_t(R, 16 * jb0 + 16, 0, lane),
                   frag_t(Pm(1), 16 * tb, 0, lane), frag_t(Pm(0), 16 * tb, 0, lane), split_t{});
         }
-        const Rsrc r0 = make_rsrc((pr == 0 ? p.dr : p.dk) + tok0, span);
-        const Rsrc r1 = make_rsrc((pr == 0 ? p.da : p.db) + tok0, span);
-        const int soff_ = t0 * HD * 4;
+        const Rsrc r0 = make_rsrc(pr == 0 ? p.dr : p.dk, out_bytes);
+        const Rsrc r1 = make_rsrc(pr == 0 ? p.da : p.db, out_bytes);
         const int tp = t > 0 ? t - 1 : 0;
         f32x4 evr[2];   // waves 0-3: -r dr - a da, added to hh_ after the barrier
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j0 = 16 * (jb0 + jj) + 4 * g4;
-            const int voff = (t * HD + j0) * 4;
+            const int voff = out_off(t, j0);
             const f32x4 g = *reinterpret_cast<const f32x4*>(gam + t * LDG + j0);
+            f32x4 sc0, sc1;   // output scales
             if (pr == 0) {
                 // dr = gamma_t aR, da = gamma_{t-1} aA; r dr = Rhat aR, a da = Ahat aA
                 const f32x4 gpl = *reinterpret_cast<const f32x4*>(gam + tp * LDG + j0);
-                const f32x4 gp = t > 0 ? gpl : f32x4{1.f, 1.f, 1.f, 1.f};
-                bstore4<kStream>(ac[0][jj] * g, r0, voff, soff_);
-                bstore4<kStream>(ac[1][jj] * gp, r1, voff, soff_);
+                sc0 = g;
+                sc1 = t > 0 ? gpl : f32x4{1.f, 1.f, 1.f, 1.f};
                 const f32x4 ah = get4(A, t, j0), rh = get4(R, t, j0);
                 const f32x4 fa = ah * ac[1][jj];
                 evr[jj] = -(rh * ac[0][jj]) - fa;
@@ -466,14 +471,16 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
                 if (r16 == 15) *reinterpret_cast<f32x4*>(red + (8 + tb) * 64 + j0) = dg;
             } else {
                 // dk = aK / gamma_t, db = aB / gamma_t; k dk = Ktil aK, b db = Btil aB
-                f32x4 ig;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) ig[q] = rcp(g[q]);
-                bstore4<kStream>(ac[0][jj] * ig, r0, voff, soff_);
-                bstore4<kStream>(ac[1][jj] * ig, r1, voff, soff_);
+                for (int q = 0; q < 4; ++q) sc0[q] = rcp(g[q]);
+                sc1 = sc0;
                 *reinterpret_cast<f32x4*>(hh_ + t * LDG + j0) =
                     get4(Km, t, j0) * ac[0][jj] + get4(Bm, t, j0) * ac[1][jj];
             }
+            // outside the branch: every wave issues the same stores, so the
+            // compiler counts this chunk's outstanding stores exactly
+            bstore4<kStream>(ac[0][jj] * sc0, r0, voff, 0);
+            bstore4<kStream>(ac[1][jj] * sc1, r1, voff, 0);
         }
         lds_barrier();
         if (pr == 0) {
@@ -516,17 +523,22 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
             acc.x += q2 < q ? v.x : 0.f;
             acc.y += q2 < q ? v.y : 0.f;
         }
-        const Rsrc rdw = make_rsrc(p.dw + tok0, span);   // tokens past the end are dropped
+        const Rsrc rdw = make_rsrc(p.dw, out_bytes);
 #pragma unroll
         for (int tt = 0; tt < TPG; ++tt) {
             const int t = q * TPG + tt;
             const float2 wv = Pair<InT>::f(cur.raw.w[tt]);
             bstore2<kStream>(make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y)), rdw,
-                    (t * HD + j0) * 4, t0 * HD * 4);
+                             out_off(t, j0), 0);
             acc.x += hx[tt].x;
             acc.y += hx[tt].y;
         }
     }
+    // The next chunk's loads (issued in phases 0-4) are all back by now; wait
+    // for them here, leaving only this chunk's six output stores in flight.
+    // Otherwise the compiler's count for their first uses (merged over the
+    // loop's back edge) would also wait for those stores to complete.
+    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
     if (!more) break;
     cur = nxt;
     idx = nidx;

@@ -29,6 +29,13 @@ struct BwdArgs {
     int B, T, H, NC;
 };
 
+// Token tensors (B, T, H, D) are addressed with 32-bit byte offsets: the entry
+// points reject shapes whose fp32 token tensors exceed kMaxTensorBytes, and a
+// store at kDropOffset lies past every tensor, so the buffer range check drops
+// it (with room for a 16-byte access before the offset would wrap).
+constexpr uint32_t kMaxTensorBytes = 0xFFFFFF00u;
+constexpr uint32_t kDropOffset = 0xFFFFFF00u;
+
 // Bytes of one chunk's transition operands P, M, E, F (the same for both
 // storage formats: two bf16 planes or one fp32 plane).
 constexpr int kOpsBytes = 36864;

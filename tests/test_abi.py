@@ -103,6 +103,7 @@ def test_fwd_rejects_bad_arguments(fn):
     assert c(T=0) == ERR_SHAPE
     assert c(B=0) == ERR_SHAPE
     assert c(H=-1) == ERR_SHAPE
+    assert c(T=1 << 20, H=16) == ERR_SHAPE           # a 4 GiB fp32 token tensor
     assert c(dt=7) == ERR_DTYPE
     assert c(v=None) == ERR_ARG
     assert c(y=None, ck=None, hT=None) == ERR_ARG
@@ -191,6 +192,8 @@ def test_bwd_rejects_bad_arguments():
 
     assert c(D=16) == ERR_SHAPE
     assert c(T=0) == ERR_SHAPE
+    assert c(T=1 << 24) == ERR_SHAPE                  # token tensors past 4 GiB (fp32)
+    assert cs(T=1 << 24) == ERR_SHAPE
     assert c(dt=2) == ERR_DTYPE
     assert c(dy=None) == ERR_ARG
     assert c(ck=None) == ERR_ARG
