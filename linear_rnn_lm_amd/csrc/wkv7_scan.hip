@@ -293,7 +293,7 @@ struct OpsCopy {
 
 // LDS plan of the scan: double buffers of one chunk's operands, of its
 // token rows (v exact, or dy split) and of its output rows (y or dv, fp32).
-template <bool SPLIT, int NWV>
+template <bool SPLIT, int NWV, int NCW>
 struct ScanLds {
     using F = Fmt<SPLIT>;
     static constexpr int NI = 16 * NWV;                 // state rows of the workgroup
@@ -301,8 +301,11 @@ struct ScanLds {
     static constexpr int XB = F::bytes(C, NI);          // rows (t, i)
     static constexpr int LDO = NI + 4;                  // fp32 output row stride
     static constexpr int OB = C * LDO * 4;
-    static constexpr int X0 = 2 * OPS, O0 = X0 + 2 * XB;
-    static constexpr int total = O0 + 2 * OB;
+    // state halves passed between the two waves of a row block (two column
+    // tiles, 16 bytes per lane each), double-buffered by chunk parity
+    static constexpr int XW = NCW > NWV ? 2 * 64 * 16 : 0;
+    static constexpr int X0 = 2 * OPS, O0 = X0 + 2 * XB, W0 = O0 + 2 * OB;
+    static constexpr int total = W0 + 2 * NCW * XW;
     static_assert(total <= 160 * 1024, "scan LDS");
 };
 
@@ -367,8 +370,12 @@ __device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD
 // BWD = false: forward over v (InT), S from h0 -> y, checkpoints, hT.
 // BWD = true : backward over dy (fp32), G from dhT -> dv, dh_ckpt, dh0.
 //
-// A workgroup has NWV compute waves (16 state rows each) and NMW memory
-// waves.  The memory waves do all the streaming: the operand block and the
+// A workgroup has NCW compute waves and NMW memory waves.  Its NWV row
+// blocks of 16 state rows go to one compute wave each (NCW = NWV) or to two
+// (NCW = 2 NWV): then wave h of a block forms the new state's column tiles
+// 2h, 2h + 1 and the output rows of token block h, and the two waves swap
+// their new tiles through LDS at the chunk's end.  The products of a chunk
+// read the whole previous state, so each wave keeps all four tiles.  The memory waves do all the streaming: the operand block and the
 // token rows of chunk it + 1 into LDS while chunk it is computed (loaded two
 // chunks ahead into two register sets), and the output rows of chunk it - 1
 // from LDS to memory.  The compute waves read LDS, run the products and
@@ -377,16 +384,18 @@ __device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD
 // past the end of a ragged last chunk read as 0 and their stores are
 // dropped by the hardware, so no branch surrounds a memory access inside the
 // chunk loop.
-template <typename InT, bool SPLIT, int NWV, int NMW, bool BWD>
-__global__ __launch_bounds__(64 * (NWV + NMW)) void scan_kernel(ScanArgs p, int xcd) {
-    constexpr int NSUB = 4 / NWV, NTC = 64 * NWV, NTM = 64 * NMW;
+template <typename InT, bool SPLIT, int NWV, int NCW, int NMW, bool BWD>
+__global__ __launch_bounds__(64 * (NCW + NMW)) void scan_kernel(ScanArgs p, int xcd) {
+    constexpr int NSUB = 4 / NWV, NTC = 64 * NCW, NTM = 64 * NMW;
+    constexpr bool HALF = NCW > NWV;   // two waves per row block
+    static_assert(NCW == NWV || NCW == 2 * NWV, "compute waves");
     using XT = typename std::conditional<BWD, float, InT>::type;
     using I = OpsImage<SPLIT>;
-    using L = ScanLds<SPLIT, NWV>;
+    using L = ScanLds<SPLIT, NWV, NCW>;
     using M = Mat<SPLIT>;
     using Fr = Frag<SPLIT>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
     int head, sub;
     block_map(blockIdx.x, NSUB, xcd != 0, head, sub);
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(64 * (NWV + NMW)) void scan_kernel(ScanArgs p, int 
     auto xmat = [&](int it) { return make_mat<SPLIT>(smem, L::X0 + (it & 1) * L::XB, C, L::NI); };
     auto obuf = [&](int it) { return reinterpret_cast<float*>(smem + L::O0 + (it & 1) * L::OB); };
 
-    if (wave >= NWV) {
+    if (wave >= NCW) {
         // ---- memory waves
         const int ct = tid - NTC;
         const char* ops = static_cast<const char*>(p.ops) + (int64_t)head * NC * kOpsBytes;
@@ -455,80 +464,117 @@ __global__ __launch_bounds__(64 * (NWV + NMW)) void scan_kernel(ScanArgs p, int 
     }
 
     // ---- compute waves
-    const int n0 = i0 + 16 * wave;  // this wave's 16 rows of the state
+    const int rb = HALF ? wave % NWV : wave;    // row block: state rows n0 .. n0 + 15
+    const int n0 = i0 + 16 * rb;
     const int roff = (n0 + r16) * D + 4 * g4;                          // this lane's part of a D x D state
     const int64_t soff = (int64_t)head * D * D + roff;
     const Rsrc rc = make_rsrc(p.ckpt ? p.ckpt + (int64_t)head * NC * D * D : nullptr,
                               p.ckpt ? (uint32_t)NC * D * D * 4 : 0);
 
-    // state rows n0 + r: st[m][q] = X[n0 + r][16m + 4g + q]
-    f32x4 st[4];
+    // The loop for half HF (0 when the row block has one wave): straight-line
+    // code, so the products' independent chains interleave.
+    auto run = [&](auto hf_c) {
+        constexpr int HF = decltype(hf_c)::value;
+        constexpr bool YA = !HALF || HF == 0, YB = !HALF || HF == 1;   // token blocks 0-15, 16-31
+        auto mine = [](int m) { return !HALF || (m >> 1) == HF; };      // column tiles formed here
+        auto xbuf = [&](int it, int w) {
+            return reinterpret_cast<f32x4*>(smem + L::W0 + ((it & 1) * NCW + w) * L::XW);
+        };
+        // state rows n0 + r: st[m][q] = X[n0 + r][16m + 4g + q]
+        f32x4 st[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) st[m] = p.s0 ? *reinterpret_cast<const f32x4*>(p.s0 + soff + 16 * m) : zero4();
-    lds_barrier();
-
-    for (int it = 0; it < NC; ++it) {
-        const int c = chunk_of(it);
-        if constexpr (!BWD) {   // checkpoint c: the state entering the chunk
-#pragma unroll
-            for (int m = 0; m < 4; ++m) bstore4(st[m], rc, (roff + 16 * m) * 4, c * D * D * 4);
-        }
-        char* lb = smem + (it & 1) * L::OPS;
-        const M Pm = make_mat<SPLIT>(lb, I::P, D, D), Mm = make_mat<SPLIT>(lb, I::M, C, D);
-        const M Em = make_mat<SPLIT>(lb, I::E, C, D), Fm = make_mat<SPLIT>(lb, I::Fm, C, C);
-        const M Xm = xmat(it);
-        float* ob = obuf(it);
-        const Fr s0f = frag_acc<SPLIT>(st[0], st[1]), s1f = frag_acc<SPLIT>(st[2], st[3]);
-        f32x4 ya, yb;
-        if constexpr (!BWD) {
-            const Fr vf = frag_t_exact(Xm, 16 * wave, 0, lane);
-            // S_end^T[j'][i] = sum_j P[j][j'] S[i][j] + sum_t M[t][j'] V[t][i]
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4 a = fmma(zero4(), frag_t(Pm, 16 * m, 0, lane), s0f);
-                a = fmma(a, frag_t(Pm, 16 * m, 32, lane), s1f);
-                st[m] = fmma<false, true>(a, frag_t(Mm, 16 * m, 0, lane), vf);
-            }
-            // Y[t][i] = sum_j E[t][j] S[i][j] + sum_s F[t][s] V[s][i]
-            ya = fmma(zero4(), frag_n(Em, 0, 0, lane), s0f);
-            ya = fmma(ya, frag_n(Em, 0, 32, lane), s1f);
-            ya = fmma<false, true>(ya, frag_n(Fm, 0, 0, lane), vf);
-            yb = fmma(zero4(), frag_n(Em, 16, 0, lane), s0f);
-            yb = fmma(yb, frag_n(Em, 16, 32, lane), s1f);
-            yb = fmma<false, true>(yb, frag_n(Fm, 16, 0, lane), vf);
-        } else {
-            const Fr df = frag_t(Xm, 16 * wave, 0, lane);
-            // dv[t][i] = sum_j M[t][j] G[i][j] + sum_u F[u][t] DY[u][i]
-            ya = fmma(zero4(), frag_n(Mm, 0, 0, lane), s0f);
-            ya = fmma(ya, frag_n(Mm, 0, 32, lane), s1f);
-            ya = fmma(ya, frag_t(Fm, 0, 0, lane), df);
-            yb = fmma(zero4(), frag_n(Mm, 16, 0, lane), s0f);
-            yb = fmma(yb, frag_n(Mm, 16, 32, lane), s1f);
-            yb = fmma(yb, frag_t(Fm, 16, 0, lane), df);
-            // G_start^T[j'][i] = sum_j P[j'][j] G[i][j] + sum_t E[t][j'] DY[t][i]
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4 a = fmma(zero4(), frag_n(Pm, 16 * m, 0, lane), s0f);
-                a = fmma(a, frag_n(Pm, 16 * m, 32, lane), s1f);
-                st[m] = fmma(a, frag_t(Em, 16 * m, 0, lane), df);
-            }
-            // gradient w.r.t. the state entering chunk c
-#pragma unroll
-            for (int m = 0; m < 4; ++m) bstore4(st[m], rc, (roff + 16 * m) * 4, c * D * D * 4);
-        }
-        // output rows (t, i) of this chunk for the memory waves
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            ob[(4 * g4 + q) * L::LDO + 16 * wave + r16] = ya[q];
-            ob[(16 + 4 * g4 + q) * L::LDO + 16 * wave + r16] = yb[q];
-        }
+        for (int m = 0; m < 4; ++m)
+            st[m] = p.s0 ? *reinterpret_cast<const f32x4*>(p.s0 + soff + 16 * m) : zero4();
         lds_barrier();
-    }
-    if (NC & 1) lds_barrier();  // the memory waves' last trip
-    if (p.sT) {
+
+        for (int it = 0; it < NC; ++it) {
+            const int c = chunk_of(it);
+            if constexpr (!BWD) {   // checkpoint c: the state entering the chunk
 #pragma unroll
-        for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(p.sT + soff + 16 * m) = st[m];
-    }
+                for (int m = 0; m < 4; ++m)
+                    if (mine(m)) bstore4(st[m], rc, (roff + 16 * m) * 4, c * D * D * 4);
+            }
+            char* lb = smem + (it & 1) * L::OPS;
+            const M Pm = make_mat<SPLIT>(lb, I::P, D, D), Mm = make_mat<SPLIT>(lb, I::M, C, D);
+            const M Em = make_mat<SPLIT>(lb, I::E, C, D), Fm = make_mat<SPLIT>(lb, I::Fm, C, C);
+            const M Xm = xmat(it);
+            float* ob = obuf(it);
+            const Fr s0f = frag_acc<SPLIT>(st[0], st[1]), s1f = frag_acc<SPLIT>(st[2], st[3]);
+            f32x4 ya = zero4(), yb = zero4();
+            if constexpr (!BWD) {
+                const Fr vf = frag_t_exact(Xm, 16 * rb, 0, lane);
+                // S_end^T[j'][i] = sum_j P[j][j'] S[i][j] + sum_t M[t][j'] V[t][i]
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if (!mine(m)) continue;
+                    f32x4 a = fmma(zero4(), frag_t(Pm, 16 * m, 0, lane), s0f);
+                    a = fmma(a, frag_t(Pm, 16 * m, 32, lane), s1f);
+                    st[m] = fmma<false, true>(a, frag_t(Mm, 16 * m, 0, lane), vf);
+                }
+                // Y[t][i] = sum_j E[t][j] S[i][j] + sum_s F[t][s] V[s][i]
+                if constexpr (YA) {
+                    ya = fmma(zero4(), frag_n(Em, 0, 0, lane), s0f);
+                    ya = fmma(ya, frag_n(Em, 0, 32, lane), s1f);
+                    ya = fmma<false, true>(ya, frag_n(Fm, 0, 0, lane), vf);
+                }
+                if constexpr (YB) {
+                    yb = fmma(zero4(), frag_n(Em, 16, 0, lane), s0f);
+                    yb = fmma(yb, frag_n(Em, 16, 32, lane), s1f);
+                    yb = fmma<false, true>(yb, frag_n(Fm, 16, 0, lane), vf);
+                }
+            } else {
+                const Fr df = frag_t(Xm, 16 * rb, 0, lane);
+                // dv[t][i] = sum_j M[t][j] G[i][j] + sum_u F[u][t] DY[u][i]
+                if constexpr (YA) {
+                    ya = fmma(zero4(), frag_n(Mm, 0, 0, lane), s0f);
+                    ya = fmma(ya, frag_n(Mm, 0, 32, lane), s1f);
+                    ya = fmma(ya, frag_t(Fm, 0, 0, lane), df);
+                }
+                if constexpr (YB) {
+                    yb = fmma(zero4(), frag_n(Mm, 16, 0, lane), s0f);
+                    yb = fmma(yb, frag_n(Mm, 16, 32, lane), s1f);
+                    yb = fmma(yb, frag_t(Fm, 16, 0, lane), df);
+                }
+                // G_start^T[j'][i] = sum_j P[j'][j] G[i][j] + sum_t E[t][j'] DY[t][i]
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if (!mine(m)) continue;
+                    f32x4 a = fmma(zero4(), frag_n(Pm, 16 * m, 0, lane), s0f);
+                    a = fmma(a, frag_n(Pm, 16 * m, 32, lane), s1f);
+                    st[m] = fmma(a, frag_t(Em, 16 * m, 0, lane), df);
+                }
+                // gradient w.r.t. the state entering chunk c
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (mine(m)) bstore4(st[m], rc, (roff + 16 * m) * 4, c * D * D * 4);
+            }
+            // output rows (t, i) of this chunk for the memory waves
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (YA) ob[(4 * g4 + q) * L::LDO + 16 * rb + r16] = ya[q];
+                if constexpr (YB) ob[(16 + 4 * g4 + q) * L::LDO + 16 * rb + r16] = yb[q];
+            }
+            if constexpr (HALF) {   // this wave's new tiles for the other wave of the row block
+                f32x4* x = xbuf(it, wave);
+                x[lane] = st[2 * HF];
+                x[64 + lane] = st[2 * HF + 1];
+            }
+            lds_barrier();
+            if constexpr (HALF) {
+                const f32x4* x = xbuf(it, rb + NWV * (1 - HF));
+                st[2 * (1 - HF)] = x[lane];
+                st[2 * (1 - HF) + 1] = x[64 + lane];
+            }
+        }
+        if (NC & 1) lds_barrier();  // the memory waves' last trip
+        if (p.sT) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if (mine(m)) *reinterpret_cast<f32x4*>(p.sT + soff + 16 * m) = st[m];
+        }
+    };
+    if (!HALF || wave < NWV) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
 }
 
 template <typename F>
@@ -552,10 +598,10 @@ hipError_t launch_prepare_typed(const PrepArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename InT, bool SPLIT, int NWV, int NMW, bool BWD>
+template <typename InT, bool SPLIT, int NWV, int NCW, int NMW, bool BWD>
 hipError_t launch_scan_typed(const ScanArgs& a, hipStream_t s) {
-    constexpr int smem_bytes = ScanLds<SPLIT, NWV>::total;
-    auto kern = scan_kernel<InT, SPLIT, NWV, NMW, BWD>;
+    constexpr int smem_bytes = ScanLds<SPLIT, NWV, NCW>::total;
+    auto kern = scan_kernel<InT, SPLIT, NWV, NCW, NMW, BWD>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = set_smem(kern, smem_bytes);
@@ -564,15 +610,15 @@ hipError_t launch_scan_typed(const ScanArgs& a, hipStream_t s) {
     }
     const int heads = a.B * a.H;
     const bool xcd = heads % 8 == 0;
-    hipLaunchKernelGGL(kern, dim3(heads * (4 / NWV)), dim3(64 * (NWV + NMW)), smem_bytes, s, a, xcd ? 1 : 0);
+    hipLaunchKernelGGL(kern, dim3(heads * (4 / NWV)), dim3(64 * (NCW + NMW)), smem_bytes, s, a, xcd ? 1 : 0);
     return hipGetLastError();
 }
 
 template <typename InT, bool SPLIT, bool BWD>
 hipError_t launch_scan_nwv(const ScanArgs& a, hipStream_t s) {
     // Fewer heads than CUs: spread each head's 4 waves over 2 workgroups.
-    if (a.B * a.H <= 128) return launch_scan_typed<InT, SPLIT, 2, 4, BWD>(a, s);
-    return launch_scan_typed<InT, SPLIT, 4, 4, BWD>(a, s);
+    if (a.B * a.H <= 128) return launch_scan_typed<InT, SPLIT, 2, 4, 4, BWD>(a, s);
+    return launch_scan_typed<InT, SPLIT, 4, 4, 4, BWD>(a, s);
 }
 
 }  // namespace
