@@ -331,16 +331,34 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     // ---- phase 2: RHS_U[s][i] = sum_j S0[i][j] Ahat[s][j] + sum_u V[u][i] Lak[s][u]
     //               RHS_D[s][i] = sum_j Ge'[i][j] Btil[s][j] + sum_u DY[u][i] Mrb[u][s]
     // (accumulator element (i, s); rows s stored with four consecutive i per lane)
-    {   // wave: tile (ib, sb) of both; the two chains interleave
-        const int ib = wave & 3, sb = wave >> 2;
-        f32x4 au = fmma(zero4(), frag_n(S0m, 16 * ib, 0, lane), frag_n(A, 16 * sb, 0, lane));
-        f32x4 ad = fmma(zero4(), frag_n(Gem, 16 * ib, 0, lane), frag_n(Bm, 16 * sb, 0, lane));
-        au = fmma(au, frag_n(S0m, 16 * ib, 32, lane), frag_n(A, 16 * sb, 32, lane));
-        ad = fmma(ad, frag_n(Gem, 16 * ib, 32, lane), frag_n(Bm, 16 * sb, 32, lane));
-        au = fmma<true, false>(au, frag_t_exact(Vm, 16 * ib, 0, lane), frag_n(Lak, 16 * sb, 0, lane));
-        ad = fmma(ad, frag_t(DYm, 16 * ib, 0, lane), frag_t(Mrb, 16 * sb, 0, lane));
-        put4(RU, 16 * sb + r16, 16 * ib + 4 * g4, au);
-        put4(RD, 16 * sb + r16, 16 * ib + 4 * g4, ad);
+    {   // waves 0-3: RU, waves 4-7: RD; wave: column block ib, both row blocks s (the i-side
+        // fragments are read once for both)
+        using Fr = Frag<SPLIT>;
+        const int ib = wave & 3;
+        f32x4 a0, a1;
+        if (wave < 4) {
+            const Fr x0 = frag_n(S0m, 16 * ib, 0, lane), x1 = frag_n(S0m, 16 * ib, 32, lane);
+            a0 = fmma(zero4(), x0, frag_n(A, 0, 0, lane));
+            a1 = fmma(zero4(), x0, frag_n(A, 16, 0, lane));
+            a0 = fmma(a0, x1, frag_n(A, 0, 32, lane));
+            a1 = fmma(a1, x1, frag_n(A, 16, 32, lane));
+            const Fr xv = frag_t_exact(Vm, 16 * ib, 0, lane);
+            a0 = fmma<true, false>(a0, xv, frag_n(Lak, 0, 0, lane));
+            a1 = fmma<true, false>(a1, xv, frag_n(Lak, 16, 0, lane));
+            put4(RU, r16, 16 * ib + 4 * g4, a0);
+            put4(RU, 16 + r16, 16 * ib + 4 * g4, a1);
+        } else {
+            const Fr x0 = frag_n(Gem, 16 * ib, 0, lane), x1 = frag_n(Gem, 16 * ib, 32, lane);
+            a0 = fmma(zero4(), x0, frag_n(Bm, 0, 0, lane));
+            a1 = fmma(zero4(), x0, frag_n(Bm, 16, 0, lane));
+            a0 = fmma(a0, x1, frag_n(Bm, 0, 32, lane));
+            a1 = fmma(a1, x1, frag_n(Bm, 16, 32, lane));
+            const Fr xd = frag_t(DYm, 16 * ib, 0, lane);
+            a0 = fmma(a0, xd, frag_t(Mrb, 0, 0, lane));
+            a1 = fmma(a1, xd, frag_t(Mrb, 16, 0, lane));
+            put4(RD, r16, 16 * ib + 4 * g4, a0);
+            put4(RD, 16 + r16, 16 * ib + 4 * g4, a1);
+        }
     }
     lds_barrier();
 
