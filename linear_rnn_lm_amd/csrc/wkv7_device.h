@@ -400,13 +400,24 @@ __device__ __forceinline__ void chunk_prep(const RawChunk<NT, InT>& raw, const P
     qp[q * 64 + j0] = p.x;
     qp[q * 64 + j0 + 1] = p.y;
     lds_barrier();
-    float2 pre = make_float2(1.f, 1.f);
+    // wave 0, lane = column: the products over earlier groups, in place (and gamma_last)
+    if (tid < 64) {
+        float qv[NG];   // all reads first, then the products, then the writes
 #pragma unroll
-    for (int q2 = 0; q2 < NG; ++q2) {   // selects, not branches: a factor 1 leaves the product unchanged
-        const float2 v = *reinterpret_cast<const float2*>(qp + q2 * 64 + j0);
-        pre.x *= q2 < q ? v.x : 1.f;
-        pre.y *= q2 < q ? v.y : 1.f;
+        for (int q2 = 0; q2 < NG; ++q2) qv[q2] = qp[q2 * 64 + tid];
+        float run = 1.f;
+#pragma unroll
+        for (int q2 = 0; q2 < NG; ++q2) {
+            const float v = qv[q2];
+            qv[q2] = run;
+            run *= v;
+        }
+#pragma unroll
+        for (int q2 = 0; q2 < NG; ++q2) qp[q2 * 64 + tid] = qv[q2];
+        o.glast[tid] = run;
     }
+    lds_barrier();
+    const float2 pre = *reinterpret_cast<const float2*>(qp + q * 64 + j0);
     float2 gprev = pre;
     float gt[2][TPG], at[2][TPG], rt[2][TPG], bt[2][TPG], kt[2][TPG];
 #pragma unroll
@@ -431,10 +442,6 @@ __device__ __forceinline__ void chunk_prep(const RawChunk<NT, InT>& raw, const P
         bt[0][tt] = bx; bt[1][tt] = by;
         kt[0][tt] = kx; kt[1][tt] = ky;
         gprev = g;
-    }
-    if (q == NG - 1) {
-        o.glast[j0] = gt[0][TPG - 1];
-        o.glast[j0 + 1] = gt[1][TPG - 1];
     }
     // transposed copies: TPG consecutive tokens of one column per thread
     const int t0 = q * TPG;

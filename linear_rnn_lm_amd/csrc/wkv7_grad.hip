@@ -80,40 +80,18 @@ __device__ __forceinline__ Mat<SPLIT> exact_mat(char* smem, int off, int K) {
     return Mat<SPLIT>{smem + off, Fmt<SPLIT>::ld(K), 0};   // one plane: lo reads see hi
 }
 
-// Where one chunk's inputs live.  `on == false` (no next chunk) gives every
-// buffer resource size 0, so the loads return zeros without touching memory.
-// The chunks of one workgroup: blockIdx.x, + gridDim.x, ... in the block_map
-// order, walked without divisions (the steps are divided out once).
-struct ChunkWalk {
-    int head, c, bb, hh;               // position: head = bb * H + hh, chunk c
-    int NC, H, dc, dh, hs, qa, ra, qb, rb;
-
-    __device__ __forceinline__ ChunkWalk(const BwdArgs& p, int blk, int grid, bool xcd) {
-        block_map(blk, p.NC, xcd, head, c);
-        NC = p.NC;
-        H = p.H;
-        bb = head / H;
-        hh = head % H;
-        hs = xcd ? 8 : 1;                       // head step of one carry out of c
-        const int gs = xcd ? grid >> 3 : grid;  // chunk-index step (grid % 8 == 0 with xcd)
-        dc = gs % NC;
-        dh = (gs / NC) * hs;
-        qa = dh / H;
-        ra = dh % H;
-        qb = (dh + hs) / H;
-        rb = (dh + hs) % H;
-    }
-    __device__ __forceinline__ void advance() {
-        c += dc;
-        const bool carry = c >= NC;
-        if (carry) c -= NC;
-        head += dh + (carry ? hs : 0);
-        hh += carry ? rb : ra;
-        bb += carry ? qb : qa;
-        if (hh >= H) {
-            hh -= H;
-            bb += 1;
-        }
+// Position of work item idx (the block_map order: with xcd, consecutive items
+// of one head stay on one XCD): head = bb * H + hh, chunk c.  The divisions
+// use the launch's multipliers.
+struct ChunkPos {
+    int head, c, bb, hh;
+    __device__ __forceinline__ ChunkPos(const BwdArgs& p, int idx, bool xcd) {
+        const uint32_t slot = xcd ? (uint32_t)idx >> 3 : (uint32_t)idx;
+        const uint32_t q = fdiv(slot, p.fd_nc);
+        c = (int)(slot - q * (uint32_t)p.NC);
+        head = xcd ? (int)(q * 8 + (idx & 7)) : (int)q;
+        bb = (int)fdiv((uint32_t)head, p.fd_h);
+        hh = head - bb * p.H;
     }
 };
 
@@ -133,7 +111,7 @@ struct ChunkSrc {
     bool on, has_ge;
     const float* ge;   // gradient at the chunk's end: next checkpoint's, dhT, or none
 
-    __device__ __forceinline__ ChunkSrc(const BwdArgs& p, const ChunkWalk& w, bool on_) {
+    __device__ __forceinline__ ChunkSrc(const BwdArgs& p, const ChunkPos& w, bool on_) {
         const int HD = p.H * D;
         tokc = (w.bb * p.T + w.c * C) * HD + w.hh * D;
         cs = ((int64_t)w.head * p.NC + w.c) * D * D;
@@ -241,9 +219,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     const int si = tid >> 3, sj0 = (tid & 7) * 8;
 
     int idx = blockIdx.x;
-    ChunkWalk cw(p, idx, gridDim.x, xcd != 0);
     GradIn<InT> cur, nxt;
-    cur.issue_all(p, ChunkSrc(p, cw, true), tid);
+    cur.issue_all(p, ChunkSrc(p, ChunkPos(p, idx, xcd != 0), true), tid);
     // The first chunk needs these at once.  Waiting here also leaves nothing
     // pending on entry to the loop, so the compiler sizes the loop's waits for
     // the steady state (where the previous chunk's stores are still in flight)
@@ -251,12 +228,11 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   for (;;) {
+    const ChunkPos cw(p, idx, xcd != 0);
     const int head = cw.head, c = cw.c, bb = cw.bb, hh = cw.hh;
     const int nidx = idx + (int)gridDim.x;
     const bool more = nidx < total;
-    ChunkWalk nw = cw;
-    nw.advance();
-    const ChunkSrc nsrc(p, nw, more);
+    const ChunkSrc nsrc(p, ChunkPos(p, more ? nidx : idx, xcd != 0), more);
     nxt.template issue<0>(p, nsrc, tid);
     const int t0 = c * C, cc = min(C, p.T - t0);
     // fp32 outputs: whole tensors; a token past the sequence's end gets an
@@ -529,18 +505,28 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         qp[q * 64 + j0] = tot.x;
         qp[q * 64 + j0 + 1] = tot.y;
         lds_barrier();
-        float2 acc = make_float2(0.f, 0.f);
+        // wave 0, lane = column: diag(Gs^T S0) (the 8 waves' G' S0 rows and the 2 token-block rows)
+        // plus the sums over earlier token groups, in place
+        if (wave == 0) {
+            float rv[GNW + 2], qv[NG];   // all reads first, then the sums, then the writes
 #pragma unroll
-        for (int g = 0; g < GNW + 2; ++g) {   // diag(Gs^T S0): 8 waves' G' S0 rows, 2 token blocks
-            acc.x += red[g * 64 + j0];
-            acc.y += red[g * 64 + j0 + 1];
-        }
+            for (int g = 0; g < GNW + 2; ++g) rv[g] = red[g * 64 + lane];
 #pragma unroll
-        for (int q2 = 0; q2 < NG; ++q2) {   // selects, not branches: adding 0 leaves the sum unchanged
-            const float2 v = *reinterpret_cast<const float2*>(qp + q2 * 64 + j0);
-            acc.x += q2 < q ? v.x : 0.f;
-            acc.y += q2 < q ? v.y : 0.f;
+            for (int q2 = 0; q2 < NG; ++q2) qv[q2] = qp[q2 * 64 + lane];
+            float run = 0.f;
+#pragma unroll
+            for (int g = 0; g < GNW + 2; ++g) run += rv[g];
+#pragma unroll
+            for (int q2 = 0; q2 < NG; ++q2) {
+                const float v = qv[q2];
+                qv[q2] = run;
+                run += v;
+            }
+#pragma unroll
+            for (int q2 = 0; q2 < NG; ++q2) qp[q2 * 64 + lane] = qv[q2];
         }
+        lds_barrier();
+        float2 acc = *reinterpret_cast<const float2*>(qp + q * 64 + j0);
         const Rsrc rdw = make_rsrc(p.dw, out_bytes);
 #pragma unroll
         for (int tt = 0; tt < TPG; ++tt) {
@@ -560,13 +546,12 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     if (!more) break;
     cur = nxt;
     idx = nidx;
-    cw = nw;
     lds_barrier();   // this chunk's last LDS reads before the next chunk's writes
   }
 }
 
 template <typename InT, bool SPLIT>
-hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_typed(BwdArgs a, hipStream_t s) {
     using L = GradSmem<SPLIT>;
     auto kern = grad_kernel<InT, SPLIT>;
     static bool attr_set = false;
@@ -589,6 +574,8 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
     const int xcd = (heads % 8 == 0) ? 1 : 0;
     int grid = total < n_cu ? total : n_cu;
     if (xcd && grid > 8) grid -= grid % 8;   // a workgroup's chunks stay on one XCD
+    a.fd_nc = make_fastdiv((uint32_t)a.NC);
+    a.fd_h = make_fastdiv((uint32_t)a.H);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(GNT), L::total, s, a, xcd, total);
     return hipGetLastError();
 }

@@ -17,6 +17,31 @@ struct FwdArgs {
     int B, T, H, NC;
 };
 
+// Division by a divisor that is fixed for a launch, without a divide
+// instruction: for 0 <= n < 2^31, n / d = (umulhi(n, m) + n) >> s with
+// s = ceil(log2 d) and the round-up multiplier m = floor(2^32 (2^s - d) / d) + 1
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).
+struct FastDiv {
+    uint32_t d, m, s;
+};
+constexpr FastDiv make_fastdiv(uint32_t d) {
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    return FastDiv{d, (uint32_t)((((1ull << s) - d) << 32) / d + 1), s};
+}
+__host__ __device__ constexpr uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (uint32_t)(((((uint64_t)n * f.m) >> 32) + n) >> f.s);
+}
+static_assert(fdiv(0, make_fastdiv(1)) == 0 && fdiv(12345, make_fastdiv(1)) == 12345, "fastdiv");
+static_assert(fdiv(31, make_fastdiv(32)) == 0 && fdiv(32, make_fastdiv(32)) == 1 && fdiv(2303, make_fastdiv(32)) == 71,
+              "fastdiv");
+static_assert(fdiv(71, make_fastdiv(6)) == 11 && fdiv(72, make_fastdiv(6)) == 12 && fdiv(0x7fffffff, make_fastdiv(6)) ==
+              0x7fffffff / 6, "fastdiv");
+static_assert(fdiv(0x7fffffff, make_fastdiv(7)) == 0x7fffffff / 7 && fdiv(0x7ffffffe, make_fastdiv(0x7fffffff)) == 0 &&
+              fdiv(0x7fffffff, make_fastdiv(0x7fffffff)) == 1, "fastdiv");
+static_assert(fdiv(999999, make_fastdiv(1000)) == 999 && fdiv(1000000, make_fastdiv(1000)) == 1000, "fastdiv");
+
 struct BwdArgs {
     const void *r, *w, *k, *v, *a, *b;
     const float* inv;  // (B,H,NC,32,32): (I - Lab)^-1 of every chunk
@@ -27,6 +52,7 @@ struct BwdArgs {
     float* dh0;
     float* gbuf;  // (B,H,NC,D,D): gradient w.r.t. the state entering each chunk
     int B, T, H, NC;
+    FastDiv fd_nc, fd_h;   // set by the launcher
 };
 
 // Token tensors (B, T, H, D) are addressed with 32-bit byte offsets: the entry
