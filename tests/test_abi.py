@@ -213,3 +213,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         L.lib()
+
+
+def test_segment_spans():
+    from linear_rnn_lm_amd.segments import _segments
+    assert _segments(100, 32) == [(0, 32), (32, 64), (64, 96), (96, 100)]
+    assert _segments(64, 64) == [(0, 64)]
+    assert _segments(5, 100) == [(0, 5)]
+    with pytest.raises(ValueError):
+        _segments(10, 0)
