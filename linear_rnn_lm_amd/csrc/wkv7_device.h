@@ -185,6 +185,29 @@ __device__ __forceinline__ void put4(Mat<true> M, int m, int k, f32x4 v) {
 __device__ __forceinline__ void put4(Mat<false> M, int m, int k, f32x4 v) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(M.p) + m * M.ld + k) = v;
 }
+// An accumulator-tile row quad, v = X[m][k0 + 4g .. + 3] of lane (g, r), with
+// k8 = k0 + 8 (g / 2).  Lanes g and g ^ 1 (16 lanes apart, same m) swap
+// halves with v_permlane16_swap so that the even one stores the hi values and
+// the odd one the lo values of the eight columns k8 .. k8 + 7: one 16-byte LDS
+// store per lane instead of two 8-byte ones.  (The swap exchanges the odd
+// 16-lane rows of its first operand with the even rows of its second.)  Every
+// lane of the wave must take part.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void put4_pair(Mat<true> M, int m, int k8, f32x4 v, int g) {
+    bf16x2 h0, l0, h1, l1;
+    split2(f32x2{v[0], v[1]}, h0, l0);
+    split2(f32x2{v[2], v[3]}, h1, l1);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, h0), __builtin_bit_cast(unsigned, l0),
+                                                     false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, h1), __builtin_bit_cast(unsigned, l1),
+                                                     false, false);
+    __bf16* h = reinterpret_cast<__bf16*>(M.p) + m * M.ld + k8 + ((g & 1) ? M.plane : 0);
+    *reinterpret_cast<u32x4_t*>(h) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+}
+__device__ __forceinline__ void put4_pair(Mat<false> M, int m, int k8, f32x4 v, int g) {
+    put4(M, m, k8 + 4 * (g & 1), v);
+}
+
 __device__ __forceinline__ void put4_exact(Mat<true> M, int m, int k, f32x4 v) {
     bf16x4 hi;
 #pragma unroll

@@ -273,12 +273,18 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     if (wave < 6) {
         const int mat = wave / 3, tile = wave % 3;
         const int ti = tile == 0 ? 0 : 1, tj = tile == 2 ? 1 : 0;
+        // accumulator element (s, t): lane (g, r) holds row t = 16 ti + r, columns s = 16 tj + 4g ..
+        const int t = 16 * ti + r16, s0_ = 16 * tj + 4 * g4;
         if (mat == 0) {
-            const f32x4 acc = mma<SPLIT, D>(zero4(), A, ti * 16, Km, tj * 16, lane);
-            store_rows<MASK_STRICT>(Lak, acc, ti * 16, tj * 16, lane);
+            f32x4 acc = mma<SPLIT, D>(zero4(), Km, tj * 16, A, ti * 16, lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = s0_ + q < t ? acc[q] : 0.f;
+            put4_pair(Lak, t, 16 * tj + 8 * (g4 >> 1), acc, g4);
         } else {
-            const f32x4 acc = mma<SPLIT, D>(zero4(), R, ti * 16, Bm, tj * 16, lane);
-            store_rows<MASK_LOWER>(Mrb, acc, ti * 16, tj * 16, lane);
+            f32x4 acc = mma<SPLIT, D>(zero4(), Bm, tj * 16, R, ti * 16, lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = s0_ + q <= t ? acc[q] : 0.f;
+            put4_pair(Mrb, t, 16 * tj + 8 * (g4 >> 1), acc, g4);
         }
     } else {
         zero_block(wave == 6 ? Lak : Mrb, 0, 16, lane);
@@ -321,8 +327,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
             const Fr xv = frag_t_exact(Vm, 16 * ib, 0, lane);
             a0 = fmma<true, false>(a0, xv, frag_n(Lak, 0, 0, lane));
             a1 = fmma<true, false>(a1, xv, frag_n(Lak, 16, 0, lane));
-            put4(RU, r16, 16 * ib + 4 * g4, a0);
-            put4(RU, 16 + r16, 16 * ib + 4 * g4, a1);
+            put4_pair(RU, r16, 16 * ib + 8 * (g4 >> 1), a0, g4);
+            put4_pair(RU, 16 + r16, 16 * ib + 8 * (g4 >> 1), a1, g4);
         } else {
             const Fr x0 = frag_n(Gem, 16 * ib, 0, lane), x1 = frag_n(Gem, 16 * ib, 32, lane);
             a0 = fmma(zero4(), x0, frag_n(Bm, 0, 0, lane));
@@ -332,8 +338,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
             const Fr xd = frag_t(DYm, 16 * ib, 0, lane);
             a0 = fmma(a0, xd, frag_t(Mrb, 0, 0, lane));
             a1 = fmma(a1, xd, frag_t(Mrb, 16, 0, lane));
-            put4(RD, r16, 16 * ib + 4 * g4, a0);
-            put4(RD, 16 + r16, 16 * ib + 4 * g4, a1);
+            put4_pair(RD, r16, 16 * ib + 8 * (g4 >> 1), a0, g4);
+            put4_pair(RD, 16 + r16, 16 * ib + 8 * (g4 >> 1), a1, g4);
         }
     }
     lds_barrier();
@@ -344,8 +350,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         const int ib = wave & 3, tb = wave >> 2;
         const f32x4 au = fmma(zero4(), frag_t(RU, 16 * ib, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
         const f32x4 ad = fmma(zero4(), frag_t(RD, 16 * ib, 0, lane), frag_t(Tm, 16 * tb, 0, lane));
-        put4(Um, 16 * tb + r16, 16 * ib + 4 * g4, au);
-        put4(DSAm, 16 * tb + r16, 16 * ib + 4 * g4, ad);
+        put4_pair(Um, 16 * tb + r16, 16 * ib + 8 * (g4 >> 1), au, g4);
+        put4_pair(DSAm, 16 * tb + r16, 16 * ib + 8 * (g4 >> 1), ad, g4);
     }
     lds_barrier();
 
@@ -355,8 +361,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     {   // wave: tile (wave % 4) of P(wave / 4) and P(wave / 4 + 2); tile 3 (s >= 16 > t) is zero
         const int tile = wave & 3, m0 = wave >> 2;
         if (tile == 3) {
-            put4(Pm(m0), r16, 16 + 4 * g4, zero4());
-            put4(Pm(m0 + 2), r16, 16 + 4 * g4, zero4());
+            put4_pair(Pm(m0), r16, 16 + 8 * (g4 >> 1), zero4(), g4);
+            put4_pair(Pm(m0 + 2), r16, 16 + 8 * (g4 >> 1), zero4(), g4);
         } else {
             const int sb = tile == 2 ? 1 : 0, tb = tile == 0 ? 0 : 1;
             // m0 = 0: P1 (DY U^T), P3 (DSA U^T); m0 = 1: P2 (DY V^T), P4 (DSA V^T)
@@ -379,8 +385,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
                 if (s > t) a0[q] = 0.f;    // P1, P2: s <= t
                 if (s >= t) a1[q] = 0.f;   // P3, P4: s < t
             }
-            put4(Pm(m0), t, s0_, a0);
-            put4(Pm(m0 + 2), t, s0_, a1);
+            put4_pair(Pm(m0), t, 16 * sb + 8 * (g4 >> 1), a0, g4);
+            put4_pair(Pm(m0 + 2), t, 16 * sb + 8 * (g4 >> 1), a1, g4);
         }
     }
     lds_barrier();
