@@ -248,7 +248,10 @@ struct OpsImage {
 };
 
 // One chunk's operand block, global (unpadded) -> registers -> LDS image.
-// Thread tid of NT moves the 16-byte units tid + NT * u.
+// Thread tid of NT moves the 16-byte units tid + NT * u.  F's tile of
+// columns 16-31 in rows 0-15 is zero (F is lower triangular): its units are
+// loaded at an offset past the block, so the buffer load returns 0 without
+// reading memory and the LDS image gets the zeros.
 template <bool SPLIT, int NT>
 struct OpsCopy {
     static constexpr int N16 = kOpsBytes / 16;
@@ -257,6 +260,7 @@ struct OpsCopy {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     u32x4 v[PER];
     int off[PER];  // LDS byte offsets inside a buffer
+    int src[PER];  // byte offsets inside the operand block (past it for the zero tile)
 
     __device__ __forceinline__ void init(int tid) {
         using O = OpsLayout<SPLIT>;
@@ -279,11 +283,15 @@ struct OpsCopy {
             const int tr = tile / (cols / 16), tc = tile % (cols / 16);
             const int row = 16 * tr + (in >> 4), col = 16 * tc + (in & 15);
             off[u] = lbase + ((plane * rows + row) * (cols + PAD) + col) * ESZ;
+            const bool zero_tile = first == O::F && tile == 1;
+            src[u] = zero_tile ? (int)kDropOffset : (tid + NT * u) * 16;
         }
     }
-    __device__ __forceinline__ void load(const char* src, int tid) {
+    __device__ __forceinline__ void load(const char* base, int) {
+        const Rsrc r = make_rsrc(base, kOpsBytes);
 #pragma unroll
-        for (int u = 0; u < PER; ++u) v[u] = reinterpret_cast<const u32x4*>(src)[tid + NT * u];
+        for (int u = 0; u < PER; ++u)
+            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, src[u], 0, 0));
     }
     __device__ __forceinline__ void store(char* buf) const {
 #pragma unroll
