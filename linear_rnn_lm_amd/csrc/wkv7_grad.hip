@@ -420,30 +420,79 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         for (int o = 0; o < 2; ++o)
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) ac[o][jj] = zero4();
+        // The four k-steps' fragments.  Split format: each step's reads are issued before the
+        // previous step's products (sched_barrier), so the LDS latency overlaps the MFMA work;
+        // fp32 fragments are twice as large and are read right before their step.
+        struct Step {
+            Fr x0, x1, y0, y1;
+        };
+        auto run4 = [&](auto ld, auto ex01, auto on_step) {
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            using I3 = std::integral_constant<int, 3>;
+            auto go = [&](const Step& st, int k) {
+                if (k < 2) kstep(ac, st.x0, st.x1, st.y0, st.y1, ex01);
+                else kstep(ac, st.x0, st.x1, st.y0, st.y1, split_t{});
+                on_step(k);
+            };
+            if constexpr (SPLIT) {
+                Step s0 = ld(I0{});
+                Step s1 = ld(I1{});
+                __builtin_amdgcn_sched_barrier(0);
+                go(s0, 0);
+                Step s2 = ld(I2{});
+                __builtin_amdgcn_sched_barrier(0);
+                go(s1, 1);
+                Step s3 = ld(I3{});
+                __builtin_amdgcn_sched_barrier(0);
+                go(s2, 2);
+                go(s3, 3);
+            } else {
+                go(ld(I0{}), 0);
+                go(ld(I1{}), 1);
+                go(ld(I2{}), 2);
+                go(ld(I3{}), 3);
+            }
+        };
+        auto no_op = [](int) {};
         if (pr == 0) {
             // aR = S0 DY + Btil P1 + Ktil P2, aA = S0 DSA + Btil P3 + Ktil P4 (j side first)
-            kstep(ac, frag_t(S0m, 16 * jb0, 0, lane), frag_t(S0m, 16 * jb0 + 16, 0, lane),
-                  frag_n(DYm, 16 * tb, 0, lane), frag_n(DSAm, 16 * tb, 0, lane), split_t{});
-            kstep(ac, frag_t(S0m, 16 * jb0, 32, lane), frag_t(S0m, 16 * jb0 + 16, 32, lane),
-                  frag_n(DYm, 16 * tb, 32, lane), frag_n(DSAm, 16 * tb, 32, lane), split_t{});
+            auto ld = [&](auto kc) {
+                constexpr int K = decltype(kc)::value;
+                if constexpr (K < 2)
+                    return Step{frag_t(S0m, 16 * jb0, 32 * K, lane), frag_t(S0m, 16 * jb0 + 16, 32 * K, lane),
+                                frag_n(DYm, 16 * tb, 32 * K, lane), frag_n(DSAm, 16 * tb, 32 * K, lane)};
+                else if constexpr (K == 2)
+                    return Step{frag_t(Bm, 16 * jb0, 0, lane), frag_t(Bm, 16 * jb0 + 16, 0, lane),
+                                frag_n(Pm(0), 16 * tb, 0, lane), frag_n(Pm(2), 16 * tb, 0, lane)};
+                else
+                    return Step{frag_t(Km, 16 * jb0, 0, lane), frag_t(Km, 16 * jb0 + 16, 0, lane),
+                                frag_n(Pm(1), 16 * tb, 0, lane), frag_n(Pm(3), 16 * tb, 0, lane)};
+            };
+            run4(ld, split_t{}, [&](int k) {
+                if (k == 1) {
 #pragma unroll
-            for (int o = 0; o < 2; ++o)
+                    for (int o = 0; o < 2; ++o)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) xs[o][jj] = ac[o][jj];
-            kstep(ac, frag_t(Bm, 16 * jb0, 0, lane), frag_t(Bm, 16 * jb0 + 16, 0, lane),
-                  frag_n(Pm(0), 16 * tb, 0, lane), frag_n(Pm(2), 16 * tb, 0, lane), split_t{});
-            kstep(ac, frag_t(Km, 16 * jb0, 0, lane), frag_t(Km, 16 * jb0 + 16, 0, lane),
-                  frag_n(Pm(1), 16 * tb, 0, lane), frag_n(Pm(3), 16 * tb, 0, lane), split_t{});
+                        for (int jj = 0; jj < 2; ++jj) xs[o][jj] = ac[o][jj];
+                }
+            });
         } else {
             // aK = Ge' V + Ahat P4^T + Rhat P2^T, aB = Ge' U + Ahat P3^T + Rhat P1^T
-            kstep(ac, frag_t(Gem, 16 * jb0, 0, lane), frag_t(Gem, 16 * jb0 + 16, 0, lane),
-                  frag_n(Vm, 16 * tb, 0, lane), frag_n(Um, 16 * tb, 0, lane), exact_t{});
-            kstep(ac, frag_t(Gem, 16 * jb0, 32, lane), frag_t(Gem, 16 * jb0 + 16, 32, lane),
-                  frag_n(Vm, 16 * tb, 32, lane), frag_n(Um, 16 * tb, 32, lane), exact_t{});
-            kstep(ac, frag_t(A, 16 * jb0, 0, lane), frag_t(A, 16 * jb0 + 16, 0, lane),
-                  frag_t(Pm(3), 16 * tb, 0, lane), frag_t(Pm(2), 16 * tb, 0, lane), split_t{});
-            kstep(ac, frag_t(R, 16 * jb0, 0, lane), frag_t(R, 16 * jb0 + 16, 0, lane),
-                  frag_t(Pm(1), 16 * tb, 0, lane), frag_t(Pm(0), 16 * tb, 0, lane), split_t{});
+            auto ld = [&](auto kc) {
+                constexpr int K = decltype(kc)::value;
+                if constexpr (K < 2)
+                    return Step{frag_t(Gem, 16 * jb0, 32 * K, lane), frag_t(Gem, 16 * jb0 + 16, 32 * K, lane),
+                                frag_n(Vm, 16 * tb, 32 * K, lane), frag_n(Um, 16 * tb, 32 * K, lane)};
+                else if constexpr (K == 2)
+                    return Step{frag_t(A, 16 * jb0, 0, lane), frag_t(A, 16 * jb0 + 16, 0, lane),
+                                frag_t(Pm(3), 16 * tb, 0, lane), frag_t(Pm(2), 16 * tb, 0, lane)};
+                else
+                    return Step{frag_t(R, 16 * jb0, 0, lane), frag_t(R, 16 * jb0 + 16, 0, lane),
+                                frag_t(Pm(1), 16 * tb, 0, lane), frag_t(Pm(0), 16 * tb, 0, lane)};
+            };
+            run4(ld, exact_t{}, no_op);
         }
         const Rsrc r0 = make_rsrc(pr == 0 ? p.dr : p.dk, out_bytes);
         const Rsrc r1 = make_rsrc(pr == 0 ? p.da : p.db, out_bytes);
