@@ -703,8 +703,11 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 //
 // CP selects the cache policy: kCached for data the next kernel reads back
 // (checkpoints, state gradients), kStream (non-temporal) for outputs that
-// leave the library.
-constexpr int kCached = 0, kStream = 2;
+// leave the library, kStreamDev (non-temporal, device scope) for outputs
+// whose stores cover a cache line in pieces from several instructions: the
+// gradient kernel's tiles write 64-byte row pieces, which with kStream alone
+// cost 1.28x their bytes in HBM writes and with kStreamDev exactly their bytes.
+constexpr int kCached = 0, kStream = 2, kStreamDev = 18;
 template <int CP = kCached>
 __device__ __forceinline__ void bstore(float v, Rsrc r, int voff, int soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff + soff, 0, CP);

@@ -528,8 +528,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
             }
             // outside the branch: every wave issues the same stores, so the
             // compiler counts this chunk's outstanding stores exactly
-            bstore4<kStream>(ac[0][jj] * sc0, r0, voff, 0);
-            bstore4<kStream>(ac[1][jj] * sc1, r1, voff, 0);
+            bstore4<kStreamDev>(ac[0][jj] * sc0, r0, voff, 0);
+            bstore4<kStreamDev>(ac[1][jj] * sc1, r1, voff, 0);
         }
         lds_barrier();
         if (pr == 0) {
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         for (int tt = 0; tt < TPG; ++tt) {
             const int t = q * TPG + tt;
             const float2 wv = Pair<InT>::f(cur.raw.w[tt]);
-            bstore2<kStream>(make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y)), rdw,
+            bstore2<kStreamDev>(make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y)), rdw,
                              out_off(t, j0), 0);
             acc.x += hx[tt].x;
             acc.y += hx[tt].y;
