@@ -618,7 +618,8 @@ __device__ __forceinline__ void chunk_cc(Mat<SPLIT> A, Mat<SPLIT> R, Mat<SPLIT> 
 // (LT[s][t] = L[t][s], fp32, stride LDF), by 16 x 16 blocks: T11 = (I - L11)^-1
 // and T22 = (I - L22)^-1 by forward substitution (lanes 0..15 and 16..31, one
 // column each), then T21 = T22 (L21 T11) with two fp32 MFMA products.  One
-// wave.  `tf` (fp32, stride LDF) receives T; `scr` is 16 x 20 floats of scratch.
+// wave.  `tf` (fp32, stride LDF) receives T except its zero block (rows 0-15,
+// columns 16-31), which the caller writes; `scr` is 16 x 20 floats of scratch.
 __device__ __forceinline__ void tri_inverse(const float* LT, float* tf, float* scr, int lane) {
     if (lane < 32) {
         const int k = lane & 15, base = lane & 16;
@@ -639,10 +640,7 @@ __device__ __forceinline__ void tri_inverse(const float* LT, float* tf, float* s
             }
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            tf[(base + t) * LDF + base + k] = x[t];
-            if (base == 0) tf[t * LDF + 16 + k] = 0.f;
-        }
+        for (int t = 0; t < 16; ++t) tf[(base + t) * LDF + base + k] = x[t];
     }
     wave_lds_sync();
     // P = L21 T11  (row t-16, column n); L21[r][c] = LT[c][16 + r]

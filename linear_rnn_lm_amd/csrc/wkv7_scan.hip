@@ -118,7 +118,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
         const f32x4 t = mma<SPLIT, D>(zero4(), A, 16 * ti, Bm, 16 * tj, lane);
         store_f32_t<MASK_STRICT>(labf, LDF, t, 16 * ti, 16 * tj, lane);
     } else {
-        for (int e = lane; e < 256; e += 64) labf[(16 + (e >> 4)) * LDF + (e & 15)] = 0.f;
+        // the zero blocks: Lab^T rows 16-31, columns 0-15 and T's rows 0-15, columns 16-31
+        for (int e = lane; e < 256; e += 64) {
+            labf[(16 + (e >> 4)) * LDF + (e & 15)] = 0.f;
+            tf[(e >> 4) * LDF + 16 + (e & 15)] = 0.f;
+        }
     }
     lds_barrier();
 
@@ -183,30 +187,34 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
     // consecutive columns of one row per tile
     E* ob = reinterpret_cast<E*>(static_cast<char*>(p.ops) + (int64_t)item * kOpsBytes);
     // Wave w: P tiles (row block w, column blocks 0..3), M and E tiles (column block w, row
-    // blocks 0, 1); wave 2 also F, wave 3 F's zero tile.  The W1 and Btil fragments of column
-    // block w serve several tiles; all tiles of a wave are independent chains.
+    // blocks 0, 1); wave 2 also F, so wave 3 takes its P tile (2, 3); wave 3 F's zero tile.
+    // The W1 and Btil fragments of column block w serve several tiles; all tiles of a wave are
+    // independent chains.
     {
         using Fr = Frag<SPLIT>;
         const Fr w1w = frag_t(W1, 16 * wave, 0, lane);   // W1 columns 16w ..
         const Fr bw = frag_t(Bm, 16 * wave, 0, lane);    // Btil columns 16w ..
-        f32x4 pa[4], ma[2], ea[2];
+        f32x4 pa[4], ma[2], ea[2], px = zero4();
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb)
-            pa[pb] = fmma(zero4(), pb == wave ? bw : frag_t(Bm, 16 * pb, 0, lane), w1w);
+            if (wave != 2 || pb != 3) pa[pb] = fmma(zero4(), pb == wave ? bw : frag_t(Bm, 16 * pb, 0, lane), w1w);
+        if (wave == 3) px = fmma(zero4(), frag_t(Bm, 48, 0, lane), frag_t(W1, 32, 0, lane));   // tile (2, 3)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             ma[tb] = fmma(zero4(), bw, frag_t(Zm, 16 * tb, 0, lane));
             ea[tb] = fmma(zero4(), w1w, frag_n(Mrb, 16 * tb, 0, lane));
         }
-        // P[j][j'] = (delta + sum_t W1[t][j] Btil[t][j']) gamma_last[j']; element (j', j), j = 16w + r
-        const int j = 16 * wave + r16;
+        // P[j][j'] = (delta + sum_t W1[t][j] Btil[t][j']) gamma_last[j']; element (j', j), j = 16 rb + r
+        auto pstore = [&](f32x4 v, int rb, int pb) {
+            const int j = 16 * rb + r16, jp0 = 16 * pb + 4 * g4;
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            const int jp0 = 16 * pb + 4 * g4;
+            for (int q = 0; q < 4; ++q) v[q] = (v[q] + (jp0 + q == j ? 1.f : 0.f)) * glast[jp0 + q];
+            tput4(ob + O::P, D * D, rb * 4 + pb, lane, v);
+        };
 #pragma unroll
-            for (int q = 0; q < 4; ++q) pa[pb][q] = (pa[pb][q] + (jp0 + q == j ? 1.f : 0.f)) * glast[jp0 + q];
-            tput4(ob + O::P, D * D, wave * 4 + pb, lane, pa[pb]);
-        }
+        for (int pb = 0; pb < 4; ++pb)
+            if (wave != 2 || pb != 3) pstore(pa[pb], wave, pb);
+        if (wave == 3) pstore(px, 2, 3);
         // M[t][j] = (sum_s Z[s][t] Btil[s][j] + Ktil[t][j]) gamma_last[j]; element (j, t), j = 16w + 4g + q
         // E[t][j] = Rhat[t][j] + sum_s Mrb[t][s] W1[s][j]; element (j, t)
         const int j0 = 16 * wave + 4 * g4;
