@@ -74,8 +74,10 @@ struct PrepSmem {
     static_assert(total <= 80 * 1024, "two workgroups per CU");
 };
 
+// Persistent: workgroup b takes items (head, chunk) b, b + gridDim.x, ...; the
+// next item's inputs load while the current one is processed.
 template <typename InT, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
+__global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p, int items) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using L = PrepSmem<SPLIT>;
     using M = Mat<SPLIT>;
@@ -84,16 +86,23 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
     constexpr int NT = 256;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
-    const int item = blockIdx.x;  // (head, chunk)
-    const int head = item / p.NC, c = item % p.NC;
-    const int bb = head / p.H, hh = head % p.H;
     const int64_t tstride = (int64_t)p.H * D;
-    const int t0 = c * C, Cc = min(C, p.T - t0);
-    const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
 
     RawChunk<NT, InT> raw;
-    raw.load(static_cast<const InT*>(p.w), static_cast<const InT*>(p.a), static_cast<const InT*>(p.r),
-             static_cast<const InT*>(p.b), static_cast<const InT*>(p.k), base, tstride, Cc, tid);
+    // raw <- the inputs of item `it` (tokens of a ragged last chunk: see RawChunk)
+    auto load_item = [&](int it) {
+        const int head = it / p.NC, c = it - head * p.NC;
+        const int bb = head / p.H, hh = head - bb * p.H;
+        const int t0 = c * C;
+        const int64_t base = ((int64_t)bb * p.T + t0) * tstride + (int64_t)hh * D;
+        raw.load(static_cast<const InT*>(p.w), static_cast<const InT*>(p.a), static_cast<const InT*>(p.r),
+                 static_cast<const InT*>(p.b), static_cast<const InT*>(p.k), base, tstride, min(C, p.T - t0), tid);
+    };
+    int item = blockIdx.x;
+    load_item(item);
+  for (;;) {
+    const int nitem = item + (int)gridDim.x;
+    const bool more = nitem < items;
 
     const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
     const M Bm = make_mat<SPLIT>(smem, L::Bm, C, D), Km = make_mat<SPLIT>(smem, L::Km, C, D);
@@ -110,6 +119,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
     const PrepOut<SPLIT> po{A, R, Bm, Km, A, A, A, A, true, true, true, true, false, false, false, false,
                             nullptr, glast};
     chunk_prep<NT, SPLIT>(raw, po, qp, tid);
+    load_item(more ? nitem : item);   // the last item loads itself again: no branch around the loads
     lds_barrier();
 
     // ---- Lab^T (fp32, for the inverse): one lower tile per wave 0-2, wave 3 the zero tile
@@ -240,6 +250,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p) {
             tput4(ob + O::F, C * C, 1, lane, zero4());   // (0, 1): u >= 16 > t
         }
     }
+    if (!more) break;
+    item = nitem;
+    lds_barrier();   // this item's last LDS reads before the next item's writes
+  }
 }
 
 // --------------------------------------------------------------------- scan
@@ -609,8 +623,16 @@ hipError_t launch_prepare_typed(const PrepArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
+    static int n_cu = 0;
+    if (n_cu == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
     const int items = a.B * a.H * a.NC;
-    hipLaunchKernelGGL(kern, dim3(items), dim3(256), L::total, s, a);
+    const int grid = items < 2 * n_cu ? items : 2 * n_cu;   // two workgroups per CU
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), L::total, s, a, items);
     return hipGetLastError();
 }
 
