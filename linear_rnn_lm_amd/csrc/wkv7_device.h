@@ -208,13 +208,6 @@ __device__ __forceinline__ void put4_pair(Mat<false> M, int m, int k8, f32x4 v, 
     put4(M, m, k8 + 4 * (g & 1), v);
 }
 
-__device__ __forceinline__ void put4_exact(Mat<true> M, int m, int k, f32x4 v) {
-    bf16x4 hi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hi[q] = (__bf16)v[q];
-    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(M.p) + m * M.ld + k) = hi;
-}
-__device__ __forceinline__ void put4_exact(Mat<false> M, int m, int k, f32x4 v) { put4(M, m, k, v); }
 
 // ---------------------------------------------------------------------------
 // acc += X[m0:m0+16, 0:K] * Y[n0:n0+16, 0:K]^T   (one wave, one 16x16 tile).
@@ -290,17 +283,6 @@ __device__ __forceinline__ void store_f32_t(float* M, int ld, f32x4 acc, int m0,
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = masked<MASK>(acc[q], m0 + 4 * g + q, n0 + r);
     *reinterpret_cast<f32x4*>(M + (n0 + r) * ld + m0 + 4 * g) = v;
-}
-
-// fp32 tile store into a plain row-major LDS array (stride ld floats)
-template <int MASK>
-__device__ __forceinline__ void store_f32(float* M, int ld, f32x4 acc, int m0, int n0, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int m = m0 + 4 * g + q, n = n0 + r;
-        M[m * ld + n] = masked<MASK>(acc[q], m, n);
-    }
 }
 
 // Zero the 16x16 block (m0.., k0..) of a matrix.
@@ -553,18 +535,6 @@ struct RawCols {
 };
 
 // ---------------------------------------------------------------------------
-// The chunk's C x C matrices.  Lab (strictly lower) goes to an fp32 array for
-// the triangular inverse; Lak (strict), Mrb, Mrk (lower) are stored as
-// operands, each in the orientation(s) the caller asks for (null = skip).
-// 12 lower tiles spread over the waves; the upper-right tiles are zeroed.
-// No barrier at the end.
-template <bool SPLIT, int NT>
-struct CcOut {
-    float* labf;  // null: Lab not wanted
-    Mat<SPLIT> lak, lakT, mrb, mrbT, mrk, mrkT;
-    bool has_lak, has_lakT, has_mrb, has_mrbT, has_mrk, has_mrkT;
-};
-
 // Store the three lower tiles of a C x C matrix as rows and/or transposed,
 // zeroing the upper-right tile.
 template <int MASK, bool SPLIT>
@@ -582,35 +552,6 @@ __device__ __forceinline__ void cc_store(Mat<SPLIT> Mr, bool rows_, Mat<SPLIT> M
         store_cols<MASK>(Mt, t11, 16, 16, lane);
         zero_block(Mt, 16, 0, lane);
     }
-}
-
-template <bool SPLIT, int NT>
-__device__ __forceinline__ void chunk_cc(Mat<SPLIT> A, Mat<SPLIT> R, Mat<SPLIT> B, Mat<SPLIT> K,
-                                         const CcOut<SPLIT, NT>& o, int tid) {
-    static_assert(NT == 256, "one matrix per wave");
-    const int lane = tid & 63, wave = tid >> 6;
-    // wave 3: Lab (A, B); wave 0: Lak (A, K); wave 1: Mrb (R, B); wave 2: Mrk (R, K)
-    const int mat = wave == 3 ? 0 : wave + 1;
-    if (mat == 0 && !o.labf) return;
-    if (mat == 3 && !o.has_mrk && !o.has_mrkT) return;
-    const Mat<SPLIT> X = mat < 2 ? A : R;
-    const Mat<SPLIT> Y = (mat & 1) ? K : B;
-    // lower tiles (0,0), (1,0), (1,1), computed together
-    f32x4 t00 = zero4(), t10 = zero4(), t11 = zero4();
-    t00 = mma<SPLIT, D>(t00, X, 0, Y, 0, lane);
-    t10 = mma<SPLIT, D>(t10, X, 16, Y, 0, lane);
-    t11 = mma<SPLIT, D>(t11, X, 16, Y, 16, lane);
-    if (mat == 0) {
-        store_f32<MASK_STRICT>(o.labf, LDF, t00, 0, 0, lane);
-        store_f32<MASK_STRICT>(o.labf, LDF, t10, 16, 0, lane);
-        store_f32<MASK_STRICT>(o.labf, LDF, t11, 16, 16, lane);
-        for (int e = lane; e < 256; e += 64) o.labf[(e >> 4) * LDF + 16 + (e & 15)] = 0.f;
-        return;
-    }
-    // one uniform branch per matrix: no run-time selection between the handles
-    if (mat == 1) cc_store<MASK_STRICT>(o.lak, o.has_lak, o.lakT, o.has_lakT, t00, t10, t11, lane);
-    else if (mat == 2) cc_store<MASK_LOWER>(o.mrb, o.has_mrb, o.mrbT, o.has_mrbT, t00, t10, t11, lane);
-    else cc_store<MASK_LOWER>(o.mrk, o.has_mrk, o.mrkT, o.has_mrkT, t00, t10, t11, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -660,24 +601,6 @@ __device__ __forceinline__ void tri_inverse(const float* LT, float* tf, float* s
 #pragma unroll
     for (int q = 0; q < 4; ++q) tf[(16 + 4 * g + q) * LDF + r] = acc[q];
     wave_lds_sync();
-}
-
-// Copy the fp32 C x C matrix tf into operand form: rows (T[t][s]) and/or
-// transposed (T[s][t]).  One wave.
-template <bool SPLIT>
-__device__ __forceinline__ void tinv_store(const float* tf, Mat<SPLIT> T, bool rows_, Mat<SPLIT> TT, bool trans,
-                                           int lane) {
-    // lane -> row t = lane / 2, columns 16*(lane%2) .. +15
-    const int t = lane >> 1, s0 = (lane & 1) * 16;
-#pragma unroll
-    for (int s4 = 0; s4 < 16; s4 += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(tf + t * LDF + s0 + s4);
-        if (rows_) put4(T, t, s0 + s4, v);
-        if (trans) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) put(TT, s0 + s4 + q, t, v[q]);
-        }
-    }
 }
 
 

@@ -140,12 +140,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p, int i
     f32x4 mk0 = zero4(), mk1 = zero4(), mk2 = zero4();
     if (wave == 3) {
         tri_inverse(labf, tf, scr, lane);
-        tinv_store<SPLIT>(tf, Tm, true, Tm, false, lane);
-        float* out = p.inv + (int64_t)item * C * C;
-        const int t = lane >> 1, s0 = (lane & 1) * 16;
-#pragma unroll
-        for (int s4 = 0; s4 < 16; s4 += 4)
-            *reinterpret_cast<f32x4*>(out + t * C + s0 + s4) = *reinterpret_cast<const f32x4*>(tf + t * LDF + s0 + s4);
     } else if (wave == 0) {
         const f32x4 t00 = mma<SPLIT, D>(zero4(), A, 0, Km, 0, lane);
         const f32x4 t10 = mma<SPLIT, D>(zero4(), A, 16, Km, 0, lane);
@@ -169,6 +163,15 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p, int i
                 mk2[q] = 0.f;
             }
         }
+    }
+    lds_barrier();
+
+    // ---- T to its operand rows and to memory: wave w rows 8w .. 8w + 7, four columns per lane
+    {
+        const int t = 8 * wave + (lane >> 3), s4 = 4 * (lane & 7);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tf + t * LDF + s4);
+        put4(Tm, t, s4, v);
+        *reinterpret_cast<f32x4*>(p.inv + (int64_t)item * C * C + t * C + s4) = v;
     }
     lds_barrier();
 
