@@ -43,7 +43,7 @@ def compile_source(src: str, out: str) -> str:
     """Compile one oracle C source into a shared object at ``out``."""
     tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
-           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, src, "-lpthread"]
+           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, src, "-lpthread", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -60,6 +60,10 @@ class OracleLib:
         lib.oracle_wkv7_fwd.restype = i
         lib.oracle_wkv7_bwd.argtypes = [i, i, i, i] + [dp] * 9 + [dp] * 7 + [i]
         lib.oracle_wkv7_bwd.restype = i
+        lib.oracle_proj_fwd.argtypes = [ctypes.c_long, i] + [dp] * 6
+        lib.oracle_proj_fwd.restype = i
+        lib.oracle_proj_bwd.argtypes = [ctypes.c_long, i] + [dp] * 9
+        lib.oracle_proj_bwd.restype = i
         self.lib = lib
         self.path = path
 
@@ -68,6 +72,12 @@ class OracleLib:
 
     def bwd(self, r, w, k, v, a, b, dy, h0=None, dhT=None, threads=None):
         return _bwd(self.lib, r, w, k, v, a, b, dy, h0, dhT, threads)
+
+    def proj_fwd(self, w_raw, kappa, alpha):
+        return _proj_fwd(self.lib, w_raw, kappa, alpha)
+
+    def proj_bwd(self, w_raw, kappa, alpha, dw, da, db):
+        return _proj_bwd(self.lib, w_raw, kappa, alpha, dw, da, db)
 
 
 def default() -> OracleLib:
@@ -110,6 +120,43 @@ def fwd(r, w, k, v, a, b, h0=None, want_ckpt=True, threads=None):
 def bwd(r, w, k, v, a, b, dy, h0=None, dhT=None, threads=None):
     """Backward with the default oracle build; see _bwd."""
     return default().bwd(r, w, k, v, a, b, dy, h0, dhT, threads)
+
+
+def proj_fwd(w_raw, kappa, alpha):
+    """Time-mix prologue with the default oracle build; see _proj_fwd."""
+    return default().proj_fwd(w_raw, kappa, alpha)
+
+
+def proj_bwd(w_raw, kappa, alpha, dw, da, db):
+    """Backward of the prologue with the default oracle build; see _proj_bwd."""
+    return default().proj_bwd(w_raw, kappa, alpha, dw, da, db)
+
+
+def _proj_fwd(lib, w_raw, kappa, alpha):
+    """(w, a, b) from raw projections of any shape (..., D): steps P1-P5 of
+    the C source's prologue comment."""
+    w_raw, kappa, alpha = (_as64(x) for x in (w_raw, kappa, alpha))
+    assert w_raw.shape == kappa.shape == alpha.shape
+    D = w_raw.shape[-1]
+    outs = [np.empty(w_raw.shape) for _ in range(3)]
+    rc = lib.oracle_proj_fwd(w_raw.size // D, D, *map(_ptr, (w_raw, kappa, alpha)), *map(_ptr, outs))
+    if rc != 0:
+        raise RuntimeError(f"oracle_proj_fwd failed with code {rc}")
+    return tuple(outs)
+
+
+def _proj_bwd(lib, w_raw, kappa, alpha, dw, da, db):
+    """(dw_raw, dkappa, dalpha) from the gradients on (w, a, b): steps Q1-Q4."""
+    w_raw, kappa, alpha, dw, da, db = (_as64(x) for x in (w_raw, kappa, alpha, dw, da, db))
+    for x in (kappa, alpha, dw, da, db):
+        assert x.shape == w_raw.shape
+    D = w_raw.shape[-1]
+    outs = [np.empty(w_raw.shape) for _ in range(3)]
+    rc = lib.oracle_proj_bwd(w_raw.size // D, D, *map(_ptr, (w_raw, kappa, alpha, dw, da, db)),
+                             *map(_ptr, outs))
+    if rc != 0:
+        raise RuntimeError(f"oracle_proj_bwd failed with code {rc}")
+    return tuple(outs)
 
 
 def _fwd(lib, r, w, k, v, a, b, h0=None, want_ckpt=True, threads=None):

@@ -45,6 +45,7 @@
  * Heads (b,h) are independent; the only parallelism here is one head per
  * worker thread.  Within a head the arithmetic is in the order written above.
  */
+#include <math.h>
 #include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
@@ -277,4 +278,78 @@ int oracle_wkv7_bwd(int B, int T, int H, int D,
     J.nthreads = nthreads;
     J.is_bwd = 1;
     return run_job(&J);
+}
+
+/*
+ * Time-mix prologue: w, a and b as functions of the layer's raw projections
+ * (w_raw, kappa, alpha), one token row of D channels at a time.  The pages
+ * print no formula for this step (they name the x070 architecture only); the
+ * definitions below are those of the synthetic workloads' w, a and b (a
+ * decay through a scaled sigmoid, a unit-norm removal key and a gated
+ * replacement key), read as the layer's own arithmetic:
+ *
+ *   P1  sw[j] = 1 / (1 + exp(-w_raw[j]))
+ *   P2  w[j]  = exp(-exp(-1/2) * sw[j])
+ *   P3  n     = sqrt(sum_j kappa[j]^2);  kh[j] = kappa[j] / n   (kh = 0 if n = 0)
+ *   P4  a[j]  = -kh[j]
+ *   P5  sa[j] = 1 / (1 + exp(-alpha[j]));  b[j] = kh[j] * sa[j]
+ *
+ * Backward, given dw, da, db (the chain rule through P1-P5):
+ *
+ *   Q1  dw_raw[j] = dw[j] * w[j] * (-exp(-1/2)) * sw[j] * (1 - sw[j])
+ *   Q2  g[j]      = -da[j] + db[j] * sa[j]              (gradient w.r.t. kh)
+ *   Q3  dalpha[j] = db[j] * kh[j] * sa[j] * (1 - sa[j])
+ *   Q4  dkappa[j] = (g[j] - kh[j] * sum_m kh[m] g[m]) / n   (0 if n = 0)
+ */
+static double logistic(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+int oracle_proj_fwd(long rows, int D, const double *w_raw, const double *kappa,
+                    const double *alpha, double *w, double *a, double *b)
+{
+    if (rows < 0 || D < 1) return 2;
+    const double c = exp(-0.5);
+    for (long row = 0; row < rows; ++row) {
+        const size_t o = (size_t)row * (size_t)D;
+        double nn = 0.0;
+        for (int j = 0; j < D; ++j) nn += kappa[o + j] * kappa[o + j];
+        const double n = sqrt(nn);
+        for (int j = 0; j < D; ++j) {
+            const double kh = n > 0.0 ? kappa[o + j] / n : 0.0;
+            w[o + j] = exp(-c * logistic(w_raw[o + j]));
+            a[o + j] = -kh;
+            b[o + j] = kh * logistic(alpha[o + j]);
+        }
+    }
+    return 0;
+}
+
+int oracle_proj_bwd(long rows, int D, const double *w_raw, const double *kappa,
+                    const double *alpha, const double *dw, const double *da,
+                    const double *db, double *dw_raw, double *dkappa, double *dalpha)
+{
+    if (rows < 0 || D < 1) return 2;
+    const double c = exp(-0.5);
+    for (long row = 0; row < rows; ++row) {
+        const size_t o = (size_t)row * (size_t)D;
+        double nn = 0.0;
+        for (int j = 0; j < D; ++j) nn += kappa[o + j] * kappa[o + j];
+        const double n = sqrt(nn);
+        double proj = 0.0;   /* sum_m kh[m] g[m] */
+        for (int j = 0; j < D; ++j) {
+            const double kh = n > 0.0 ? kappa[o + j] / n : 0.0;
+            const double sa = logistic(alpha[o + j]);
+            proj += kh * (-da[o + j] + db[o + j] * sa);
+        }
+        for (int j = 0; j < D; ++j) {
+            const double sw = logistic(w_raw[o + j]);
+            const double wj = exp(-c * sw);
+            dw_raw[o + j] = dw[o + j] * wj * (-c) * sw * (1.0 - sw);
+            const double kh = n > 0.0 ? kappa[o + j] / n : 0.0;
+            const double sa = logistic(alpha[o + j]);
+            const double g = -da[o + j] + db[o + j] * sa;
+            dalpha[o + j] = db[o + j] * kh * sa * (1.0 - sa);
+            dkappa[o + j] = n > 0.0 ? (g - kh * proj) / n : 0.0;
+        }
+    }
+    return 0;
 }

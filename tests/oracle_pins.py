@@ -29,6 +29,23 @@ What each check compares against (none of it re-types the recurrence):
 * ``adjoint``          -- <grad, delta> against a directional difference at
                           a larger shape.
 * ``autograd``         -- torch.autograd through a naive fp64 forward loop.
+
+The time-mix prologue (w, a, b from raw projections):
+
+* ``proj_identities``  -- facts of the logistic function and of a unit
+                          vector, not its formula: w(x) w(-x) = exp(-e^-1/2)
+                          and w(0)^2 equals it too; w decreases in w_raw and
+                          tends to 1 and exp(-e^-1/2); a has unit norm and
+                          points against kappa; a, b do not change when kappa
+                          is scaled; the gate b / (-a) does not depend on
+                          kappa, is 1/2 at alpha = 0 and g(x) + g(-x) = 1;
+                          kappa = 0 gives a = b = 0.
+* ``proj_finite_difference`` -- central differences of the (pinned) prologue
+                          against its backward, and the gradient w.r.t. kappa
+                          orthogonal to kappa (scale invariance).
+* ``proj_composed``    -- central differences of the whole layer (prologue,
+                          then the recurrence) against the chain of the two
+                          backwards, at a tiny shape.
 """
 from __future__ import annotations
 
@@ -243,6 +260,98 @@ def autograd(orc, seed=8):
     return err
 
 
+def proj_identities(orc, seed=9):
+    rng = np.random.default_rng(seed)
+    D = 8
+    x = rng.standard_normal((4, D)) * 3
+    kap = rng.standard_normal((4, D))
+    al = rng.standard_normal((4, D)) * 2
+    wp, ap, bp = orc.proj_fwd(x, kap, al)
+    wm, _, _ = orc.proj_fwd(-x, kap, al)
+    lim = np.exp(-np.exp(-0.5))
+    err = float(np.max(np.abs(wp * wm - lim)))
+    w0, _, _ = orc.proj_fwd(np.zeros((1, D)), kap[:1], al[:1])
+    err = max(err, float(np.max(np.abs(w0 * w0 - lim))))
+    ws, _, _ = orc.proj_fwd(np.linspace(-40, 40, D)[None, :], kap[:1], al[:1])
+    err = max(err, abs(ws[0, 0] - 1.0), abs(ws[0, -1] - lim))
+    if not np.all(np.diff(ws[0]) < 0):
+        err = max(err, 1.0)
+    err = max(err, float(np.max(np.abs(np.linalg.norm(ap, axis=-1) - 1.0))))
+    err = max(err, float(np.max(np.abs(np.sum(ap * kap, axis=-1) + np.linalg.norm(kap, axis=-1)))))
+    _, a3, b3 = orc.proj_fwd(x, 3.0 * kap, al)
+    err = max(err, float(np.max(np.abs(a3 - ap))), float(np.max(np.abs(b3 - bp))))
+    kap2 = rng.standard_normal((4, D))
+    _, a2, b2 = orc.proj_fwd(x, kap2, al)
+    gate, gate2 = bp / -ap, b2 / -a2
+    err = max(err, float(np.max(np.abs(gate - gate2))))
+    _, am, bm = orc.proj_fwd(x, kap, -al)
+    err = max(err, float(np.max(np.abs(gate + bm / -am - 1.0))))
+    _, ah, bh = orc.proj_fwd(x, kap, np.zeros_like(al))
+    err = max(err, float(np.max(np.abs(bh / -ah - 0.5))))
+    _, az, bz = orc.proj_fwd(x[:1], np.zeros((1, D)), al[:1])
+    err = max(err, float(np.max(np.abs(az))), float(np.max(np.abs(bz))))
+    return err
+
+
+def _proj_loss(orc, raws, cw, ca, cb):
+    w, a, b = orc.proj_fwd(*raws)
+    return float(np.sum(w * cw) + np.sum(a * ca) + np.sum(b * cb))
+
+
+def proj_finite_difference(orc, seed=10):
+    rng = np.random.default_rng(seed)
+    shape = (3, 6)
+    raws = [rng.standard_normal(shape) * s for s in (2.0, 1.0, 2.0)]
+    cw, ca, cb = (rng.standard_normal(shape) for _ in range(3))
+    grads = orc.proj_bwd(*raws, cw, ca, cb)
+    eps = 1e-6
+    err = 0.0
+    for n in range(3):
+        num = np.zeros(shape)
+        for idx in np.ndindex(*shape):
+            p = [x.copy() for x in raws]
+            p[n][idx] += eps
+            m = [x.copy() for x in raws]
+            m[n][idx] -= eps
+            num[idx] = (_proj_loss(orc, p, cw, ca, cb) - _proj_loss(orc, m, cw, ca, cb)) / (2 * eps)
+        err = max(err, rel(grads[n], num))
+    # a and b depend on kappa only through its direction
+    err = max(err, float(np.max(np.abs(np.sum(grads[1] * raws[1], axis=-1)))))
+    return err
+
+
+def proj_composed(orc, seed=11):
+    rng = np.random.default_rng(seed)
+    B, T, H, D = 1, 5, 1, 6
+    r = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, T, H, D)) * 0.5
+    v = rng.standard_normal((B, T, H, D))
+    raws = [rng.standard_normal((B, T, H, D)) for _ in range(3)]
+    h0 = rng.standard_normal((B, H, D, D)) * 0.3
+    dy = rng.standard_normal((B, T, H, D))
+    dhT = rng.standard_normal((B, H, D, D))
+
+    def loss(rw):
+        w, a, b = orc.proj_fwd(*rw)
+        return _loss(orc, [r, w, k, v, a, b], h0, dy, dhT)
+
+    w, a, b = orc.proj_fwd(*raws)
+    g = orc.bwd(r, w, k, v, a, b, dy, h0, dhT)
+    chain = orc.proj_bwd(*raws, g[1], g[4], g[5])
+    eps = 1e-6
+    err = 0.0
+    for n in range(3):
+        num = np.zeros(raws[n].shape)
+        for idx in np.ndindex(*raws[n].shape):
+            p = [x.copy() for x in raws]
+            p[n][idx] += eps
+            m = [x.copy() for x in raws]
+            m[n][idx] -= eps
+            num[idx] = (loss(p) - loss(m)) / (2 * eps)
+        err = max(err, rel(chain[n], num))
+    return err
+
+
 ALL = {
     "t1_closed_form": t1_closed_form,
     "linear_attention": linear_attention,
@@ -252,6 +361,9 @@ ALL = {
     "finite_difference": finite_difference,
     "adjoint": adjoint,
     "autograd": autograd,
+    "proj_identities": proj_identities,
+    "proj_finite_difference": proj_finite_difference,
+    "proj_composed": proj_composed,
 }
 
 # tolerance of each check for a correct fp64 oracle
@@ -264,4 +376,7 @@ TOL = {
     "finite_difference": 1e-7,
     "adjoint": 1e-6,
     "autograd": 1e-12,
+    "proj_identities": 1e-14,
+    "proj_finite_difference": 1e-7,
+    "proj_composed": 1e-7,
 }

@@ -37,6 +37,22 @@ MUTATIONS = [
     ("g_carry_uses_b", "g[i * D + j] = wt[j] * g[i * D + j] + dsa[i] * at[j];",
      "g[i * D + j] = wt[j] * g[i * D + j] + dsa[i] * bt[j];"),
     ("dhT_ignored", "if (J->dhT) memcpy(g,", "if (0) memcpy(g,"),
+    ("proj_w_sign", "w[o + j] = exp(-c * logistic(w_raw[o + j]));", "w[o + j] = exp(c * logistic(w_raw[o + j]));"),
+    ("proj_w_no_scale", "w[o + j] = exp(-c * logistic(w_raw[o + j]));", "w[o + j] = exp(-logistic(w_raw[o + j]));"),
+    ("proj_a_sign", "a[o + j] = -kh;", "a[o + j] = kh;"),
+    ("proj_b_ungated", "b[o + j] = kh * logistic(alpha[o + j]);", "b[o + j] = kh;"),
+    ("proj_b_gate_flipped", "b[o + j] = kh * logistic(alpha[o + j]);", "b[o + j] = kh * logistic(-alpha[o + j]);"),
+    ("proj_norm_squared", "const double n = sqrt(nn);\n        for (int j = 0; j < D; ++j) {\n            const double kh",
+     "const double n = nn;\n        for (int j = 0; j < D; ++j) {\n            const double kh"),
+    ("proj_dw_raw_sign", "dw_raw[o + j] = dw[o + j] * wj * (-c) * sw * (1.0 - sw);",
+     "dw_raw[o + j] = dw[o + j] * wj * c * sw * (1.0 - sw);"),
+    ("proj_dw_raw_no_w", "dw_raw[o + j] = dw[o + j] * wj * (-c) * sw * (1.0 - sw);",
+     "dw_raw[o + j] = dw[o + j] * (-c) * sw * (1.0 - sw);"),
+    ("proj_g_sign", "const double g = -da[o + j] + db[o + j] * sa;", "const double g = da[o + j] + db[o + j] * sa;"),
+    ("proj_dalpha_no_kh", "dalpha[o + j] = db[o + j] * kh * sa * (1.0 - sa);",
+     "dalpha[o + j] = db[o + j] * sa * (1.0 - sa);"),
+    ("proj_dkappa_no_projection", "dkappa[o + j] = n > 0.0 ? (g - kh * proj) / n : 0.0;",
+     "dkappa[o + j] = n > 0.0 ? g / n : 0.0;"),
 ]
 
 
