@@ -246,6 +246,55 @@ wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype,
                                 const float *h0, float *y, float *h_ckpt, float *hT,
                                 void *stream);
 
+/*
+ * The layer with its time-mix prologue: w, a and b are not passed but formed
+ * inside the kernels' loads from the layer's raw projections, per token and
+ * head (the pages print no formula for this step; these are the definitions
+ * of RWKV-7's decay, removal key and replacement key that the workloads use,
+ * read as the layer's own arithmetic):
+ *
+ *     w[j] = exp(-e^-1/2 * sigmoid(w_raw[j]))
+ *     kh   = kappa / |kappa|        (L2 norm over the head's D channels;
+ *                                    a zero kappa gives kh = 0)
+ *     a    = -kh,   b[j] = kh[j] * sigmoid(alpha[j])
+ *
+ * w_raw, kappa and alpha are (B,T,H,D) in_dtype, like r, k, v; w never exists
+ * in memory, so the decay-range rule above is met by construction.
+ *
+ * wkv7_fwd_proj: as wkv7_fwd with (w_raw, kappa, alpha) in place of (w, a, b);
+ * it always runs the chunked path, so `workspace` must hold
+ * wkv7_chunk_ops_bytes(B,T,H,D) bytes for every T (not
+ * wkv7_fwd_workspace_bytes, which is 0 for T == 1).
+ */
+wkv7_status wkv7_fwd_proj(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                          const void *r, const void *w_raw, const void *k,
+                          const void *v, const void *kappa, const void *alpha,
+                          const float *h0, float *y, float *h_ckpt, float *hT,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * wkv7_bwd_proj: as wkv7_bwd with (w_raw, kappa, alpha) in place of (w, a, b)
+ * and the chain rule through the prologue applied before the stores:
+ *
+ *     dw_raw[j] = dw[j] * w[j] * (-e^-1/2) * s(1 - s),  s = sigmoid(w_raw[j])
+ *     g         = -da + db * sigmoid(alpha)              (gradient w.r.t. kh)
+ *     dkappa    = (g - kh (kh . g)) / |kappa|            (0 for kappa = 0)
+ *     dalpha[j] = db[j] * kh[j] * s(1 - s),  s = sigmoid(alpha[j])
+ *
+ * dw_raw, dkappa, dalpha take the places of dw, da, db (fp32, required); the
+ * other arguments and the workspace are as for wkv7_bwd, h_ckpt from
+ * wkv7_fwd_proj.
+ */
+wkv7_status wkv7_bwd_proj(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                          const float *dy, const float *dhT,
+                          const void *r, const void *w_raw, const void *k,
+                          const void *v, const void *kappa, const void *alpha,
+                          const float *h_ckpt,
+                          float *dr, float *dw_raw, float *dk, float *dv,
+                          float *dkappa, float *dalpha, float *dh0,
+                          void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,10 @@ def lib():
         L.wkv7_bwd_scan.restype = i
         L.wkv7_bwd_inputs.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] * 3 + [vp] * 5 + [vp]
         L.wkv7_bwd_inputs.restype = i
+        L.wkv7_fwd_proj.argtypes = L.wkv7_fwd.argtypes
+        L.wkv7_fwd_proj.restype = i
+        L.wkv7_bwd_proj.argtypes = L.wkv7_bwd.argtypes
+        L.wkv7_bwd_proj.restype = i
         _lib = L
     return _lib
 
@@ -215,6 +219,39 @@ def bwd(dy, r, w, k, v, a, b, ckpt, dhT=None, *, want_dh0=True, workspace=None, 
                         *map(_ptr, (r, w, k, v, a, b)), _ptr(ckpt), *map(_ptr, out), _ptr(dh0),
                         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check("wkv7_bwd", st)
+    return (*out, dh0)
+
+
+def fwd_proj(r, w_raw, k, v, kappa, alpha, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
+             y=None, ckpt=None, hT=None, workspace=None):
+    """Forward of the layer with its time-mix prologue (w, a, b formed in the
+    kernels from w_raw, kappa, alpha; see wkv7_fwd_proj).  Returns (y, ckpt, hT)."""
+    B, T, H, D = _shape(r)
+    y, ckpt, hT = _fwd_outputs(r, want_y, want_ckpt, want_hT, y, ckpt, hT)
+    if workspace is None:
+        workspace = _f32_bytes(chunk_ops_bytes(B, T, H, D), r.device)
+    st = lib().wkv7_fwd_proj(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w_raw, k, v, kappa, alpha)), _ptr(h0),
+                             _ptr(y), _ptr(ckpt), _ptr(hT), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(r.device))
+    _check("wkv7_fwd_proj", st)
+    return y, ckpt, hT
+
+
+def bwd_proj(dy, r, w_raw, k, v, kappa, alpha, ckpt, dhT=None, *, want_dh0=True, workspace=None, out=None):
+    """Backward of ``fwd_proj``: (dr, dw_raw, dk, dv, dkappa, dalpha, dh0), fp32."""
+    import torch
+    B, T, H, D = _shape(r)
+    dev = r.device
+    f32 = dict(device=dev, dtype=torch.float32)
+    if out is None:
+        out = [torch.empty((B, T, H, D), **f32) for _ in range(6)]
+    dh0 = torch.empty((B, H, D, D), **f32) if want_dh0 else None
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(B, T, H, D) // 4, **f32)
+    st = lib().wkv7_bwd_proj(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
+                             *map(_ptr, (r, w_raw, k, v, kappa, alpha)), _ptr(ckpt), *map(_ptr, out), _ptr(dh0),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("wkv7_bwd_proj", st)
     return (*out, dh0)
 
 

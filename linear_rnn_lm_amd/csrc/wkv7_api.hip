@@ -138,14 +138,15 @@ wkv7_status status_of(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ER
 int64_t inv_bytes(const Sizes& sz) { return sz.heads * sz.nc * kChunk * kChunk * 4; }
 int64_t ops_bytes(const Sizes& sz) { return inv_bytes(sz) + sz.heads * sz.nc * wkv7::kOpsBytes; }
 
-wkv7_status launch_prepare(int B, int T, int H, const Sizes& sz, bool bf16, const void* r, const void* w,
-                           const void* k, const void* a, const void* b, void* chunk_ops, hipStream_t s) {
+wkv7_status launch_prepare(int B, int T, int H, const Sizes& sz, bool bf16, bool proj, const void* r,
+                           const void* w, const void* k, const void* a, const void* b, void* chunk_ops,
+                           hipStream_t s) {
     wkv7::PrepArgs pa;
     pa.r = r; pa.w = w; pa.k = k; pa.a = a; pa.b = b;
     pa.inv = static_cast<float*>(chunk_ops);
     pa.ops = static_cast<char*>(chunk_ops) + inv_bytes(sz);
     pa.B = B; pa.T = T; pa.H = H; pa.NC = (int)sz.nc;
-    return status_of(wkv7::launch_chunk_prepare(pa, bf16, s));
+    return status_of(wkv7::launch_chunk_prepare(pa, bf16, proj, s));
 }
 
 wkv7_status launch_scan(int B, int T, int H, const Sizes& sz, bool bf16, bool bwd, const void* x,
@@ -215,7 +216,7 @@ wkv7_status wkv7_chunk_prepare(int B, int T, int H, int D, wkv7_dtype in_dtype, 
     if (st != WKV7_OK) return st;
     st = check_alias(bufs, 6);
     if (st != WKV7_OK) return st;
-    return launch_prepare(B, T, H, sz, in_dtype == WKV7_BF16, r, w, k, a, b, chunk_ops,
+    return launch_prepare(B, T, H, sz, in_dtype == WKV7_BF16, false, r, w, k, a, b, chunk_ops,
                           static_cast<hipStream_t>(stream));
 }
 
@@ -239,7 +240,12 @@ wkv7_status wkv7_fwd_scan(int B, int T, int H, int D, wkv7_dtype in_dtype, const
                        static_cast<hipStream_t>(stream));
 }
 
-wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
+}  // extern "C"
+
+namespace {
+
+// wkv7_fwd and wkv7_fwd_proj (proj: w, a, b hold w_raw, kappa, alpha; always chunked)
+wkv7_status fwd_impl(int B, int T, int H, int D, wkv7_dtype in_dtype, bool proj, const void* r, const void* w,
                      const void* k, const void* v, const void* a, const void* b, const float* h0,
                      float* y, float* h_ckpt, float* hT, void* workspace, size_t workspace_bytes,
                      void* stream) {
@@ -248,7 +254,7 @@ wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const void
     if (st != WKV7_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = in_dtype == WKV7_BF16;
-    if (T <= kSequentialMaxT) {
+    if (!proj && T <= kSequentialMaxT) {
         const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, nullptr, h0, y, h_ckpt, hT);
         return status_of(wkv7::launch_fwd_sequential(fa, bf16, s));
     }
@@ -262,9 +268,69 @@ wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const void
                           {hT, sz.state_elems * 4, false, true}, {workspace, ops_bytes(sz), true, true}};
     st = check_alias(bufs, 11, h0, hT);
     if (st != WKV7_OK) return st;
-    st = launch_prepare(B, T, H, sz, bf16, r, w, k, a, b, workspace, s);
+    st = launch_prepare(B, T, H, sz, bf16, proj, r, w, k, a, b, workspace, s);
     if (st != WKV7_OK) return st;
     return launch_scan(B, T, H, sz, bf16, false, v, workspace, h0, y, h_ckpt, hT, s);
+}
+
+// wkv7_bwd and wkv7_bwd_proj (proj: w, a, b hold w_raw, kappa, alpha, and dw, da, db
+// receive dw_raw, dkappa, dalpha)
+wkv7_status bwd_impl(int B, int T, int H, int D, wkv7_dtype in_dtype, bool proj, const float* dy,
+                     const float* dhT, const void* r, const void* w, const void* k, const void* v, const void* a,
+                     const void* b, const float* h_ckpt, float* dr, float* dw, float* dk, float* dv,
+                     float* da, float* db, float* dh0, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    wkv7_status st = check_dtype(in_dtype);
+    if (st != WKV7_OK) return st;
+    Sizes sz;
+    st = check_shape(B, T, H, D, &sz);
+    if (st != WKV7_OK) return st;
+    const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
+    const int64_t c32 = sz.ckpt_elems * 4;
+    const int64_t need = c32 + ops_bytes(sz);
+    const Buf bufs[17] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
+                          {w, tin, true, false},  {k, tin, true, false},    {v, tin, true, false},
+                          {a, tin, true, false},  {b, tin, true, false},    {h_ckpt, c32, true, false},
+                          {dr, t32, true, true},  {dw, t32, true, true},    {dk, t32, true, true},
+                          {dv, t32, true, true},  {da, t32, true, true},    {db, t32, true, true},
+                          {dh0, s32, false, true}, {workspace, need, false, true}};
+    st = check_bufs(bufs, 17);
+    if (st != WKV7_OK) return st;
+    if (!workspace || workspace_bytes < (size_t)need) return WKV7_ERR_WORKSPACE;
+    st = check_alias(bufs, 17);
+    if (st != WKV7_OK) return st;
+    float* gbuf = static_cast<float*>(workspace);
+    void* ops = gbuf + sz.ckpt_elems;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = in_dtype == WKV7_BF16;
+    st = launch_prepare(B, T, H, sz, bf16, proj, r, w, k, a, b, ops, s);
+    if (st != WKV7_OK) return st;
+    st = launch_scan(B, T, H, sz, bf16, true, dy, ops, dhT, dv, gbuf, dh0, s);
+    if (st != WKV7_OK) return st;
+    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, static_cast<const float*>(ops), h_ckpt,
+                                gbuf);
+    ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.da = da; ba.db = db;
+    return status_of(wkv7::launch_bwd_inputs(ba, bf16, proj, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
+                     const void* k, const void* v, const void* a, const void* b, const float* h0,
+                     float* y, float* h_ckpt, float* hT, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    return fwd_impl(B, T, H, D, in_dtype, false, r, w, k, v, a, b, h0, y, h_ckpt, hT, workspace, workspace_bytes,
+                    stream);
+}
+
+wkv7_status wkv7_fwd_proj(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w_raw,
+                          const void* k, const void* v, const void* kappa, const void* alpha, const float* h0,
+                          float* y, float* h_ckpt, float* hT, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return fwd_impl(B, T, H, D, in_dtype, true, r, w_raw, k, v, kappa, alpha, h0, y, h_ckpt, hT, workspace,
+                    workspace_bytes, stream);
 }
 
 wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r,
@@ -321,7 +387,7 @@ wkv7_status wkv7_bwd_inputs(int B, int T, int H, int D, wkv7_dtype in_dtype, con
     wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, static_cast<const float*>(chunk_ops),
                                 h_ckpt, const_cast<float*>(dh_ckpt));
     ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.da = da; ba.db = db;
-    return status_of(wkv7::launch_bwd_inputs(ba, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
+    return status_of(wkv7::launch_bwd_inputs(ba, in_dtype == WKV7_BF16, false, static_cast<hipStream_t>(stream)));
 }
 
 wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy, const float* dhT,
@@ -329,37 +395,17 @@ wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const floa
                      const void* b, const float* h_ckpt, float* dr, float* dw, float* dk, float* dv,
                      float* da, float* db, float* dh0, void* workspace, size_t workspace_bytes,
                      void* stream) {
-    wkv7_status st = check_dtype(in_dtype);
-    if (st != WKV7_OK) return st;
-    Sizes sz;
-    st = check_shape(B, T, H, D, &sz);
-    if (st != WKV7_OK) return st;
-    const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
-    const int64_t c32 = sz.ckpt_elems * 4;
-    const int64_t need = c32 + ops_bytes(sz);
-    const Buf bufs[17] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
-                          {w, tin, true, false},  {k, tin, true, false},    {v, tin, true, false},
-                          {a, tin, true, false},  {b, tin, true, false},    {h_ckpt, c32, true, false},
-                          {dr, t32, true, true},  {dw, t32, true, true},    {dk, t32, true, true},
-                          {dv, t32, true, true},  {da, t32, true, true},    {db, t32, true, true},
-                          {dh0, s32, false, true}, {workspace, need, false, true}};
-    st = check_bufs(bufs, 17);
-    if (st != WKV7_OK) return st;
-    if (!workspace || workspace_bytes < (size_t)need) return WKV7_ERR_WORKSPACE;
-    st = check_alias(bufs, 17);
-    if (st != WKV7_OK) return st;
-    float* gbuf = static_cast<float*>(workspace);
-    void* ops = gbuf + sz.ckpt_elems;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool bf16 = in_dtype == WKV7_BF16;
-    st = launch_prepare(B, T, H, sz, bf16, r, w, k, a, b, ops, s);
-    if (st != WKV7_OK) return st;
-    st = launch_scan(B, T, H, sz, bf16, true, dy, ops, dhT, dv, gbuf, dh0, s);
-    if (st != WKV7_OK) return st;
-    wkv7::BwdArgs ba = bwd_args(B, T, H, sz, dy, dhT, r, w, k, v, a, b, static_cast<const float*>(ops), h_ckpt,
-                                gbuf);
-    ba.dr = dr; ba.dw = dw; ba.dk = dk; ba.da = da; ba.db = db;
-    return status_of(wkv7::launch_bwd_inputs(ba, bf16, s));
+    return bwd_impl(B, T, H, D, in_dtype, false, dy, dhT, r, w, k, v, a, b, h_ckpt, dr, dw, dk, dv, da, db, dh0,
+                    workspace, workspace_bytes, stream);
+}
+
+wkv7_status wkv7_bwd_proj(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy, const float* dhT,
+                          const void* r, const void* w_raw, const void* k, const void* v, const void* kappa,
+                          const void* alpha, const float* h_ckpt, float* dr, float* dw_raw, float* dk, float* dv,
+                          float* dkappa, float* dalpha, float* dh0, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return bwd_impl(B, T, H, D, in_dtype, true, dy, dhT, r, w_raw, k, v, kappa, alpha, h_ckpt, dr, dw_raw, dk, dv,
+                    dkappa, dalpha, dh0, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

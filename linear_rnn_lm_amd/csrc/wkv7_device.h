@@ -82,6 +82,29 @@ __device__ __forceinline__ float sum_stride8(float x) {
 // 1/x with v_rcp_f32 (at most 1 ulp off).
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Sum over the 32 lanes of a half wave (lanes 0-31 or 32-63), returned in all
+// of them; VALU only.  Rotations by 8, 4, 2, 1 inside each DPP row of 16 leave
+// the row's sum in every lane of the row; permlane16_swap then adds each row
+// to its neighbour (see sum_stride8).
+__device__ __forceinline__ float half_sum32(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
+// Time-mix prologue (w, a, b from the layer's raw projections w_raw, kappa,
+// alpha): w = exp(-e^-1/2 sigmoid(w_raw)), a = -kappa / |kappa|,
+// b = kappa / |kappa| * sigmoid(alpha), the norm over the head's D channels
+// (a zero kappa gives a = b = 0).  e^x is v_exp_f32 (2^x, 1 ulp) of x log2(e).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kDecayScale = 0.60653065971263342f;   // e^-1/2
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float logistic_f(float x) { return rcp(1.f + exp_f(-x)); }
+__device__ __forceinline__ float proj_decay(float x) { return exp_f(-kDecayScale * logistic_f(x)); }
+
 // One MFMA step: 16x16 tile, accumulator c (fp32).
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -342,14 +365,18 @@ struct Pair<float> {
 // holds columns 2*jp, 2*jp+1 (jp = tid % 32) of tokens q*TPG .. q*TPG+TPG-1
 // (q = tid / 32) for w, a, r, b, k.  Tokens at or beyond `cc` (the chunk's
 // length) read the last valid token and are replaced at use: w = 1, the
-// rest 0.
-template <int NT, typename InT>
+// rest 0.  With PROJ the w, a, b slots hold the raw projections w_raw, kappa,
+// alpha, and fw, fa, fb apply the prologue; finish() must run first (once the
+// loads have landed) to form each token's 1 / |kappa| from the 32 lanes that
+// share the token.
+template <int NT, typename InT, bool PROJ = false>
 struct RawChunk {
     static constexpr int NG = NT / 32;
     static constexpr int TPG = C / NG;
     static_assert(NT % 32 == 0 && C % NG == 0 && TPG >= 1, "raw chunk thread shape");
     using W = typename Pair<InT>::T;
     W w[TPG], a[TPG], r[TPG], b[TPG], k[TPG];
+    float inv[PROJ ? TPG : 1];   // PROJ: 1 / |kappa| of each token (0 for kappa = 0)
     int cc;
 
     __device__ __forceinline__ void load(const InT* pw, const InT* pa, const InT* pr, const InT* pb,
@@ -371,6 +398,48 @@ struct RawChunk {
     __device__ __forceinline__ float2 get(const W& x, int tt, int tid, float fill) const {
         return valid(tt, tid) ? Pair<InT>::f(x) : make_float2(fill, fill);
     }
+    __device__ __forceinline__ void finish() {
+        if constexpr (PROJ) {
+#pragma unroll
+            for (int tt = 0; tt < TPG; ++tt) {
+                const float2 kv = Pair<InT>::f(a[tt]);
+                const float ss = half_sum32(kv.x * kv.x + kv.y * kv.y);
+                inv[tt] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+            }
+        }
+    }
+    __device__ __forceinline__ float2 fw(int tt, int tid) const {
+        if constexpr (PROJ) {
+            const float2 x = Pair<InT>::f(w[tt]);
+            return valid(tt, tid) ? make_float2(proj_decay(x.x), proj_decay(x.y)) : make_float2(1.f, 1.f);
+        } else {
+            return get(w[tt], tt, tid, 1.f);
+        }
+    }
+    // kappa / |kappa| (PROJ only)
+    __device__ __forceinline__ float2 kappa_hat(int tt) const {
+        const float2 x = Pair<InT>::f(a[tt]);
+        return make_float2(x.x * inv[tt], x.y * inv[tt]);
+    }
+    __device__ __forceinline__ float2 fa(int tt, int tid) const {
+        if constexpr (PROJ) {
+            const float2 kh = kappa_hat(tt);
+            return valid(tt, tid) ? make_float2(-kh.x, -kh.y) : make_float2(0.f, 0.f);
+        } else {
+            return get(a[tt], tt, tid, 0.f);
+        }
+    }
+    __device__ __forceinline__ float2 fb(int tt, int tid) const {
+        if constexpr (PROJ) {
+            const float2 kh = kappa_hat(tt), al = Pair<InT>::f(b[tt]);
+            return valid(tt, tid) ? make_float2(kh.x * logistic_f(al.x), kh.y * logistic_f(al.y))
+                                  : make_float2(0.f, 0.f);
+        } else {
+            return get(b[tt], tt, tid, 0.f);
+        }
+    }
+    __device__ __forceinline__ float2 fr(int tt, int tid) const { return get(r[tt], tt, tid, 0.f); }
+    __device__ __forceinline__ float2 fk(int tt, int tid) const { return get(k[tt], tt, tid, 0.f); }
 };
 
 // Where chunk_prep writes.  Null handles are skipped.
@@ -386,18 +455,18 @@ constexpr int LDG = 68;           // row stride of the fp32 gamma array
 
 // Chunk preparation from the registers of RawChunk: gamma (cumulative product
 // of w within the chunk), the scaled operands, gamma_last.  `qp` is LDS
-// scratch of NG x 64 floats.  Contains one barrier; the caller must barrier
-// before the outputs are read.
-template <int NT, bool SPLIT, typename InT>
-__device__ __forceinline__ void chunk_prep(const RawChunk<NT, InT>& raw, const PrepOut<SPLIT>& o, float* qp,
+// scratch of NG x 64 floats.  Contains two barriers; the caller must barrier
+// before the outputs are read.  With PROJ, raw.finish() must have run.
+template <int NT, bool SPLIT, typename InT, bool PROJ>
+__device__ __forceinline__ void chunk_prep(const RawChunk<NT, InT, PROJ>& raw, const PrepOut<SPLIT>& o, float* qp,
                                            int tid) {
-    constexpr int NG = RawChunk<NT, InT>::NG, TPG = RawChunk<NT, InT>::TPG;
+    constexpr int NG = RawChunk<NT, InT, PROJ>::NG, TPG = RawChunk<NT, InT, PROJ>::TPG;
     const int jp = tid & 31, q = tid >> 5, j0 = 2 * jp;
     float2 loc[TPG];
     float2 p = make_float2(1.f, 1.f);
 #pragma unroll
     for (int tt = 0; tt < TPG; ++tt) {
-        const float2 wv = raw.get(raw.w[tt], tt, tid, 1.f);
+        const float2 wv = raw.fw(tt, tid);
         p.x *= wv.x;
         p.y *= wv.y;
         loc[tt] = p;
@@ -430,8 +499,8 @@ __device__ __forceinline__ void chunk_prep(const RawChunk<NT, InT>& raw, const P
         const int t = q * TPG + tt;
         const float2 g = (q == 0) ? loc[tt] : make_float2(pre.x * loc[tt].x, pre.y * loc[tt].y);
         const float ix = rcp(g.x), iy = rcp(g.y);
-        const float2 av = raw.get(raw.a[tt], tt, tid, 0.f), rv = raw.get(raw.r[tt], tt, tid, 0.f);
-        const float2 bv = raw.get(raw.b[tt], tt, tid, 0.f), kv = raw.get(raw.k[tt], tt, tid, 0.f);
+        const float2 av = raw.fa(tt, tid), rv = raw.fr(tt, tid);
+        const float2 bv = raw.fb(tt, tid), kv = raw.fk(tt, tid);
         const float ax = av.x * gprev.x, ay = av.y * gprev.y;
         const float rx = rv.x * g.x, ry = rv.y * g.y;
         const float bx = bv.x * ix, by = bv.y * iy;

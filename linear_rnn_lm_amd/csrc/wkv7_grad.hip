@@ -73,6 +73,9 @@ struct GradSmem {
     static constexpr int DSA = U + RM;               // DSA rows (t, i)
     static constexpr int total = DSA + RM;
     static_assert(total <= 160 * 1024, "gradient kernel LDS exceeds 160 KiB");
+    // with the time-mix prologue, da and db (fp32 [t][j], stride LDG) pass from phase 5 to
+    // phase 6 in the U and DSA rows
+    static_assert(C * LDG * 4 <= RM, "da / db do not fit the U / DSA rows");
 };
 
 template <bool SPLIT>
@@ -129,11 +132,11 @@ struct ChunkSrc {
 // loads are issued in five parts, one per compute phase, so that no wave
 // stalls on a full memory queue; buffer loads without branches keep the
 // wave's count of outstanding loads exact.
-template <typename InT>
+template <typename InT, bool PROJ>
 struct GradIn {
     using W = typename Pair<InT>::T;
     static constexpr int ES = sizeof(InT);
-    RawChunk<GNT, InT> raw;          // w, a, r, b, k
+    RawChunk<GNT, InT, PROJ> raw;    // w, a, r, b, k (PROJ: w_raw, kappa, r, alpha, k)
     RawCols<GNT, D, InT> rv;         // v
     RawCols<GNT, D, float> rdy;      // dy
     f32x4 s0v[2], gev[2];            // S0, Ge (gradient at the chunk's end): row si, 8 columns
@@ -157,7 +160,7 @@ struct GradIn {
     }
     // w, a, r, b, k: columns 2 jp, 2 jp + 1 of tokens q TPG + tt
     __device__ __forceinline__ void raw_part(W* dst, const void* src, const BwdArgs& p, const ChunkSrc& s, int tid) {
-        constexpr int TPG = RawChunk<GNT, InT>::TPG;
+        constexpr int TPG = RawChunk<GNT, InT, PROJ>::TPG;
         const Rsrc r = tok(src, p, s, ES);
         const int jp = tid & 31, q = tid >> 5, HD = p.H * D;
 #pragma unroll
@@ -207,7 +210,7 @@ struct GradIn {
 
 // Persistent: each workgroup takes chunks blockIdx.x, + gridDim.x, ... of the
 // total; while it works on one chunk the next chunk's inputs are loading.
-template <typename InT, bool SPLIT>
+template <typename InT, bool SPLIT, bool PROJ>
 __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using L = GradSmem<SPLIT>;
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     const int si = tid >> 3, sj0 = (tid & 7) * 8;
 
     int idx = blockIdx.x;
-    GradIn<InT> cur, nxt;
+    GradIn<InT, PROJ> cur, nxt;
     cur.issue_all(p, ChunkSrc(p, ChunkPos(p, idx, xcd != 0), true), tid);
     // The first chunk needs these at once.  Waiting here also leaves nothing
     // pending on entry to the loop, so the compiler sizes the loop's waits for
@@ -260,6 +263,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
 
     const PrepOut<SPLIT> po{A, R, Bm, Km, A, A, A, A, true, true, true, true, false, false, false, false,
                             gam, glast};
+    cur.raw.finish();
     chunk_prep<GNT, SPLIT>(cur.raw, po, qp, tid);
     cur.rv.template store_rows<SPLIT, true>(Vm, tid);
     cur.rdy.template store_rows<SPLIT, false>(DYm, tid);
@@ -498,6 +502,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
         const Rsrc r1 = make_rsrc(pr == 0 ? p.da : p.db, out_bytes);
         const int tp = t > 0 ? t - 1 : 0;
         f32x4 evr[2];   // waves 0-3: -r dr - a da, added to hh_ after the barrier
+        f32x4 o1[2];    // PROJ: da (waves 0-3) or db (waves 4-7), to LDS after the barrier
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j0 = 16 * (jb0 + jj) + 4 * g4;
@@ -529,7 +534,8 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
             // outside the branch: every wave issues the same stores, so the
             // compiler counts this chunk's outstanding stores exactly
             bstore4<kStreamDev>(ac[0][jj] * sc0, r0, voff, 0);
-            bstore4<kStreamDev>(ac[1][jj] * sc1, r1, voff, 0);
+            if constexpr (PROJ) o1[jj] = ac[1][jj] * sc1;
+            else bstore4<kStreamDev>(ac[1][jj] * sc1, r1, voff, 0);
         }
         lds_barrier();
         if (pr == 0) {
@@ -539,13 +545,21 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
                 *h = *h + evr[jj];
             }
         }
+        if constexpr (PROJ) {
+            // the prologue's backward (phase 6) needs da and db at one (t, j): they meet in the
+            // U and DSA rows, which no wave reads after the products above
+            float* dst = reinterpret_cast<float*>(smem + (pr == 0 ? L::U : L::DSA));
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                *reinterpret_cast<f32x4*>(dst + t * LDG + 16 * (jb0 + jj) + 4 * g4) = o1[jj];
+        }
     }
     lds_barrier();
 
     // ---- phase 6: dw: phi_t = diag(Gs^T S0) - sum_{s<=t} a da + sum_{s<t} (k dk + b db - r dr),
     //      dw_t = phi_t / w_t.  Thread (jp, q) scans tokens TPG q .. of columns 2jp, 2jp+1.
     {
-        constexpr int TPG = RawChunk<GNT, InT>::TPG, NG = RawChunk<GNT, InT>::NG;
+        constexpr int TPG = RawChunk<GNT, InT, PROJ>::TPG, NG = RawChunk<GNT, InT, PROJ>::NG;
         const int jp = tid & 31, q = tid >> 5, j0 = 2 * jp;
         float2 hx[TPG], fx[TPG];
         float2 tot = make_float2(0.f, 0.f);
@@ -586,18 +600,50 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
 #pragma unroll
         for (int tt = 0; tt < TPG; ++tt) {
             const int t = q * TPG + tt;
-            const float2 wv = Pair<InT>::f(cur.raw.w[tt]);
-            bstore2<kStreamDev>(make_float2((acc.x - fx[tt].x) * rcp(wv.x), (acc.y - fx[tt].y) * rcp(wv.y)), rdw,
-                             out_off(t, j0), 0);
+            const float2 phi = make_float2(acc.x - fx[tt].x, acc.y - fx[tt].y);   // dw_t w_t
+            const float2 x = Pair<InT>::f(cur.raw.w[tt]);
+            if constexpr (PROJ) {
+                // dw_raw = dw w (-e^-1/2) s (1 - s), s = sigmoid(w_raw)
+                const float sx = logistic_f(x.x), sy = logistic_f(x.y);
+                bstore2<kStreamDev>(make_float2(-kDecayScale * phi.x * sx * (1.f - sx),
+                                                -kDecayScale * phi.y * sy * (1.f - sy)), rdw, out_off(t, j0), 0);
+            } else {
+                bstore2<kStreamDev>(make_float2(phi.x * rcp(x.x), phi.y * rcp(x.y)), rdw, out_off(t, j0), 0);
+            }
             acc.x += hx[tt].x;
             acc.y += hx[tt].y;
         }
+        if constexpr (PROJ) {
+            // the prologue's backward for a = -kh and b = kh sigmoid(alpha), kh = kappa / |kappa|:
+            // g = -da + sigmoid(alpha) db (the gradient w.r.t. kh), dkappa = (g - kh (kh . g)) / |kappa|
+            // with the dot product over the token's 64 columns (the 32 lanes of this half wave),
+            // dalpha = db kh s (1 - s), s = sigmoid(alpha)
+            const float* lda = reinterpret_cast<const float*>(smem + L::U);
+            const float* ldb = reinterpret_cast<const float*>(smem + L::DSA);
+            const Rsrc rka = make_rsrc(p.da, out_bytes), ral = make_rsrc(p.db, out_bytes);
+#pragma unroll
+            for (int tt = 0; tt < TPG; ++tt) {
+                const int t = q * TPG + tt;
+                const float2 dav = *reinterpret_cast<const float2*>(lda + t * LDG + j0);
+                const float2 dbv = *reinterpret_cast<const float2*>(ldb + t * LDG + j0);
+                const float2 kh = cur.raw.kappa_hat(tt), al = Pair<InT>::f(cur.raw.b[tt]);
+                const float sx = logistic_f(al.x), sy = logistic_f(al.y);
+                const float gx = dbv.x * sx - dav.x, gy = dbv.y * sy - dav.y;
+                const float dot = half_sum32(kh.x * gx + kh.y * gy);
+                const float iv = cur.raw.inv[tt];
+                bstore2<kStreamDev>(make_float2((gx - kh.x * dot) * iv, (gy - kh.y * dot) * iv), rka,
+                                    out_off(t, j0), 0);
+                bstore2<kStreamDev>(make_float2(dbv.x * kh.x * sx * (1.f - sx), dbv.y * kh.y * sy * (1.f - sy)), ral,
+                                    out_off(t, j0), 0);
+            }
+        }
     }
     // The next chunk's loads (issued in phases 0-4) are all back by now; wait
-    // for them here, leaving only this chunk's six output stores in flight.
-    // Otherwise the compiler's count for their first uses (merged over the
-    // loop's back edge) would also wait for those stores to complete.
-    __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
+    // for them here, leaving only this chunk's output stores in flight (six;
+    // eight with the prologue).  Otherwise the compiler's count for their first
+    // uses (merged over the loop's back edge) would also wait for those stores
+    // to complete.
+    __builtin_amdgcn_s_waitcnt(PROJ ? 0x0F78 : 0x0F76);   // vmcnt(8) / vmcnt(6)
     if (!more) break;
     cur = nxt;
     idx = nidx;
@@ -605,10 +651,10 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
   }
 }
 
-template <typename InT, bool SPLIT>
+template <typename InT, bool SPLIT, bool PROJ>
 hipError_t launch_typed(BwdArgs a, hipStream_t s) {
     using L = GradSmem<SPLIT>;
-    auto kern = grad_kernel<InT, SPLIT>;
+    auto kern = grad_kernel<InT, SPLIT, PROJ>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -637,9 +683,13 @@ hipError_t launch_typed(BwdArgs a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, hipStream_t s) {
-    if (bf16) return launch_typed<uint16_t, true>(a, s);
-    return launch_typed<float, false>(a, s);
+hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, bool proj, hipStream_t s) {
+    if (proj) {
+        if (bf16) return launch_typed<uint16_t, true, true>(a, s);
+        return launch_typed<float, false, true>(a, s);
+    }
+    if (bf16) return launch_typed<uint16_t, true, false>(a, s);
+    return launch_typed<float, false, false>(a, s);
 }
 
 }  // namespace wkv7

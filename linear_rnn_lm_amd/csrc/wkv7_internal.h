@@ -83,10 +83,13 @@ struct ScanArgs {
     int B, T, H, NC;
 };
 
-// Each returns hipSuccess or the launch error.
-hipError_t launch_chunk_prepare(const PrepArgs& a, bool bf16, hipStream_t s);
+// Each returns hipSuccess or the launch error.  proj: the w, a, b pointers
+// hold the raw projections w_raw, kappa, alpha, and the time-mix prologue runs
+// inside the kernels' loads (backward: dw, da, db receive dw_raw, dkappa,
+// dalpha).
+hipError_t launch_chunk_prepare(const PrepArgs& a, bool bf16, bool proj, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, bool bf16, bool bwd, hipStream_t s);
 hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, bool proj, hipStream_t s);
 
 }  // namespace wkv7

@@ -75,8 +75,9 @@ struct PrepSmem {
 };
 
 // Persistent: workgroup b takes items (head, chunk) b, b + gridDim.x, ...; the
-// next item's inputs load while the current one is processed.
-template <typename InT, bool SPLIT>
+// next item's inputs load while the current one is processed.  PROJ: the w, a,
+// b inputs are the raw projections w_raw, kappa, alpha (see RawChunk).
+template <typename InT, bool SPLIT, bool PROJ>
 __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p, int items) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     using L = PrepSmem<SPLIT>;
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p, int i
     const int r16 = lane & 15, g4 = lane >> 4;
     const int64_t tstride = (int64_t)p.H * D;
 
-    RawChunk<NT, InT> raw;
+    RawChunk<NT, InT, PROJ> raw;
     // raw <- the inputs of item `it` (tokens of a ragged last chunk: see RawChunk)
     auto load_item = [&](int it) {
         const int head = it / p.NC, c = it - head * p.NC;
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p, int i
     // ---- gamma, gamma_last and the scaled operand rows
     const PrepOut<SPLIT> po{A, R, Bm, Km, A, A, A, A, true, true, true, true, false, false, false, false,
                             nullptr, glast};
+    raw.finish();
     chunk_prep<NT, SPLIT>(raw, po, qp, tid);
     load_item(more ? nitem : item);   // the last item loads itself again: no branch around the loads
     lds_barrier();
@@ -616,10 +618,10 @@ hipError_t set_smem(F kern, int bytes) {
                                bytes);
 }
 
-template <typename InT, bool SPLIT>
+template <typename InT, bool SPLIT, bool PROJ>
 hipError_t launch_prepare_typed(const PrepArgs& a, hipStream_t s) {
     using L = PrepSmem<SPLIT>;
-    auto kern = chunk_prepare_kernel<InT, SPLIT>;
+    auto kern = chunk_prepare_kernel<InT, SPLIT, PROJ>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = set_smem(kern, L::total);
@@ -664,9 +666,13 @@ hipError_t launch_scan_nwv(const ScanArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_chunk_prepare(const PrepArgs& a, bool bf16, hipStream_t s) {
-    if (bf16) return launch_prepare_typed<uint16_t, true>(a, s);
-    return launch_prepare_typed<float, false>(a, s);
+hipError_t launch_chunk_prepare(const PrepArgs& a, bool bf16, bool proj, hipStream_t s) {
+    if (proj) {
+        if (bf16) return launch_prepare_typed<uint16_t, true, true>(a, s);
+        return launch_prepare_typed<float, false, true>(a, s);
+    }
+    if (bf16) return launch_prepare_typed<uint16_t, true, false>(a, s);
+    return launch_prepare_typed<float, false, false>(a, s);
 }
 
 hipError_t launch_scan(const ScanArgs& a, bool bf16, bool bwd, hipStream_t s) {

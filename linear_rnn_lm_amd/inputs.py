@@ -117,6 +117,51 @@ def make_inputs(B: int, T: int, H: int, dtype: torch.dtype = torch.bfloat16, see
                   None if h0 is None else h0.contiguous(), dy.contiguous())
 
 
+@dataclasses.dataclass
+class ProjInputs:
+    """Inputs of the layer with its time-mix prologue: raw projections in
+    place of w, a and b."""
+    r: torch.Tensor
+    w_raw: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    kappa: torch.Tensor
+    alpha: torch.Tensor
+    h0: Optional[torch.Tensor]
+    dy: torch.Tensor
+
+    def tensors(self):
+        return (self.r, self.w_raw, self.k, self.v, self.kappa, self.alpha)
+
+    def to(self, device):
+        f = lambda x: None if x is None else x.to(device)
+        return ProjInputs(*(f(getattr(self, n)) for n in ("r", "w_raw", "k", "v", "kappa", "alpha", "h0", "dy")))
+
+
+def make_proj_inputs(B: int, T: int, H: int, dtype: torch.dtype = torch.bfloat16, seed: int = 0,
+                     with_h0: bool = False, h0_std: float = 0.1) -> ProjInputs:
+    """The draws of make_inputs, in the same order, with w_raw, kappa and alpha
+    left as drawn (N(0,1)): the layer's prologue derives w, a and b from them."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = (B, T, H, D)
+
+    def n01(*s):
+        return torch.randn(*s, generator=g, dtype=torch.float32)
+
+    r = n01(*shape)
+    w_raw = n01(*shape)
+    k = n01(*shape) / 8.0
+    v = n01(*shape)
+    kappa = n01(*shape)
+    alpha = n01(*shape)
+    h0 = n01(B, H, D, D) * h0_std if with_h0 else None
+    dy = n01(*shape)
+    cast = lambda x: x.to(dtype).contiguous()
+    return ProjInputs(cast(r), cast(w_raw), cast(k), cast(v), cast(kappa), cast(alpha),
+                      None if h0 is None else h0.contiguous(), dy.contiguous())
+
+
 def workload_inputs(wl: Workload, layer: int = 0) -> Inputs:
     """Inputs of one workload (for the recurrent-step workload: of one layer)."""
     return make_inputs(wl.B, wl.T, wl.H, wl.dtype, wl.seed + layer, wl.with_h0)

@@ -88,7 +88,7 @@ def call_fwd(fn="wkv7_fwd", **over):
     a = fwd_args(**over)
     f = getattr(L.lib(), fn)
     head = (a["B"], a["T"], a["H"], a["D"], a["dt"], a["r"], a["w"], a["k"], a["v"], a["a"], a["b"])
-    if fn == "wkv7_fwd":
+    if fn in ("wkv7_fwd", "wkv7_fwd_proj"):
         return f(*head, a["h0"], a["y"], a["ck"], a["hT"], a["ws"], a["wsb"], None)
     if fn == "wkv7_fwd_scan":
         return f(*head[:5], a["v"], a["ops"], a["h0"], a["y"], a["ck"], a["hT"], None)
@@ -96,7 +96,7 @@ def call_fwd(fn="wkv7_fwd", **over):
 
 
 @needs_no_gpu
-@pytest.mark.parametrize("fn", ["wkv7_fwd", "wkv7_fwd_sequential", "wkv7_fwd_scan"])
+@pytest.mark.parametrize("fn", ["wkv7_fwd", "wkv7_fwd_proj", "wkv7_fwd_sequential", "wkv7_fwd_scan"])
 def test_fwd_rejects_bad_arguments(fn):
     c = lambda **o: call_fwd(fn, **o)
     assert c(D=32) == ERR_SHAPE
@@ -120,7 +120,10 @@ def test_fwd_rejects_bad_arguments(fn):
         assert c(w=fake(1) + 4) == ERR_ALIGN
         assert c(y=fake(0)) == ERR_ALIAS             # y on top of r
         assert c(y=fake(5) + 4096) == ERR_ALIAS      # y overlapping the tail of b
-    if fn == "wkv7_fwd":
+    if fn == "wkv7_fwd_proj":
+        assert c(T=1, ws=None) == ERR_WS                 # the prologue path is always chunked
+        assert c(T=1, wsb=L.chunk_ops_bytes(1, 1, 1) - 16) == ERR_WS
+    if fn in ("wkv7_fwd", "wkv7_fwd_proj"):
         assert c(ws=None) == ERR_WS
         assert c(wsb=1000) == ERR_WS
         assert c(ws=fake(11) + 4) == ERR_ALIGN
@@ -148,7 +151,8 @@ def test_chunk_prepare_rejects_bad_arguments():
 
 
 @needs_no_gpu
-def test_bwd_rejects_bad_arguments():
+@pytest.mark.parametrize("fn", ["wkv7_bwd", "wkv7_bwd_proj"])
+def test_bwd_rejects_bad_arguments(fn):
     lib = L.lib()
     B, T, H, D = 1, 64, 1, 64
     ws = L.workspace_bytes(B, T, H)
@@ -158,7 +162,7 @@ def test_bwd_rejects_bad_arguments():
                  v=fake(4), a=fake(5), b=fake(6), ck=fake(7), dr=fake(8), dw=fake(9), dk=fake(10),
                  dv=fake(11), da=fake(12), db=fake(13), dh0=fake(14), ws=fake(15), wsb=ws)
         a.update(o)
-        return lib.wkv7_bwd(a["B"], a["T"], a["H"], a["D"], a["dt"], a["dy"], a["dhT"], a["r"], a["w"],
+        return getattr(lib, fn)(a["B"], a["T"], a["H"], a["D"], a["dt"], a["dy"], a["dhT"], a["r"], a["w"],
                             a["k"], a["v"], a["a"], a["b"], a["ck"], a["dr"], a["dw"], a["dk"], a["dv"],
                             a["da"], a["db"], a["dh0"], a["ws"], a["wsb"], None)
 

@@ -1,0 +1,100 @@
+"""The layer with its time-mix prologue (w, a, b formed inside the kernels
+from w_raw, kappa, alpha) through the C ABI, against the oracle's prologue
+followed by its recurrence, and the recurrence's backward followed by the
+prologue's backward."""
+import numpy as np
+import pytest
+import torch
+
+import linear_rnn_lm_amd as L
+import oracle
+from linear_rnn_lm_amd.inputs import ProjInputs, make_proj_inputs
+from tests.gpu_util import TOL, note, rel
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+FWD = ("y", "ckpt", "hT")
+BWD = ("dr", "dw_raw", "dk", "dv", "dkappa", "dalpha", "dh0")
+
+
+def _np(t):
+    return None if t is None else t.detach().double().cpu().numpy()
+
+
+def run_gpu_proj(x, dhT=None):
+    dev = torch.device("cuda:0")
+    ins = [t.to(dev) for t in x.tensors()]
+    h0 = None if x.h0 is None else x.h0.to(dev)
+    y, ck, hT = L.fwd_proj(*ins, h0)
+    g = L.bwd_proj(x.dy.to(dev), *ins, ck, None if dhT is None else dhT.to(dev))
+    torch.cuda.synchronize()
+    out = {"y": y, "ckpt": ck, "hT": hT}
+    out.update(dict(zip(BWD, g)))
+    return {k: _np(v) for k, v in out.items()}
+
+
+def run_oracle_proj(x, dhT=None):
+    r, w_raw, k, v, kappa, alpha = x.tensors()
+    w, a, b = oracle.proj_fwd(w_raw, kappa, alpha)
+    y, ck, hT = oracle.fwd(r, w, k, v, a, b, x.h0)
+    dr, dw, dk, dv, da, db, dh0 = oracle.bwd(r, w, k, v, a, b, x.dy, x.h0, dhT)
+    dw_raw, dkappa, dalpha = oracle.proj_bwd(w_raw, kappa, alpha, dw, da, db)
+    return {"y": y, "ckpt": ck, "hT": hT, "dr": dr, "dw_raw": dw_raw, "dk": dk, "dv": dv,
+            "dkappa": dkappa, "dalpha": dalpha, "dh0": dh0}
+
+
+def check(gpu, ref, dtype, names=FWD + BWD):
+    errs = {n: rel(gpu[n], ref[n]) for n in names}
+    bad = [n for n in names if not errs[n] <= TOL[dtype]["fwd" if n in FWD else "bwd"]]
+    note(f"rel-L2 {errs}")
+    assert not bad, (bad, errs)
+
+
+SMALL = [
+    (1, 64, 1, F32, False, False),
+    (2, 70, 3, F32, True, True),
+    (3, 33, 1, F32, False, False),
+    (1, 5, 2, BF16, True, False),
+    (2, 100, 2, BF16, False, True),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dtype,with_h0,with_dhT", SMALL,
+                         ids=[f"B{c[0]}T{c[1]}H{c[2]}-{str(c[3])[6:]}-h0{int(c[4])}-dhT{int(c[5])}" for c in SMALL])
+def test_proj_small_shapes(B, T, H, dtype, with_h0, with_dhT):
+    x = make_proj_inputs(B, T, H, dtype, seed=700 + T, with_h0=with_h0)
+    dhT = torch.randn(B, H, 64, 64, generator=torch.Generator().manual_seed(701)) * 0.1 if with_dhT else None
+    note(f"proj B{B} T{T} H{H} {dtype} h0={with_h0} dhT={with_dhT}")
+    check(run_gpu_proj(x, dhT), run_oracle_proj(x, dhT), dtype)
+
+
+def test_proj_zero_kappa_tokens():
+    """Tokens whose kappa is zero get a = b = 0 and a zero kappa gradient; the
+    rest of the sequence is unaffected."""
+    x = make_proj_inputs(2, 45, 2, F32, seed=702, with_h0=True)
+    kappa = x.kappa.clone()
+    kappa[0, 3] = 0.0
+    kappa[1, 40, 1] = 0.0
+    x = ProjInputs(x.r, x.w_raw, x.k, x.v, kappa, x.alpha, x.h0, x.dy)
+    note("proj zero kappa tokens")
+    gpu, ref = run_gpu_proj(x), run_oracle_proj(x)
+    assert np.all(gpu["dkappa"][0, 3] == 0.0) and np.all(gpu["dkappa"][1, 40, 1] == 0.0)
+    check(gpu, ref, F32)
+
+
+def test_proj_debug_shape_sampled_heads():
+    """B12 T1024 H6 bf16 (the training-shape layer) in one call; the oracle
+    runs on three of its 72 heads."""
+    B, T, H = 12, 1024, 6
+    x = make_proj_inputs(B, T, H, BF16, seed=703)
+    note("proj B12 T1024 H6 bf16")
+    gpu = run_gpu_proj(x)
+    for bb, hh in ((0, 0), (7, 4), (11, 5)):
+        sl = lambda t: t[bb:bb + 1, :, hh:hh + 1].contiguous()
+        xs = ProjInputs(*(sl(t) for t in x.tensors()), None, sl(x.dy))
+        ref = run_oracle_proj(xs)
+        sub = {n: (v[bb:bb + 1][:, hh:hh + 1] if n in ("ckpt", "hT", "dh0") else v[bb:bb + 1, :, hh:hh + 1])
+               for n, v in gpu.items()}
+        note(f"head ({bb}, {hh})")
+        check(sub, ref, BF16)
