@@ -8,6 +8,11 @@ of the workload's shape, resident in HBM before timing starts.
 
 Prints one JSON line.  Default workload: B12 T1024 H6 D64, bf16 inputs
 (the 36M "debug" training layer).
+
+--prologue times the layer with its time-mix prologue fused into the kernels
+(wkv7_fwd_proj + wkv7_bwd_proj: w, a, b formed from raw projections inside the
+loads), and beside it the same two calls without the prologue (wkv7_fwd +
+wkv7_bwd on w, a, b) and with the prologue as separate torch operations.
 """
 from __future__ import annotations
 
@@ -162,6 +167,120 @@ def cpu_baseline(wl, budget_s: float) -> dict:
 
 
 STEP_METRIC = "WKV7 recurrent step tokens/s and % HBM peak, 32 layers x B256 T1 H64 D64 (1 MI355X)"
+PROLOGUE_METRIC = "WKV7 layer with fused time-mix prologue, fwd+bwd tokens/s (1 MI355X)"
+
+
+def _time_steps(torch, stream, fn, warmup, steps):
+    """Milliseconds per call of fn, from two events on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_prologue(args, wl) -> int:
+    """One step = wkv7_fwd_proj then wkv7_bwd_proj (each runs the chunk
+    preparation itself, as a training framework calling forward and backward
+    separately would).  Also timed: wkv7_fwd + wkv7_bwd on w, a, b (the layer
+    without a prologue), and the prologue as torch operations around them."""
+    import torch
+    import linear_rnn_lm_amd as L
+    from linear_rnn_lm_amd.inputs import make_proj_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, T, H = wl.B, wl.T, wl.H
+    x = make_proj_inputs(B, T, H, wl.dtype, wl.seed, wl.with_h0)
+    r, w_raw, k, v, kappa, alpha = (t.to(dev) for t in x.tensors())
+    h0 = None if x.h0 is None else x.h0.to(dev)
+    dy = x.dy.to(dev)
+    f32 = dict(device=dev, dtype=torch.float32)
+    nc = L.num_chunks(T)
+    y = torch.empty(B, T, H, D, **f32)
+    ck = torch.empty(B, H, nc, D, D, **f32)
+    hT = torch.empty(B, H, D, D, **f32)
+    grads = [torch.empty(B, T, H, D, **f32) for _ in range(6)]
+    fws = torch.empty(L.chunk_ops_bytes(B, T, H) // 4, **f32)
+    bws = torch.empty(L.workspace_bytes(B, T, H) // 4, **f32)
+    stream = torch.cuda.current_stream(dev)
+
+    def fused_fwd():
+        L.fwd_proj(r, w_raw, k, v, kappa, alpha, h0, y=y, ckpt=ck, hT=hT, workspace=fws)
+
+    def fused_bwd():
+        L.bwd_proj(dy, r, w_raw, k, v, kappa, alpha, ck, None, workspace=bws, out=grads)
+
+    def fused():
+        fused_fwd()
+        fused_bwd()
+
+    # the layer without a prologue, on w, a, b of the same values' dtype
+    c = -0.6065306597126334
+    sw = torch.sigmoid(w_raw.float())
+    kf = kappa.float()
+    nrm = kf.norm(dim=-1, keepdim=True)
+    kh = kf / nrm
+    sa = torch.sigmoid(alpha.float())
+    wd, ad, bd = (t.to(wl.dtype) for t in (torch.exp(c * sw), -kh, kh * sa))
+
+    def core():
+        L.fwd(r, wd, k, v, ad, bd, h0, y=y, ckpt=ck, hT=hT, workspace=fws)
+        L.bwd(dy, r, wd, k, v, ad, bd, ck, None, workspace=bws, out=grads)
+
+    def unfused():
+        s1 = torch.sigmoid(w_raw.float())
+        w1 = torch.exp(c * s1)
+        k1 = kappa.float()
+        n1 = k1.norm(dim=-1, keepdim=True)
+        h1 = k1 / n1
+        a1 = torch.sigmoid(alpha.float())
+        wb, ab, bb = w1.to(wl.dtype), (-h1).to(wl.dtype), (h1 * a1).to(wl.dtype)
+        L.fwd(r, wb, k, v, ab, bb, h0, y=y, ckpt=ck, hT=hT, workspace=fws)
+        dr, dw, dk, dv, da, db, _ = L.bwd(dy, r, wb, k, v, ab, bb, ck, None, workspace=bws, out=grads)
+        g = db * a1 - da
+        return (dw * w1 * c * s1 * (1 - s1), (g - h1 * (h1 * g).sum(-1, keepdim=True)) / n1,
+                db * h1 * a1 * (1 - a1))
+
+    ms = _time_steps(torch, stream, fused, args.warmup, args.steps)
+    ms_fwd = _time_steps(torch, stream, fused_fwd, args.warmup, args.steps)
+    ms_bwd = _time_steps(torch, stream, fused_bwd, args.warmup, args.steps)
+    ms_core = _time_steps(torch, stream, core, args.warmup, args.steps)
+    ms_unfused = _time_steps(torch, stream, unfused, args.warmup, args.steps)
+    in_bytes = 2 if wl.dtype == torch.bfloat16 else 4
+    kb = kernel_bytes(wl, in_bytes)
+    tokens = B * T
+    out = {
+        "metric": PROLOGUE_METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} with raw projections w_raw, kappa, alpha: {wl.description}",
+                   "B": B, "T": T, "H": H, "D": D,
+                   "in_dtype": "bf16" if in_bytes == 2 else "f32", "state_dtype": "f32"},
+        "ms_fwd_proj": ms_fwd,
+        "ms_bwd_proj": ms_bwd,
+        "ms_without_prologue": ms_core,
+        "ms_prologue_in_torch": ms_unfused,
+        "path_hbm": {"algorithmic_bytes": kb["path"],
+                     "achieved_GBs": kb["path"] / (ms * 1e-3) / 1e9,
+                     "frac_of_peak": kb["path"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def step_bytes(wl, in_bytes: int) -> int:
@@ -260,6 +379,8 @@ def main() -> int:
     ap.add_argument("--workload", default="debug_36m")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prologue", action="store_true",
+                    help="time the layer with its fused time-mix prologue (see the module docstring)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -290,6 +411,8 @@ def main() -> int:
     wl = WORKLOADS[args.workload]
     if args.copy_calibration:
         copy_calibration(torch.device("cuda:0"))
+    if args.prologue:
+        return bench_prologue(args, wl)
     if wl.T == 1:
         return bench_step(args, wl)
     dev = torch.device("cuda:0")
