@@ -13,6 +13,10 @@ Prints one JSON line.  Default workload: B12 T1024 H6 D64, bf16 inputs
 (wkv7_fwd_proj + wkv7_bwd_proj: w, a, b formed from raw projections inside the
 loads), and beside it the same two calls without the prologue (wkv7_fwd +
 wkv7_bwd on w, a, b) and with the prologue as separate torch operations.
+
+--division times the diagnostic division-walk backward (wkv7_bwd_division,
+restarting from the exact state at every chunk end) beside the recompute
+backward (wkv7_bwd) on the same forward's checkpoints.
 """
 from __future__ import annotations
 
@@ -182,6 +186,51 @@ def _time_steps(torch, stream, fn, warmup, steps):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+DIVISION_METRIC = "WKV7 backward by division (diagnostic), tokens/s (1 MI355X)"
+
+
+def bench_division(args, wl) -> int:
+    """One step = wkv7_bwd_division (restart at every chunk end) on the
+    checkpoints of one forward; wkv7_bwd on the same checkpoints beside it."""
+    import torch
+    import linear_rnn_lm_amd as L
+    from linear_rnn_lm_amd.inputs import workload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = workload_inputs(wl)
+    ins = [t.to(dev) for t in x.tensors()]
+    h0 = None if x.h0 is None else x.h0.to(dev)
+    dy = x.dy.to(dev)
+    y, ck, hT = L.fwd(*ins, h0)
+    stream = torch.cuda.current_stream(dev)
+    steps, warmup = max(1, min(args.steps, 5)), min(args.warmup, 1)
+    ms_div = _time_steps(torch, stream, lambda: L.bwd_division(dy, *ins, ck, hT, None, restart=True),
+                         warmup, steps)
+    ms_rec = _time_steps(torch, stream, lambda: L.bwd(dy, *ins, ck, None), args.warmup, args.steps)
+    tokens = wl.B * wl.T
+    out = {
+        "metric": DIVISION_METRIC,
+        "value": tokens / (ms_div * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_div,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: backward only, {wl.description}", "B": wl.B, "T": wl.T, "H": wl.H,
+                   "D": D},
+        "ms_recompute_bwd": ms_rec,
+        "slowdown_vs_recompute": ms_div / ms_rec,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def bench_prologue(args, wl) -> int:
@@ -381,6 +430,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prologue", action="store_true",
                     help="time the layer with its fused time-mix prologue (see the module docstring)")
+    ap.add_argument("--division", action="store_true",
+                    help="time the diagnostic division-walk backward (see the module docstring)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -413,6 +464,8 @@ def main() -> int:
         copy_calibration(torch.device("cuda:0"))
     if args.prologue:
         return bench_prologue(args, wl)
+    if args.division:
+        return bench_division(args, wl)
     if wl.T == 1:
         return bench_step(args, wl)
     dev = torch.device("cuda:0")

@@ -295,6 +295,37 @@ wkv7_status wkv7_bwd_proj(int B, int T, int H, int D, wkv7_dtype in_dtype,
                           void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/*
+ * Diagnostic, not for training: the backward of the rwkv-mlx page's Metal
+ * design ("Metal kernel architecture", backward block, and the paragraph
+ * after it on error growth), which walks each chunk in reverse from an exact
+ * state and rebuilds every earlier state by undoing the update, i.e. by
+ * dividing by w, instead of recomputing it from a checkpoint as wkv7_bwd
+ * does.  Rounding errors grow by about (1/w) per token walked, which is why
+ * wkv7_bwd recomputes.  sa, which the division needs before the earlier state
+ * is known, is solved from the update itself: with z = S_t[i] - v[i] k,
+ * sa[i] = (z . (a / w)) / (1 + b . (a / w)) and S_{t-1}[i] = (z - sa[i] b) / w.
+ * One wave per head, one state row per lane; slow by design.
+ *
+ *   dy, dhT, r..b : as for wkv7_bwd.
+ *   h_ckpt        : checkpoints from wkv7_fwd; required when restart = 1.
+ *   hT            : (B,H,D,D) final state from wkv7_fwd, required.
+ *   restart       : 1 = each chunk's walk starts from the exact state at the
+ *                   chunk's end (checkpoint c + 1, hT for the last chunk): at
+ *                   most 32 divisions in a row, the page's design; 0 = one
+ *                   walk over the whole sequence from hT (T divisions in a row).
+ *                   Other values: WKV7_ERR_ARG.
+ *   dr..db, dh0   : as for wkv7_bwd (dh0 may be NULL).  No workspace.
+ * w must be nonzero; results are not finite when 1 + b . (a / w) is zero.
+ */
+wkv7_status wkv7_bwd_division(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                              const float *dy, const float *dhT,
+                              const void *r, const void *w, const void *k,
+                              const void *v, const void *a, const void *b,
+                              const float *h_ckpt, const float *hT, int restart,
+                              float *dr, float *dw, float *dk, float *dv,
+                              float *da, float *db, float *dh0, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

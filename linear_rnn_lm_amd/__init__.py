@@ -73,6 +73,8 @@ def lib():
         L.wkv7_fwd_proj.restype = i
         L.wkv7_bwd_proj.argtypes = L.wkv7_bwd.argtypes
         L.wkv7_bwd_proj.restype = i
+        L.wkv7_bwd_division.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] * 2 + [i] + [vp] * 7 + [vp]
+        L.wkv7_bwd_division.restype = i
         _lib = L
     return _lib
 
@@ -252,6 +254,22 @@ def bwd_proj(dy, r, w_raw, k, v, kappa, alpha, ckpt, dhT=None, *, want_dh0=True,
                              *map(_ptr, (r, w_raw, k, v, kappa, alpha)), _ptr(ckpt), *map(_ptr, out), _ptr(dh0),
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     _check("wkv7_bwd_proj", st)
+    return (*out, dh0)
+
+
+def bwd_division(dy, r, w, k, v, a, b, ckpt, hT, dhT=None, *, restart=True, want_dh0=True):
+    """Diagnostic backward that rebuilds earlier states by dividing by w (see
+    wkv7_bwd_division): (dr, dw, dk, dv, da, db, dh0).  restart=True walks each
+    chunk from the exact state at its end; False walks the whole sequence from hT."""
+    import torch
+    B, T, H, D = _shape(r)
+    f32 = dict(device=r.device, dtype=torch.float32)
+    out = [torch.empty((B, T, H, D), **f32) for _ in range(6)]
+    dh0 = torch.empty((B, H, D, D), **f32) if want_dh0 else None
+    st = lib().wkv7_bwd_division(B, T, H, D, _dtype_code(r), _ptr(dy), _ptr(dhT),
+                                 *map(_ptr, (r, w, k, v, a, b)), _ptr(ckpt), _ptr(hT), 1 if restart else 0,
+                                 *map(_ptr, out), _ptr(dh0), _stream(r.device))
+    _check("wkv7_bwd_division", st)
     return (*out, dh0)
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwkv7.so")
-SOURCES = ["wkv7_api.hip", "wkv7_scan.hip", "wkv7_seq.hip", "wkv7_grad.hip"]
+SOURCES = ["wkv7_api.hip", "wkv7_scan.hip", "wkv7_seq.hip", "wkv7_grad.hip", "wkv7_division.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

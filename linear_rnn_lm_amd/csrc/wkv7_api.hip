@@ -399,6 +399,36 @@ wkv7_status wkv7_bwd(int B, int T, int H, int D, wkv7_dtype in_dtype, const floa
                     workspace, workspace_bytes, stream);
 }
 
+wkv7_status wkv7_bwd_division(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy, const float* dhT,
+                              const void* r, const void* w, const void* k, const void* v, const void* a,
+                              const void* b, const float* h_ckpt, const float* hT, int restart, float* dr,
+                              float* dw, float* dk, float* dv, float* da, float* db, float* dh0, void* stream) {
+    wkv7_status st = check_dtype(in_dtype);
+    if (st != WKV7_OK) return st;
+    Sizes sz;
+    st = check_shape(B, T, H, D, &sz);
+    if (st != WKV7_OK) return st;
+    if (restart != 0 && restart != 1) return WKV7_ERR_ARG;
+    if (restart && !h_ckpt) return WKV7_ERR_ARG;
+    const int64_t tin = sz.tok_elems * elem_size(in_dtype), t32 = sz.tok_elems * 4, s32 = sz.state_elems * 4;
+    const Buf bufs[17] = {{dy, t32, true, false}, {dhT, s32, false, false}, {r, tin, true, false},
+                          {w, tin, true, false},  {k, tin, true, false},    {v, tin, true, false},
+                          {a, tin, true, false},  {b, tin, true, false},    {h_ckpt, sz.ckpt_elems * 4, false, false},
+                          {hT, s32, true, false}, {dr, t32, true, true},    {dw, t32, true, true},
+                          {dk, t32, true, true},  {dv, t32, true, true},    {da, t32, true, true},
+                          {db, t32, true, true},  {dh0, s32, false, true}};
+    st = check_bufs(bufs, 17);
+    if (st != WKV7_OK) return st;
+    st = check_alias(bufs, 17);
+    if (st != WKV7_OK) return st;
+    wkv7::DivArgs da_ = {};
+    da_.r = r; da_.w = w; da_.k = k; da_.v = v; da_.a = a; da_.b = b;
+    da_.dy = dy; da_.dhT = dhT; da_.ckpt = h_ckpt; da_.hT = hT;
+    da_.dr = dr; da_.dw = dw; da_.dk = dk; da_.dv = dv; da_.da = da; da_.db = db; da_.dh0 = dh0;
+    da_.B = B; da_.T = T; da_.H = H; da_.NC = (int)sz.nc; da_.restart = restart;
+    return status_of(wkv7::launch_bwd_division(da_, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
+}
+
 wkv7_status wkv7_bwd_proj(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy, const float* dhT,
                           const void* r, const void* w_raw, const void* k, const void* v, const void* kappa,
                           const void* alpha, const float* h_ckpt, float* dr, float* dw_raw, float* dk, float* dv,

@@ -83,6 +83,19 @@ struct ScanArgs {
     int B, T, H, NC;
 };
 
+// The division-walk backward (a diagnostic; wkv7_division.hip).
+struct DivArgs {
+    const void *r, *w, *k, *v, *a, *b;
+    const float* dy;
+    const float* dhT;   // NULL = zero
+    const float* ckpt;  // (B,H,NC,D,D) states entering each chunk (read when restart != 0)
+    const float* hT;    // (B,H,D,D) state after the last token
+    float *dr, *dw, *dk, *dv, *da, *db;
+    float* dh0;         // NULL = not wanted
+    int B, T, H, NC;
+    int restart;        // 1: each chunk's walk starts from the exact state at its end; 0: only the last
+};
+
 // Each returns hipSuccess or the launch error.  proj: the w, a, b pointers
 // hold the raw projections w_raw, kappa, alpha, and the time-mix prologue runs
 // inside the kernels' loads (backward: dw, da, db receive dw_raw, dkappa,
@@ -91,5 +104,6 @@ hipError_t launch_chunk_prepare(const PrepArgs& a, bool bf16, bool proj, hipStre
 hipError_t launch_scan(const ScanArgs& a, bool bf16, bool bwd, hipStream_t s);
 hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, bool proj, hipStream_t s);
+hipError_t launch_bwd_division(const DivArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace wkv7

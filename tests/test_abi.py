@@ -135,6 +135,32 @@ def test_fwd_rejects_bad_arguments(fn):
 
 
 @needs_no_gpu
+def test_bwd_division_rejects_bad_arguments():
+    lib = L.lib()
+
+    def c(**o):
+        a = dict(B=1, T=64, H=1, D=64, dt=1, dy=fake(0), dhT=None, r=fake(1), w=fake(2), k=fake(3), v=fake(4),
+                 a=fake(5), b=fake(6), ck=fake(7), hT=fake(16), restart=1, dr=fake(8), dw=fake(9), dk=fake(10),
+                 dv=fake(11), da=fake(12), db=fake(13), dh0=fake(14))
+        a.update(o)
+        return lib.wkv7_bwd_division(a["B"], a["T"], a["H"], a["D"], a["dt"], a["dy"], a["dhT"], a["r"], a["w"],
+                                     a["k"], a["v"], a["a"], a["b"], a["ck"], a["hT"], a["restart"], a["dr"],
+                                     a["dw"], a["dk"], a["dv"], a["da"], a["db"], a["dh0"], None)
+
+    assert c(D=16) == ERR_SHAPE
+    assert c(T=0) == ERR_SHAPE
+    assert c(dt=3) == ERR_DTYPE
+    assert c(restart=2) == ERR_ARG
+    assert c(ck=None) == ERR_ARG                      # restarting needs the checkpoints
+    assert c(hT=None) == ERR_ARG
+    assert c(dy=None) == ERR_ARG
+    assert c(da=None) == ERR_ARG
+    assert c(dv=fake(11) + 4) == ERR_ALIGN
+    assert c(dr=fake(0)) == ERR_ALIAS                 # dr on dy
+    assert c(dh0=fake(16)) == ERR_ALIAS               # dh0 on hT
+
+
+@needs_no_gpu
 def test_chunk_prepare_rejects_bad_arguments():
     lib = L.lib()
     c = lambda B=1, T=64, H=1, D=64, dt=1, r=fake(4), w=fake(0), k=fake(5), a=fake(1), b=fake(2), out=fake(3): \
