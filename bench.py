@@ -49,7 +49,8 @@ def source_digest() -> str:
 
 def kernel_bytes(wl, in_bytes: int) -> dict:
     """Bytes each kernel must move per launch (inputs read once, outputs
-    written once); see the design doc for the per-head-token figures."""
+    written once).  Per head-token with bf16 inputs the path moves 1,536 B
+    forward and 3,072 B backward."""
     ht = wl.B * wl.T * wl.H          # head-tokens
     heads = wl.B * wl.H
     nc = (wl.T + 31) // 32
