@@ -46,6 +46,10 @@ The time-mix prologue (w, a, b from raw projections):
 * ``proj_composed``    -- central differences of the whole layer (prologue,
                           then the recurrence) against the chain of the two
                           backwards, at a tiny shape.
+* ``proj_recipe``      -- the prologue applied to the raw draws of the input
+                          generator gives the w, a, b that the generator's own
+                          fp32 recipe forms from the same draws (an
+                          independent implementation, in torch).
 """
 from __future__ import annotations
 
@@ -352,6 +356,15 @@ def proj_composed(orc, seed=11):
     return err
 
 
+def proj_recipe(orc, seed=12):
+    from linear_rnn_lm_amd.inputs import make_inputs, make_proj_inputs
+    x = make_inputs(2, 40, 3, torch.float32, seed=seed)
+    xr = make_proj_inputs(2, 40, 3, torch.float32, seed=seed)
+    err = max(rel(xr.r.numpy(), x.r.numpy()), rel(xr.k.numpy(), x.k.numpy()), rel(xr.v.numpy(), x.v.numpy()))
+    w, a, b = orc.proj_fwd(xr.w_raw, xr.kappa, xr.alpha)
+    return max(err, rel(w, x.w.numpy()), rel(a, x.a.numpy()), rel(b, x.b.numpy()))
+
+
 ALL = {
     "t1_closed_form": t1_closed_form,
     "linear_attention": linear_attention,
@@ -364,6 +377,7 @@ ALL = {
     "proj_identities": proj_identities,
     "proj_finite_difference": proj_finite_difference,
     "proj_composed": proj_composed,
+    "proj_recipe": proj_recipe,
 }
 
 # tolerance of each check for a correct fp64 oracle
@@ -379,4 +393,5 @@ TOL = {
     "proj_identities": 1e-14,
     "proj_finite_difference": 1e-7,
     "proj_composed": 1e-7,
+    "proj_recipe": 1e-6,
 }

@@ -53,6 +53,8 @@ def check(gpu, ref, dtype, names=FWD + BWD):
 
 SMALL = [
     (1, 64, 1, F32, False, False),
+    (2, 1, 3, F32, True, True),
+    (1, 31, 2, BF16, True, True),
     (2, 70, 3, F32, True, True),
     (3, 33, 1, F32, False, False),
     (1, 5, 2, BF16, True, False),
