@@ -1,0 +1,34 @@
+"""bench.py's contract on the CPU: one GPU only, and the byte model behind
+its roofline figures."""
+import os
+import subprocess
+import sys
+
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from linear_rnn_lm_amd.inputs import Workload  # noqa: E402
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_path_bytes_per_head_token():
+    """bf16 inputs: the forward moves 1,536 B and the backward 3,072 B per
+    head-token (inputs once, fp32 outputs once, one fp32 state per 32 tokens
+    written and read back), plus the final state and its gradient per head."""
+    wl = Workload("t", 1, 320, 1, torch.bfloat16, 0, False)
+    kb = bench.kernel_bytes(wl, 2)
+    assert kb["path"] == 320 * (1536 + 3072) + 2 * 64 * 64 * 4
+    wl3 = Workload("t", 2, 100, 3, torch.float32, 0, True)
+    kb3 = bench.kernel_bytes(wl3, 4)
+    ht, heads, nc = 600, 6, 4
+    fwd = ht * 64 * (6 * 4 + 4) + heads * nc * 64 * 64 * 4 + 2 * heads * 64 * 64 * 4
+    bwd = ht * 64 * (6 * 4 + 4 + 6 * 4) + heads * nc * 64 * 64 * 4 + heads * 64 * 64 * 4
+    assert kb3["path"] == fwd + bwd
