@@ -638,17 +638,41 @@ __device__ __forceinline__ void tri_inverse(const float* LT, float* tf, float* s
         float x[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) x[t] = (t == k) ? 1.f : 0.f;
+        // The pieces do not depend on x: each third of the steps has all of its reads issued
+        // before its first product (the scheduling barriers keep them there), so the reads'
+        // latency is paid three times instead of once per step.
+        auto part = [&](auto s_lo, auto s_hi) {
+            constexpr int S0 = decltype(s_lo)::value, S1 = decltype(s_hi)::value;
+            constexpr int NP = [] {
+                int n = 0;
+                for (int s = S0; s < S1; ++s) n += 4 - ((s + 1) >> 2);
+                return n;
+            }();
+            f32x4 piece[NP];
+            int n = 0;
 #pragma unroll
-        for (int s = 0; s < 15; ++s) {
-            const float* col = LT + (base + s) * LDF + base;
+            for (int s = S0; s < S1; ++s) {
 #pragma unroll
-            for (int q0 = ((s + 1) >> 2) << 2; q0 < 16; q0 += 4) {
-                const f32x4 l = *reinterpret_cast<const f32x4*>(col + q0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (q0 + e > s) x[q0 + e] = fmaf(l[e], x[s], x[q0 + e]);
+                for (int q0 = ((s + 1) >> 2) << 2; q0 < 16; q0 += 4)
+                    piece[n++] = *reinterpret_cast<const f32x4*>(LT + (base + s) * LDF + base + q0);
             }
-        }
+            __builtin_amdgcn_sched_barrier(0);
+            n = 0;
+#pragma unroll
+            for (int s = S0; s < S1; ++s) {
+#pragma unroll
+                for (int q0 = ((s + 1) >> 2) << 2; q0 < 16; q0 += 4) {
+                    const f32x4 l = piece[n++];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (q0 + e > s) x[q0 + e] = fmaf(l[e], x[s], x[q0 + e]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        part(std::integral_constant<int, 0>{}, std::integral_constant<int, 5>{});
+        part(std::integral_constant<int, 5>{}, std::integral_constant<int, 10>{});
+        part(std::integral_constant<int, 10>{}, std::integral_constant<int, 15>{});
 #pragma unroll
         for (int t = 0; t < 16; ++t) tf[(base + t) * LDF + base + k] = x[t];
     }
