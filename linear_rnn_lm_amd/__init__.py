@@ -343,16 +343,45 @@ def _make_autograd():
             grads = [cast(g, x) for g, x in zip((dr, dw, dk, dv, da, db), ins)]
             return (*grads, dh0 if ctx.has_h0 else None)
 
-    return WKV7
+    class WKV7Proj(torch.autograd.Function):
+        """Differentiable op with the fused time-mix prologue: (r, w_raw, k, v, kappa, alpha, h0)
+        -> (y, hT), gradients by wkv7_bwd_proj (w, a, b are formed inside the kernels)."""
+
+        @staticmethod
+        def forward(ctx, r, w_raw, k, v, kappa, alpha, h0=None):
+            ins = [x.contiguous() for x in (r, w_raw, k, v, kappa, alpha)]
+            h0c = None if h0 is None else h0.contiguous().float()
+            y, ckpt, hT = fwd_proj(*ins, h0c)
+            ctx.save_for_backward(*ins, ckpt)
+            ctx.has_h0 = h0 is not None
+            return y, hT
+
+        @staticmethod
+        def backward(ctx, dy, dhT):
+            *ins, ckpt = ctx.saved_tensors
+            if dy is None:
+                dy = torch.zeros(ins[0].shape, dtype=torch.float32, device=ins[0].device)
+            else:
+                dy = dy.contiguous().float()
+            dhT = None if dhT is None else dhT.contiguous().float()
+            *g, dh0 = bwd_proj(dy, *ins, ckpt, dhT)
+            grads = [gi.to(x.dtype) for gi, x in zip(g, ins)]
+            return (*grads, dh0 if ctx.has_h0 else None)
+
+    return WKV7, WKV7Proj
 
 
-class _LazyWKV7:
-    _cls = None
+class _LazyOp:
+    _classes = None
+
+    def __init__(self, index):
+        self._index = index
 
     def __getattr__(self, name):
-        if _LazyWKV7._cls is None:
-            _LazyWKV7._cls = _make_autograd()
-        return getattr(_LazyWKV7._cls, name)
+        if _LazyOp._classes is None:
+            _LazyOp._classes = _make_autograd()
+        return getattr(_LazyOp._classes[self._index], name)
 
 
-WKV7 = _LazyWKV7()
+WKV7 = _LazyOp(0)
+WKV7Proj = _LazyOp(1)

@@ -100,3 +100,21 @@ def test_proj_debug_shape_sampled_heads():
                for n, v in gpu.items()}
         note(f"head ({bb}, {hh})")
         check(sub, ref, BF16)
+
+
+def test_proj_autograd_op_matches_raw_calls():
+    """The autograd op over the prologue path gives the raw calls' gradients, bitwise."""
+    dev = torch.device("cuda:0")
+    x = make_proj_inputs(2, 70, 3, F32, seed=704, with_h0=True)
+    ins = [t.to(dev) for t in x.tensors()]
+    h0, dy = x.h0.to(dev), x.dy.to(dev)
+    dhT = (torch.randn(2, 3, 64, 64, generator=torch.Generator().manual_seed(705)) * 0.1).to(dev)
+    leaves = [t.clone().requires_grad_(True) for t in ins] + [h0.clone().requires_grad_(True)]
+    note("proj autograd op")
+    y, hT = L.WKV7Proj.apply(*leaves)
+    ((y * dy).sum() + (hT * dhT).sum()).backward()
+    _, ck, _ = L.fwd_proj(*ins, h0)
+    g = L.bwd_proj(dy, *ins, ck, dhT)
+    torch.cuda.synchronize()
+    for leaf, ref in zip(leaves, g):
+        assert torch.equal(leaf.grad, ref)
