@@ -173,6 +173,7 @@ def cpu_baseline(wl, budget_s: float) -> dict:
 
 STEP_METRIC = "WKV7 recurrent step tokens/s and % HBM peak, 32 layers x B256 T1 H64 D64 (1 MI355X)"
 PROLOGUE_METRIC = "WKV7 layer with fused time-mix prologue, fwd+bwd tokens/s (1 MI355X)"
+STEP_PROLOGUE_METRIC = "WKV7 recurrent step with fused time-mix prologue tokens/s, 32 layers x B256 T1 H64 D64 (1 MI355X)"
 
 
 def _time_steps(torch, stream, fn, warmup, steps):
@@ -343,17 +344,21 @@ def step_bytes(wl, in_bytes: int) -> int:
 def bench_step(args, wl) -> int:
     """The one-token recurrent step (forward only): one call per layer, each
     updating that layer's (B,H,64,64) fp32 state in place.  A step is all
-    layers; tokens/s counts the B sequences' tokens per step."""
+    layers; tokens/s counts the B sequences' tokens per step.  With --prologue
+    the layers take raw projections (wkv7_fwd_proj), and the same step on
+    precomputed w, a, b and with the prologue as torch operations is timed
+    beside it."""
     import torch
     import linear_rnn_lm_amd as L
-    from linear_rnn_lm_amd.inputs import make_inputs
+    from linear_rnn_lm_amd.inputs import make_inputs, make_proj_inputs
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     in_bytes = 2 if wl.dtype == torch.bfloat16 else 4
     layers = []
     gen = torch.Generator(device=dev)
     for layer in range(wl.layers):
-        x = make_inputs(wl.B, 1, wl.H, wl.dtype, wl.seed + layer, with_h0=False)
+        make = make_proj_inputs if args.prologue else make_inputs
+        x = make(wl.B, 1, wl.H, wl.dtype, wl.seed + layer, with_h0=False)
         gen.manual_seed(wl.seed + layer)
         # the states: N(0, 0.1), drawn on the device (8.6 GB for 32 layers)
         state = torch.randn(wl.B, wl.H, D, D, generator=gen, device=dev, dtype=torch.float32) * 0.1
@@ -365,9 +370,11 @@ def bench_step(args, wl) -> int:
     sh = stream.cuda_stream
     calls = [([t.data_ptr() for t in ins], st.data_ptr(), y.data_ptr()) for ins, st, y in layers]
 
+    entry = lib.wkv7_fwd_proj if args.prologue else lib.wkv7_fwd
+
     def call(c):
         p, ps, py = c
-        st = lib.wkv7_fwd(wl.B, 1, wl.H, D, code, *p, ps, py, None, ps, None, 0, sh)
+        st = entry(wl.B, 1, wl.H, D, code, *p, ps, py, None, ps, None, 0, sh)
         assert st == 0, lib.wkv7_status_str(st)
 
     def step():
@@ -417,6 +424,32 @@ def bench_step(args, wl) -> int:
         "roofline": {"kernel": "fwd_sequential", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
     }
+    if args.prologue:
+        out["metric"] = STEP_PROLOGUE_METRIC
+        c = -0.6065306597126334
+        pre = []
+        for ins, st, y in layers:
+            r, w_raw, k, v, kappa, alpha = ins
+            kf = kappa.float()
+            kh = kf / kf.norm(dim=-1, keepdim=True)
+            wd = torch.exp(c * torch.sigmoid(w_raw.float())).to(wl.dtype)
+            pre.append(([r, wd, k, v, (-kh).to(wl.dtype), (kh * torch.sigmoid(alpha.float())).to(wl.dtype)], st, y))
+
+        def core():
+            for ins, st, y in pre:
+                L.fwd(*ins, st, want_ckpt=False, y=y, hT=st)
+
+        def unfused():
+            for ins, st, y in layers:
+                r, w_raw, k, v, kappa, alpha = ins
+                kf = kappa.float()
+                kh = kf / kf.norm(dim=-1, keepdim=True)
+                wd = torch.exp(c * torch.sigmoid(w_raw.float())).to(wl.dtype)
+                L.fwd(r, wd, k, v, (-kh).to(wl.dtype), (kh * torch.sigmoid(alpha.float())).to(wl.dtype), st,
+                      want_ckpt=False, y=y, hT=st)
+
+        out["ms_without_prologue"] = _time_steps(torch, stream, core, args.warmup, args.steps)
+        out["ms_prologue_in_torch"] = _time_steps(torch, stream, unfused, args.warmup, args.steps)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -463,12 +496,12 @@ def main() -> int:
     wl = WORKLOADS[args.workload]
     if args.copy_calibration:
         copy_calibration(torch.device("cuda:0"))
+    if wl.T == 1:
+        return bench_step(args, wl)
     if args.prologue:
         return bench_prologue(args, wl)
     if args.division:
         return bench_division(args, wl)
-    if wl.T == 1:
-        return bench_step(args, wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = workload_inputs(wl)

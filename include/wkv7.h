@@ -261,10 +261,9 @@ wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype,
  * w_raw, kappa and alpha are (B,T,H,D) in_dtype, like r, k, v; w never exists
  * in memory, so the decay-range rule above is met by construction.
  *
- * wkv7_fwd_proj: as wkv7_fwd with (w_raw, kappa, alpha) in place of (w, a, b);
- * it always runs the chunked path, so `workspace` must hold
- * wkv7_chunk_ops_bytes(B,T,H,D) bytes for every T (not
- * wkv7_fwd_workspace_bytes, which is 0 for T == 1).
+ * wkv7_fwd_proj: as wkv7_fwd with (w_raw, kappa, alpha) in place of (w, a, b),
+ * the same workspace rule included (wkv7_fwd_workspace_bytes; none for T == 1,
+ * where the one-token step applies the prologue to its loads as well).
  */
 wkv7_status wkv7_fwd_proj(int B, int T, int H, int D, wkv7_dtype in_dtype,
                           const void *r, const void *w_raw, const void *k,

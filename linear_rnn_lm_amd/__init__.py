@@ -230,11 +230,12 @@ def fwd_proj(r, w_raw, k, v, kappa, alpha, h0=None, *, want_y=True, want_ckpt=Tr
     kernels from w_raw, kappa, alpha; see wkv7_fwd_proj).  Returns (y, ckpt, hT)."""
     B, T, H, D = _shape(r)
     y, ckpt, hT = _fwd_outputs(r, want_y, want_ckpt, want_hT, y, ckpt, hT)
-    if workspace is None:
-        workspace = _f32_bytes(chunk_ops_bytes(B, T, H, D), r.device)
+    need = fwd_workspace_bytes(B, T, H, D)
+    if workspace is None and need:
+        workspace = _f32_bytes(need, r.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().wkv7_fwd_proj(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w_raw, k, v, kappa, alpha)), _ptr(h0),
-                             _ptr(y), _ptr(ckpt), _ptr(hT), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(r.device))
+                             _ptr(y), _ptr(ckpt), _ptr(hT), _ptr(workspace), wsb, _stream(r.device))
     _check("wkv7_fwd_proj", st)
     return y, ckpt, hT
 

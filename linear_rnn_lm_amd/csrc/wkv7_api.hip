@@ -244,7 +244,7 @@ wkv7_status wkv7_fwd_scan(int B, int T, int H, int D, wkv7_dtype in_dtype, const
 
 namespace {
 
-// wkv7_fwd and wkv7_fwd_proj (proj: w, a, b hold w_raw, kappa, alpha; always chunked)
+// wkv7_fwd and wkv7_fwd_proj (proj: w, a, b hold w_raw, kappa, alpha)
 wkv7_status fwd_impl(int B, int T, int H, int D, wkv7_dtype in_dtype, bool proj, const void* r, const void* w,
                      const void* k, const void* v, const void* a, const void* b, const float* h0,
                      float* y, float* h_ckpt, float* hT, void* workspace, size_t workspace_bytes,
@@ -254,9 +254,9 @@ wkv7_status fwd_impl(int B, int T, int H, int D, wkv7_dtype in_dtype, bool proj,
     if (st != WKV7_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = in_dtype == WKV7_BF16;
-    if (!proj && T <= kSequentialMaxT) {
+    if (T <= kSequentialMaxT) {
         const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, nullptr, h0, y, h_ckpt, hT);
-        return status_of(wkv7::launch_fwd_sequential(fa, bf16, s));
+        return status_of(wkv7::launch_fwd_sequential(fa, bf16, proj, s));
     }
     if (workspace && !aligned16(workspace)) return WKV7_ERR_ALIGN;
     if (!workspace || workspace_bytes < (size_t)ops_bytes(sz)) return WKV7_ERR_WORKSPACE;
@@ -341,7 +341,7 @@ wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype,
     wkv7_status st = check_fwd(B, T, H, D, in_dtype, r, w, k, v, a, b, h0, y, h_ckpt, hT, &sz);
     if (st != WKV7_OK) return st;
     const wkv7::FwdArgs fa = fwd_args(B, T, H, sz, r, w, k, v, a, b, nullptr, h0, y, h_ckpt, hT);
-    return status_of(wkv7::launch_fwd_sequential(fa, in_dtype == WKV7_BF16, static_cast<hipStream_t>(stream)));
+    return status_of(wkv7::launch_fwd_sequential(fa, in_dtype == WKV7_BF16, false, static_cast<hipStream_t>(stream)));
 }
 
 wkv7_status wkv7_bwd_scan(int B, int T, int H, int D, wkv7_dtype in_dtype, const float* dy, const float* dhT,

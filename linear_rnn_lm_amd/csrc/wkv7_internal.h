@@ -102,7 +102,7 @@ struct DivArgs {
 // dalpha).
 hipError_t launch_chunk_prepare(const PrepArgs& a, bool bf16, bool proj, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, bool bf16, bool bwd, hipStream_t s);
-hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, bool proj, hipStream_t s);
 hipError_t launch_bwd_inputs(const BwdArgs& a, bool bf16, bool proj, hipStream_t s);
 hipError_t launch_bwd_division(const DivArgs& a, bool bf16, hipStream_t s);
 

@@ -115,7 +115,10 @@ __device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
 // the four 4-column pieces at flat offsets 1024 q + 4 tid of the head's state:
 // rows tid / 16 + 16 q, columns 4 (tid % 16) .. + 3.  The 16 threads of a row
 // are one DPP row, so the row dot products need no LDS.
-template <typename InT>
+// PROJ: the w, a, b pointers hold the raw projections w_raw, kappa, alpha and
+// the time-mix prologue runs on the loaded values (the 16 lanes of a DPP row
+// hold one token's 64 channels, so |kappa| is a row sum).
+template <typename InT, bool PROJ>
 __global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
     const int tid = threadIdx.x;
     const int head = blockIdx.x;
@@ -131,8 +134,23 @@ __global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(p.ckpt + hoff + 1024 * q) = st[q];
     }
-    const f32x4 w = load4(static_cast<const InT*>(p.w) + base + c0), k = load4(static_cast<const InT*>(p.k) + base + c0);
-    const f32x4 a = load4(static_cast<const InT*>(p.a) + base + c0), b = load4(static_cast<const InT*>(p.b) + base + c0);
+    f32x4 w = load4(static_cast<const InT*>(p.w) + base + c0);
+    const f32x4 k = load4(static_cast<const InT*>(p.k) + base + c0);
+    f32x4 a = load4(static_cast<const InT*>(p.a) + base + c0), b = load4(static_cast<const InT*>(p.b) + base + c0);
+    if constexpr (PROJ) {
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ss = fmaf(a[c], a[c], ss);
+        ss = row16_allsum(ss);
+        const float inv = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float kh = a[c] * inv;
+            w[c] = proj_decay(w[c]);
+            a[c] = -kh;
+            b[c] = kh * logistic_f(b[c]);
+        }
+    }
     const f32x4 r = load4(static_cast<const InT*>(p.r) + base + c0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -158,13 +176,19 @@ __global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
 
 }  // namespace
 
-hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, hipStream_t s) {
+hipError_t launch_fwd_sequential(const FwdArgs& a, bool bf16, bool proj, hipStream_t s) {
     const int heads = a.B * a.H;
     if (a.T == 1) {   // the recurrent step: coalesced state access
-        if (bf16) hipLaunchKernelGGL(step_kernel<uint16_t>, dim3(heads), dim3(SEQ_NT), 0, s, a);
-        else hipLaunchKernelGGL(step_kernel<float>, dim3(heads), dim3(SEQ_NT), 0, s, a);
+        if (proj) {
+            if (bf16) hipLaunchKernelGGL((step_kernel<uint16_t, true>), dim3(heads), dim3(SEQ_NT), 0, s, a);
+            else hipLaunchKernelGGL((step_kernel<float, true>), dim3(heads), dim3(SEQ_NT), 0, s, a);
+        } else {
+            if (bf16) hipLaunchKernelGGL((step_kernel<uint16_t, false>), dim3(heads), dim3(SEQ_NT), 0, s, a);
+            else hipLaunchKernelGGL((step_kernel<float, false>), dim3(heads), dim3(SEQ_NT), 0, s, a);
+        }
         return hipGetLastError();
     }
+    if (proj) return hipErrorInvalidValue;   // the prologue runs in the step and the chunked kernels only
     if (bf16) hipLaunchKernelGGL(fwd_sequential_kernel<uint16_t>, dim3(heads), dim3(SEQ_NT), 0, s, a);
     else hipLaunchKernelGGL(fwd_sequential_kernel<float>, dim3(heads), dim3(SEQ_NT), 0, s, a);
     return hipGetLastError();

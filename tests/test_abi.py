@@ -120,9 +120,6 @@ def test_fwd_rejects_bad_arguments(fn):
         assert c(w=fake(1) + 4) == ERR_ALIGN
         assert c(y=fake(0)) == ERR_ALIAS             # y on top of r
         assert c(y=fake(5) + 4096) == ERR_ALIAS      # y overlapping the tail of b
-    if fn == "wkv7_fwd_proj":
-        assert c(T=1, ws=None) == ERR_WS                 # the prologue path is always chunked
-        assert c(T=1, wsb=L.chunk_ops_bytes(1, 1, 1) - 16) == ERR_WS
     if fn in ("wkv7_fwd", "wkv7_fwd_proj"):
         assert c(ws=None) == ERR_WS
         assert c(wsb=1000) == ERR_WS

@@ -54,6 +54,7 @@ def check(gpu, ref, dtype, names=FWD + BWD):
 SMALL = [
     (1, 64, 1, F32, False, False),
     (2, 1, 3, F32, True, True),
+    (3, 1, 5, BF16, True, True),
     (1, 31, 2, BF16, True, True),
     (2, 70, 3, F32, True, True),
     (3, 33, 1, F32, False, False),
@@ -118,3 +119,21 @@ def test_proj_autograd_op_matches_raw_calls():
     torch.cuda.synchronize()
     for leaf, ref in zip(leaves, g):
         assert torch.equal(leaf.grad, ref)
+
+
+def test_proj_recurrent_step_7b_layer():
+    """The one-token step with the prologue in its loads (B256 H64, one layer of the 7B
+    step shape, state in place): y and the new state against the oracle on every head."""
+    dev = torch.device("cuda:0")
+    x = make_proj_inputs(256, 1, 64, BF16, seed=706, with_h0=True)
+    ins = [t.to(dev) for t in x.tensors()]
+    state = x.h0.to(dev).clone()
+    note("proj step B256 T1 H64 bf16, in place")
+    y, _, _ = L.fwd_proj(*ins, state, want_ckpt=False, hT=state)
+    torch.cuda.synchronize()
+    r, w_raw, k, v, kappa, alpha = x.tensors()
+    w, a, b = oracle.proj_fwd(w_raw, kappa, alpha)
+    yo, _, hTo = oracle.fwd(r, w, k, v, a, b, x.h0, want_ckpt=False)
+    errs = {"y": rel(_np(y), yo), "hT": rel(_np(state), hTo)}
+    note(f"rel-L2 {errs}")
+    assert max(errs.values()) <= TOL[BF16]["fwd"], errs
