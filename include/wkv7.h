@@ -37,8 +37,11 @@
  * - Every pointer must be a device pointer (hipMalloc'd or equivalent) aligned
  *   to 16 bytes.  Optional pointers may be NULL where stated.
  * - The library allocates nothing, frees nothing and keeps no pointer after a
- *   call returns.  It holds no mutable global state; calls on different
- *   streams may run concurrently if their outputs do not overlap.
+ *   call returns.  Its only mutable global state is a per-device, per-kernel
+ *   flag recording that the kernel's dynamic LDS limit has been raised, set
+ *   once under a lock by the first launch on that device.  Every entry point
+ *   may therefore be called from several host threads at once; calls on
+ *   different streams may run concurrently if their outputs do not overlap.
  * - `stream` is a hipStream_t (NULL = the null stream).  Every entry point is
  *   asynchronous: it only enqueues kernels and never synchronises.
  * - Argument, shape, alignment, workspace and aliasing errors are detected on
@@ -64,7 +67,11 @@ typedef enum {
     WKV7_ERR_SHAPE = 2,     /* D != 64, B/T/H < 1, sizes overflowing int64,
                                or B*T*H*D*4 > 0xFFFFFF00: token tensors are
                                addressed with 32-bit byte offsets (at D = 64,
-                               B*T*H below 2^24); split larger batches      */
+                               B*T*H below 2^24); split larger batches.
+                               Checkpoints and state gradients are addressed
+                               per chunk with 64-bit bases, so they set no
+                               further limit (B = H = 1 allows T up to
+                               16,777,215, 8 GiB of checkpoints)            */
     WKV7_ERR_DTYPE = 3,     /* in_dtype not a wkv7_dtype                    */
     WKV7_ERR_ALIGN = 4,     /* a pointer not 16-byte aligned                */
     WKV7_ERR_ALIAS = 5,     /* an output overlaps an input or another output */

@@ -655,21 +655,13 @@ template <typename InT, bool SPLIT, bool PROJ>
 hipError_t launch_typed(BwdArgs a, hipStream_t s) {
     using L = GradSmem<SPLIT>;
     auto kern = grad_kernel<InT, SPLIT, PROJ>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static PerDeviceOnce once;
+    hipError_t e = set_smem_once(once, kern, L::total);
+    if (e != hipSuccess) return e;
     // one workgroup per CU (the LDS plan takes most of a CU's 160 KiB)
-    static int n_cu = 0;
-    if (n_cu == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-    }
+    int n_cu = 0;
+    e = device_cus(&n_cu);
+    if (e != hipSuccess) return e;
     const int heads = a.B * a.H;
     const int total = heads * a.NC;
     const int xcd = (heads % 8 == 0) ? 1 : 0;

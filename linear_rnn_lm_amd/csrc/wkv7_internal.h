@@ -5,7 +5,51 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace wkv7 {
+
+// One-time setup per device (a kernel's dynamic LDS limit), safe to reach
+// from several host threads at once: the first caller on a device runs the
+// setup under a lock; a failed setup is not recorded, so the next call tries
+// again.  Nothing else in the library is mutable.
+constexpr int kMaxDevices = 64;
+struct PerDeviceOnce {
+    std::atomic<bool> done[kMaxDevices] = {};
+    std::mutex lock;
+    template <typename F>
+    hipError_t run(F&& setup) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+        std::lock_guard<std::mutex> g(lock);
+        if (done[dev].load(std::memory_order_relaxed)) return hipSuccess;
+        e = setup(dev);
+        if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
+        return e;
+    }
+};
+
+// Raise a kernel's dynamic LDS limit to `bytes`, once per device.
+template <typename K>
+hipError_t set_smem_once(PerDeviceOnce& once, K kern, int bytes) {
+    return once.run([&](int) {
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   bytes);
+    });
+}
+
+// Compute units of the current device (queried on every call: it is a
+// cached attribute in the runtime, so nothing is kept here).
+inline hipError_t device_cus(int* n_cu) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    return e;
+}
 
 struct FwdArgs {
     const void *r, *w, *k, *v, *a, *b;

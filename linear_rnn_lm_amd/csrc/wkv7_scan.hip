@@ -366,8 +366,9 @@ struct XCopy {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int pc = piece(ct, u), t = pc / NPR, e0 = (pc % NPR) * EPP;
-            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 r, (t * HD + e0 + c * C * HD) * (int)sizeof(XT), 0, 0));
+            // byte offset inside the head's tokens: below 4 GiB, unsigned arithmetic
+            const uint32_t off = ((uint32_t)t * HD + e0 + (uint32_t)c * C * HD) * (uint32_t)sizeof(XT);
+            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
         }
     }
     // rows (t, i) of an operand matrix: exact bf16 (v) or split (dy)
@@ -398,7 +399,8 @@ __device__ __forceinline__ void store_out(const float* ob, Rsrc r, int c, int HD
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int pc = ct + NT * u, t = pc / NPR, e0 = (pc % NPR) * 4;
-        bstore4<kStream>(*reinterpret_cast<const f32x4*>(ob + t * LDO + e0), r, (t * HD + e0) * 4, c * C * HD * 4);
+        const uint32_t off = ((uint32_t)t * HD + e0 + (uint32_t)c * C * HD) * 4u;   // below 4 GiB
+        bstore4<kStream>(*reinterpret_cast<const f32x4*>(ob + t * LDO + e0), r, (int)off, 0);
     }
 }
 
@@ -503,8 +505,13 @@ __global__ __launch_bounds__(64 * (NCW + NMW)) void scan_kernel(ScanArgs p, int 
     const int n0 = i0 + 16 * rb;
     const int roff = (n0 + r16) * D + 4 * g4;                          // this lane's part of a D x D state
     const int64_t soff = (int64_t)head * D * D + roff;
-    const Rsrc rc = make_rsrc(p.ckpt ? p.ckpt + (int64_t)head * NC * D * D : nullptr,
-                              p.ckpt ? (uint32_t)NC * D * D * 4 : 0);
+    // Checkpoints (or state gradients) of this head: one buffer resource per
+    // chunk, based at that chunk's D x D block with a 64-bit address, so the
+    // per-lane offset stays below 16 KiB for any number of chunks.
+    float* const cbase = p.ckpt ? p.ckpt + (int64_t)head * NC * D * D : nullptr;
+    auto ckpt_rsrc = [&](int c) {
+        return make_rsrc(cbase ? cbase + (int64_t)c * D * D : nullptr, cbase ? D * D * 4 : 0);
+    };
 
     // The loop for half HF (0 when the row block has one wave): straight-line
     // code, so the products' independent chains interleave.
@@ -524,10 +531,11 @@ __global__ __launch_bounds__(64 * (NCW + NMW)) void scan_kernel(ScanArgs p, int 
 
         for (int it = 0; it < NC; ++it) {
             const int c = chunk_of(it);
+            const Rsrc rc = ckpt_rsrc(c);
             if constexpr (!BWD) {   // checkpoint c: the state entering the chunk
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
-                    if (mine(m)) bstore4(st[m], rc, (roff + 16 * m) * 4, c * D * D * 4);
+                    if (mine(m)) bstore4(st[m], rc, (roff + 16 * m) * 4, 0);
             }
             char* lb = smem + (it & 1) * L::OPS;
             const M Pm = make_mat<SPLIT>(lb, I::P, D, D), Mm = make_mat<SPLIT>(lb, I::M, C, D);
@@ -581,7 +589,7 @@ __global__ __launch_bounds__(64 * (NCW + NMW)) void scan_kernel(ScanArgs p, int 
                 // gradient w.r.t. the state entering chunk c
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
-                    if (mine(m)) bstore4(st[m], rc, (roff + 16 * m) * 4, c * D * D * 4);
+                    if (mine(m)) bstore4(st[m], rc, (roff + 16 * m) * 4, 0);
             }
             // output rows (t, i) of this chunk for the memory waves
 #pragma unroll
@@ -612,29 +620,16 @@ __global__ __launch_bounds__(64 * (NCW + NMW)) void scan_kernel(ScanArgs p, int 
     else run(std::integral_constant<int, 1>{});
 }
 
-template <typename F>
-hipError_t set_smem(F kern, int bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               bytes);
-}
-
 template <typename InT, bool SPLIT, bool PROJ>
 hipError_t launch_prepare_typed(const PrepArgs& a, hipStream_t s) {
     using L = PrepSmem<SPLIT>;
     auto kern = chunk_prepare_kernel<InT, SPLIT, PROJ>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = set_smem(kern, L::total);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    static int n_cu = 0;
-    if (n_cu == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-    }
+    static PerDeviceOnce once;
+    hipError_t e = set_smem_once(once, kern, L::total);
+    if (e != hipSuccess) return e;
+    int n_cu = 0;
+    e = device_cus(&n_cu);
+    if (e != hipSuccess) return e;
     const int items = a.B * a.H * a.NC;
     const int grid = items < 2 * n_cu ? items : 2 * n_cu;   // two workgroups per CU
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), L::total, s, a, items);
@@ -645,12 +640,9 @@ template <typename InT, bool SPLIT, int NWV, int NCW, int NMW, bool BWD>
 hipError_t launch_scan_typed(const ScanArgs& a, hipStream_t s) {
     constexpr int smem_bytes = ScanLds<SPLIT, NWV, NCW>::total;
     auto kern = scan_kernel<InT, SPLIT, NWV, NCW, NMW, BWD>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = set_smem(kern, smem_bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static PerDeviceOnce once;
+    const hipError_t e = set_smem_once(once, kern, smem_bytes);
+    if (e != hipSuccess) return e;
     const int heads = a.B * a.H;
     const bool xcd = heads % 8 == 0;
     hipLaunchKernelGGL(kern, dim3(heads * (4 / NWV)), dim3(64 * (NCW + NMW)), smem_bytes, s, a, xcd ? 1 : 0);

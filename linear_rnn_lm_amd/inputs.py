@@ -93,14 +93,16 @@ class Inputs:
 
 
 def make_inputs(B: int, T: int, H: int, dtype: torch.dtype = torch.bfloat16, seed: int = 0,
-                with_h0: bool = False, h0_std: float = 0.1) -> Inputs:
-    """Draw one set of inputs on the CPU.  Deterministic for a given seed."""
-    g = torch.Generator(device="cpu")
+                with_h0: bool = False, h0_std: float = 0.1, device: str = "cpu") -> Inputs:
+    """Draw one set of inputs (on the CPU unless `device` says otherwise; a
+    device generator gives a different, equally seeded stream, for shapes too
+    large to draw on the host).  Deterministic for a given seed and device."""
+    g = torch.Generator(device=device)
     g.manual_seed(seed)
     shape = (B, T, H, D)
 
     def n01(*s):
-        return torch.randn(*s, generator=g, dtype=torch.float32)
+        return torch.randn(*s, generator=g, dtype=torch.float32, device=device)
 
     r = n01(*shape)
     w = torch.exp(-math.exp(-0.5) * torch.sigmoid(n01(*shape)))
@@ -115,6 +117,41 @@ def make_inputs(B: int, T: int, H: int, dtype: torch.dtype = torch.bfloat16, see
     cast = lambda x: x.to(dtype).contiguous()
     return Inputs(cast(r), cast(w), cast(k), cast(v), cast(a), cast(b),
                   None if h0 is None else h0.contiguous(), dy.contiguous())
+
+
+# Inputs at the edges of the recurrence's domain.  Each kind starts from the
+# draws of make_inputs (same seed, same order) and replaces some of them:
+#   w_eighth     w = 1/8 everywhere: the smallest decay the library accepts, so
+#                a chunk's running decay products reach 2^-96
+#   w_near_one   w ~ U[0.999, 1]: the state barely decays and grows over T
+#   linear_attn  w = 1, a = b = 0: the state is the running sum of v k^T
+#   a_zero       a = 0 (b as drawn): no state-dependent term, sa = 0
+#   delta_rule   w = 1, r = k = kh, a = -kh, b = kh for a unit vector kh:
+#                each token writes v along kh and reads it back
+EDGE_KINDS = ("w_eighth", "w_near_one", "linear_attn", "a_zero", "delta_rule")
+
+
+def make_edge_inputs(kind: str, B: int, T: int, H: int, dtype: torch.dtype = torch.float32, seed: int = 0,
+                     with_h0: bool = False) -> Inputs:
+    if kind not in EDGE_KINDS:
+        raise ValueError(f"unknown edge kind {kind!r}; one of {EDGE_KINDS}")
+    x = make_inputs(B, T, H, torch.float32, seed, with_h0)
+    r, w, k, v, a, b = x.tensors()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 1)
+    if kind == "w_eighth":
+        w = torch.full_like(w, 0.125)
+    elif kind == "w_near_one":
+        w = 1.0 - 0.001 * torch.rand(w.shape, generator=g)
+    elif kind == "linear_attn":
+        w, a, b = torch.ones_like(w), torch.zeros_like(a), torch.zeros_like(b)
+    elif kind == "a_zero":
+        a = torch.zeros_like(a)
+    else:
+        kh = -a                      # the recipe's unit vector kappa
+        w, r, k, b = torch.ones_like(w), kh.clone(), kh.clone(), kh.clone()
+    cast = lambda t: t.to(dtype).contiguous()
+    return Inputs(cast(r), cast(w), cast(k), cast(v), cast(a), cast(b), x.h0, x.dy)
 
 
 @dataclasses.dataclass

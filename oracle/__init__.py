@@ -101,11 +101,16 @@ def _as64(x):
     return np.ascontiguousarray(x, dtype=np.float64)
 
 
+MAX_THREADS = 16   # worker threads at most (one head each; each holds all states of its head)
+
+
 def default_threads() -> int:
+    """Host cores available to this process, at most MAX_THREADS."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_THREADS))
 
 
 def num_chunks(T: int) -> int:

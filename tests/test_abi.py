@@ -249,3 +249,63 @@ def test_segment_spans():
     assert _segments(5, 100) == [(0, 5)]
     with pytest.raises(ValueError):
         _segments(10, 0)
+
+
+def test_checkpoint_addressing_has_no_32_bit_limit():
+    """Checkpoints and state gradients are addressed per chunk with 64-bit
+    bases: one head of 16,777,215 tokens (524,288 chunks, 8 GiB of
+    checkpoints) is a valid shape; only the token tensors' 32-bit byte
+    offsets bound T (the next token past 2^24 per head is refused)."""
+    T = (1 << 24) - 1
+    nc = L.num_chunks(T)
+    per_chunk = 32 * 32 * 4 + 36864
+    assert nc == 1 << 19
+    assert L.chunk_ops_bytes(1, T, 1) == nc * per_chunk
+    assert L.workspace_bytes(1, T, 1) == nc * 64 * 64 * 4 + nc * per_chunk
+    assert L.workspace_bytes(1, T + 1, 1) == 0          # 4 GiB fp32 token tensor: refused
+    assert L.workspace_bytes(1, (1 << 23) + 40, 1) > (1 << 32)
+
+
+@needs_no_gpu
+def test_fwd_accepts_long_single_head_on_the_host():
+    """B = H = 1 with T above 2^23 passes every host check of wkv7_fwd (made-up
+    buffers of the right sizes, 64 GiB apart); without a GPU the launch then
+    fails, never the shape check."""
+    T = (1 << 23) + 40
+    big = lambda n: BASE + n * (64 << 30)
+    ws = L.fwd_workspace_bytes(1, T, 1)
+    st = call_fwd("wkv7_fwd", T=T, r=big(0), w=big(1), k=big(2), v=big(3), a=big(4), b=big(5), y=big(6),
+                  ck=big(7), hT=big(8), ws=big(9), wsb=ws)
+    assert st == ERR_HIP
+
+
+@needs_no_gpu
+def test_entry_points_from_two_threads():
+    """Queries and launch paths called from two host threads at once (ctypes
+    releases the GIL): every call returns the same status it returns alone
+    (the launch fails for want of a GPU, after the host checks)."""
+    import threading
+    lib = L.lib()
+    alone = (call_fwd("wkv7_fwd"), call_fwd("wkv7_fwd_sequential"), call_fwd("wkv7_fwd_scan"))
+    assert alone == (ERR_HIP, ERR_HIP, ERR_HIP)
+    results, errors = [], []
+
+    def worker():
+        try:
+            for _ in range(200):
+                got = (lib.wkv7_num_chunks(1000), lib.wkv7_bwd_workspace_bytes(2, 100, 3, 64),
+                       lib.wkv7_status_str(6), call_fwd("wkv7_fwd"), call_fwd("wkv7_fwd_sequential"),
+                       call_fwd("wkv7_fwd_scan"), call_fwd("wkv7_fwd", D=32))
+                results.append(got)
+        except Exception as e:  # pragma: no cover
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker) for _ in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors
+    expect = (32, lib.wkv7_bwd_workspace_bytes(2, 100, 3, 64), lib.wkv7_status_str(6), ERR_HIP, ERR_HIP, ERR_HIP,
+              ERR_SHAPE)
+    assert len(results) == 400 and all(r == expect for r in results)

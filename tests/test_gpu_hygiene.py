@@ -95,5 +95,9 @@ def test_device_buffers_rejected_before_launch():
     assert lib.wkv7_fwd(B, T, H, D, 1, *p, None, y.data_ptr(), ck.data_ptr(), None, fws.data_ptr(), wsb - 4,
                         s) == 7
     ws = torch.empty(16, device=DEV)
-    with pytest.raises(L.Wkv7Error, match="workspace"):
+    with pytest.raises(ValueError, match="workspace"):
         L.bwd(dy, *ins, ck, None, workspace=ws)
+    # the library's own check, reached through the C ABI with the same buffer
+    out = [torch.empty(B, T, H, D, device=DEV) for _ in range(6)]
+    assert lib.wkv7_bwd(B, T, H, D, 1, dy.data_ptr(), None, *p, ck.data_ptr(), *[o.data_ptr() for o in out], None,
+                        ws.data_ptr(), 64, s) == 7

@@ -66,3 +66,54 @@ def test_segments_match_oracle_16k():
     errs, bad = compare(gpu, ref, BF16, names=["y", "hT", *NAMES])
     note(f"rel-L2 {errs}")
     assert not bad, errs
+
+
+def test_single_head_past_2_23_tokens():
+    """One call over B = H = 1, T = 2^23 + 40 (262,146 chunks, 4 GiB of
+    checkpoints, past the 32-bit byte range of one head's checkpoints).  The
+    inputs are drawn on the device with the workloads' distributions.  No
+    oracle runs over 8.4M tokens; instead every checkpoint must be written
+    (NaN-prefilled buffers) and chunks on both sides of the 2^17 and 2^18
+    chunk marks, and the last (ragged) one, must agree with a call over that
+    chunk alone, started from the long call's checkpoint (forward) and from
+    its state gradient at the chunk's end (backward)."""
+    T = (1 << 23) + 40
+    dev = torch.device("cuda:0")
+    note(f"single head T{T}: inputs")
+    x = make_inputs(1, T, 1, BF16, seed=610, with_h0=True, device="cuda")
+    ins = list(x.tensors())
+    h0, dy = x.h0, x.dy
+    nc = L.num_chunks(T)
+    y = torch.full((1, T, 1, 64), float("nan"), device=dev)
+    ck = torch.full((1, 1, nc, 64, 64), float("nan"), device=dev)
+    hT = torch.empty(1, 1, 64, 64, device=dev)
+    note(f"single head T{T}: fwd ({nc} chunks)")
+    L.fwd(*ins, h0, y=y, ckpt=ck, hT=hT)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ck).all() and torch.isfinite(y).all()
+    note(f"single head T{T}: bwd")
+    ops = L.chunk_prepare(ins[0], ins[1], ins[2], ins[4], ins[5])
+    dck = torch.full((1, 1, nc, 64, 64), float("nan"), device=dev)
+    dck, dv, dh0 = L.bwd_scan(dy, ops, None, in_dtype=BF16, dh_ckpt=dck)
+    del ops
+    g = L.bwd(dy, *ins, ck, None)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dck).all() and torch.isfinite(dv).all()
+    for t in g[:6]:
+        assert torch.isfinite(t).all()
+    assert torch.equal(g[3], dv) and torch.equal(g[6], dh0)
+    worst = 0.0
+    for c in (0, (1 << 17) - 1, 1 << 17, (1 << 18) - 1, 1 << 18, nc - 2, nc - 1):
+        t0, t1 = 32 * c, min(T, 32 * c + 32)
+        sl = [t[:, t0:t1].contiguous() for t in ins]
+        yc, _, hc = L.fwd(*sl, ck[:, :, c].contiguous())
+        end = hT if c == nc - 1 else ck[:, :, c + 1]
+        dend = None if c == nc - 1 else dck[:, :, c + 1].contiguous()
+        gc = L.bwd(dy[:, t0:t1].contiguous(), *sl, ck[:, :, c:c + 1].contiguous(), dend)
+        torch.cuda.synchronize()
+        pairs = [(yc, y[:, t0:t1]), (hc, end), (gc[6], dck[:, :, c])] + \
+                [(gc[i], g[i][:, t0:t1]) for i in range(6)]
+        for a, b in pairs:
+            worst = max(worst, _rel(a, b))
+    note(f"single head T{T}: worst chunk-local rel {worst:.2e}")
+    assert worst <= 1e-6, worst

@@ -1,7 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle.
 
 Every case draws seeded inputs once on the CPU, runs both implementations on
-the identical (rounded) values and compares each output tensor by rel-L2.
+the identical (rounded) values and compares every output, head by head, by
+rel-L2.
 """
 import numpy as np
 import pytest
@@ -9,7 +10,7 @@ import torch
 
 import linear_rnn_lm_amd as L
 from linear_rnn_lm_amd.inputs import WORKLOADS, make_inputs, workload_inputs
-from tests.gpu_util import compare, note, run_gpu, run_oracle, select_heads, slice_heads
+from tests.gpu_util import compare, note, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -73,20 +74,18 @@ def test_training_workload_full(name):
     assert not bad, errs
 
 
-def test_rwkv_1b5_sampled_heads():
-    """Full-size B8 T4096 H32 run on the GPU; 6 of its 256 heads recomputed by
-    the oracle (heads are independent, so these are exact expected values)."""
+def test_rwkv_1b5_all_heads():
+    """Full-size B8 T4096 H32 (h0 != 0): every output of all 256 heads against
+    the oracle, head by head."""
     wl = WORKLOADS["rwkv_1b5"]
     x = workload_inputs(wl)
-    note("workload rwkv_1b5 full, sampled heads")
+    note("workload rwkv_1b5 full")
     g = run_gpu(x)
-    bsel, hsel = [0, 7, 3], [0, 31]
-    o = run_oracle(slice_heads(x, bsel, hsel))
-    errs, bad = compare(select_heads(g, bsel, hsel), o, wl.dtype)
-    note(f"rel-L2 {errs}")
+    note("workload rwkv_1b5: oracle on all 256 heads")
+    o = run_oracle(x)
+    errs, bad = compare(g, o, wl.dtype)
+    note(f"rel-L2 (worst head) {errs}")
     assert not bad, errs
-    for n in ("y", "dr", "dw", "dk", "dv", "da", "db"):
-        assert np.isfinite(g[n]).all(), n
 
 
 @pytest.mark.parametrize("layer", [0, 13, 31])

@@ -9,7 +9,7 @@ import torch
 import linear_rnn_lm_amd as L
 import oracle
 from linear_rnn_lm_amd.inputs import ProjInputs, make_proj_inputs
-from tests.gpu_util import TOL, note, rel
+from tests.gpu_util import TOL, note, rel_heads
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,8 @@ def run_oracle_proj(x, dhT=None):
 
 
 def check(gpu, ref, dtype, names=FWD + BWD):
-    errs = {n: rel(gpu[n], ref[n]) for n in names}
+    """Every output, every (b, h) head within tolerance (worst head reported)."""
+    errs = {n: rel_heads(n, gpu[n], ref[n]) for n in names}
     bad = [n for n in names if not errs[n] <= TOL[dtype]["fwd" if n in FWD else "bwd"]]
     note(f"rel-L2 {errs}")
     assert not bad, (bad, errs)
@@ -134,6 +135,6 @@ def test_proj_recurrent_step_7b_layer():
     r, w_raw, k, v, kappa, alpha = x.tensors()
     w, a, b = oracle.proj_fwd(w_raw, kappa, alpha)
     yo, _, hTo = oracle.fwd(r, w, k, v, a, b, x.h0, want_ckpt=False)
-    errs = {"y": rel(_np(y), yo), "hT": rel(_np(state), hTo)}
+    errs = {"y": rel_heads("y", _np(y), yo), "hT": rel_heads("hT", _np(state), hTo)}
     note(f"rel-L2 {errs}")
     assert max(errs.values()) <= TOL[BF16]["fwd"], errs
