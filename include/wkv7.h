@@ -163,6 +163,33 @@ wkv7_status wkv7_fwd(int B, int T, int H, int D, wkv7_dtype in_dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): wkv7_fwd without a
+ * workspace argument.  The chunk operands go to a static device array of
+ * wkv7_fwd_noalloc_max_bytes() bytes (128 MiB) inside the library, one copy
+ * per GPU, held until the process ends; its device address is looked up once
+ * per device on the first call there.  Nothing is allocated or freed by the
+ * call itself.
+ *
+ *   Arguments, results and errors as wkv7_fwd (T == 1 uses no scratch).
+ *   WKV7_ERR_WORKSPACE: the call would need more than
+ *     wkv7_fwd_noalloc_max_bytes() of chunk operands, i.e.
+ *     wkv7_fwd_workspace_bytes(B,T,H,D) > 128 MiB (B*H*NC > 3276 chunks);
+ *     detected on the host, nothing is enqueued.
+ *   WKV7_ERR_HIP: the scratch's address could not be looked up.
+ * All calls on one GPU share that GPU's array and leave their chunk operands
+ * in it: two calls that overlap in time on one GPU (different streams, or
+ * host threads without ordering) race and give wrong results.  Calls in
+ * order on one stream are safe.
+ */
+size_t wkv7_fwd_noalloc_max_bytes(void);
+wkv7_status wkv7_fwd_noalloc(int B, int T, int H, int D, wkv7_dtype in_dtype,
+                             const void *r, const void *w, const void *k,
+                             const void *v, const void *a, const void *b,
+                             const float *h0, float *y, float *h_ckpt, float *hT,
+                             void *stream);
+
+/*
  * Forward given the chunk operands (from wkv7_chunk_prepare for the same r, w,
  * k, a, b): the state is carried from chunk to chunk, S_end = S0 P + V^T M,
  * and every chunk's y = E S0^T + F V.  Arguments as wkv7_fwd; chunk_ops is

@@ -73,6 +73,9 @@ def lib():
         L.wkv7_fwd_proj.restype = i
         L.wkv7_bwd_proj.argtypes = L.wkv7_bwd.argtypes
         L.wkv7_bwd_proj.restype = i
+        L.wkv7_fwd_noalloc.argtypes = [i, i, i, i, i] + [vp] * 6 + [vp] * 4 + [vp]
+        L.wkv7_fwd_noalloc.restype = i
+        L.wkv7_fwd_noalloc_max_bytes.restype = sz
         L.wkv7_bwd_division.argtypes = [i, i, i, i, i] + [vp] * 2 + [vp] * 6 + [vp] * 2 + [i] + [vp] * 7 + [vp]
         L.wkv7_bwd_division.restype = i
         _lib = L
@@ -234,6 +237,18 @@ def fwd(r, w, k, v, a, b, h0=None, *, want_y=True, want_ckpt=True, want_hT=True,
     st = lib().wkv7_fwd(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, v, a, b)), _ptr(h0),
                         _ptr(y), _ptr(ckpt), _ptr(hT), _ptr(workspace), wsb, _stream(r.device))
     _check("wkv7_fwd", st)
+    return y, ckpt, hT
+
+
+def fwd_noalloc(r, w, k, v, a, b, h0=None, *, y, ckpt=None, hT=None):
+    """Forward whose chunk operands live in the library's static device scratch
+    (wkv7_fwd_noalloc): nothing is allocated, so the outputs must be passed.
+    Calls that overlap in time on one GPU race on that scratch."""
+    B, T, H, D = _check_tokens("wkv7_fwd_noalloc", "rwkvab", (r, w, k, v, a, b))
+    _check_fwd_states("wkv7_fwd_noalloc", r, h0, y, ckpt, hT)
+    st = lib().wkv7_fwd_noalloc(B, T, H, D, _dtype_code(r), *map(_ptr, (r, w, k, v, a, b)), _ptr(h0),
+                                _ptr(y), _ptr(ckpt), _ptr(hT), _stream(r.device))
+    _check("wkv7_fwd_noalloc", st)
     return y, ckpt, hT
 
 

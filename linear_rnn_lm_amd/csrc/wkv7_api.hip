@@ -7,6 +7,35 @@
 
 namespace {
 
+// Scratch of wkv7_fwd_noalloc: the chunk operands of one forward call live in
+// this file-scope device array instead of a caller-supplied workspace.  Every
+// GPU the library runs on holds its own copy until the process ends.  Host
+// code never uses the array's name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+struct ScratchAddr {
+    wkv7::PerDeviceOnce once;
+    void* ptr[wkv7::kMaxDevices] = {};
+};
+
+// The current device's copy of `scratch` (nullptr and an error on failure).
+hipError_t scratch_address(void** out) {
+    static ScratchAddr sa;
+    hipError_t e = sa.once.run([&](int d) {   // with device d current
+        void* p = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (r == hipSuccess) sa.ptr[d] = p;   // published by run() before it reports success
+        return r;
+    });
+    int dev = 0;
+    if (e == hipSuccess) e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    *out = sa.ptr[dev];
+    return *out ? hipSuccess : hipErrorInvalidSymbol;
+}
+
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int kD = 64;
 constexpr int kChunk = 32;
@@ -331,6 +360,24 @@ wkv7_status wkv7_fwd_proj(int B, int T, int H, int D, wkv7_dtype in_dtype, const
                           void* stream) {
     return fwd_impl(B, T, H, D, in_dtype, true, r, w_raw, k, v, kappa, alpha, h0, y, h_ckpt, hT, workspace,
                     workspace_bytes, stream);
+}
+
+size_t wkv7_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+wkv7_status wkv7_fwd_noalloc(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r, const void* w,
+                             const void* k, const void* v, const void* a, const void* b, const float* h0,
+                             float* y, float* h_ckpt, float* hT, void* stream) {
+    Sizes sz;
+    wkv7_status st = check_fwd(B, T, H, D, in_dtype, r, w, k, v, a, b, h0, y, h_ckpt, hT, &sz);
+    if (st != WKV7_OK) return st;
+    if (T <= kSequentialMaxT)   // the one-token path uses no scratch
+        return fwd_impl(B, T, H, D, in_dtype, false, r, w, k, v, a, b, h0, y, h_ckpt, hT, nullptr, 0, stream);
+    if ((size_t)ops_bytes(sz) > kScratchBytes) return WKV7_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return WKV7_ERR_HIP;
+    // every byte of the chunk operands is written by the prepare kernel before
+    // the scan reads it, so the scratch needs no clearing
+    return fwd_impl(B, T, H, D, in_dtype, false, r, w, k, v, a, b, h0, y, h_ckpt, hT, ws, kScratchBytes, stream);
 }
 
 wkv7_status wkv7_fwd_sequential(int B, int T, int H, int D, wkv7_dtype in_dtype, const void* r,

@@ -309,3 +309,26 @@ def test_entry_points_from_two_threads():
     expect = (32, lib.wkv7_bwd_workspace_bytes(2, 100, 3, 64), lib.wkv7_status_str(6), ERR_HIP, ERR_HIP, ERR_HIP,
               ERR_SHAPE)
     assert len(results) == 400 and all(r == expect for r in results)
+
+
+@needs_no_gpu
+def test_fwd_noalloc_host_checks():
+    """wkv7_fwd_noalloc: wkv7_fwd's checks, then a refusal of operands larger
+    than the library's static scratch, both before any launch."""
+    lib = L.lib()
+    cap = lib.wkv7_fwd_noalloc_max_bytes()
+    assert cap == 128 << 20
+
+    def c(**o):
+        a = fwd_args(**o)
+        return lib.wkv7_fwd_noalloc(a["B"], a["T"], a["H"], a["D"], a["dt"], a["r"], a["w"], a["k"], a["v"],
+                                    a["a"], a["b"], a["h0"], a["y"], a["ck"], a["hT"], None)
+
+    assert c(D=32) == ERR_SHAPE
+    assert c(v=None) == ERR_ARG
+    assert c(y=fake(3)) == ERR_ALIAS
+    assert L.fwd_workspace_bytes(16, 1024, 8) > cap
+    big = lambda n: BASE + n * (1 << 30)
+    assert c(B=16, T=1024, H=8, r=big(0), w=big(1), k=big(2), v=big(3), a=big(4), b=big(5), y=big(6),
+             ck=big(7), hT=big(8)) == ERR_WS
+    assert c() == ERR_HIP           # fits: passes the host checks, then no GPU to launch on
