@@ -36,6 +36,37 @@ HBM_PEAK_GBS = 8000.0
 D = 64
 CSRC = os.path.join(ROOT, "linear_rnn_lm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+FLUSH_BYTES = 1 << 30   # read before every timed step: more than the L2s and the 256 MB MALL
+MIN_WARMUP_S = 0.5      # warm-up lasts at least this long (the clocks settle under sustained load)
+
+
+class Flush:
+    """Evicts the L2s and the MALL by reading a 1 GiB buffer (a sum).  A read
+    is used rather than a write: a write leaves 256 MB of dirty lines whose
+    write-back would land in the first timed kernels; a read writes back
+    whatever is dirty during the flush itself and leaves clean lines."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.zeros(FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
+        self.acc = torch.zeros((), device=dev, dtype=torch.float32)
+        self.torch = torch
+
+    def __call__(self):
+        self.torch.sum(self.buf, out=self.acc)
+
+
+def warm_up(torch, fn, steps):
+    """At least `steps` calls and at least MIN_WARMUP_S seconds of them."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < steps or time.perf_counter() - t0 < MIN_WARMUP_S:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 OPS_BYTES = 36864      # transition operands P, M, E, F of one chunk of one head
 
 
@@ -48,9 +79,17 @@ def source_digest() -> str:
 
 
 def kernel_bytes(wl, in_bytes: int) -> dict:
-    """Bytes each kernel must move per launch (inputs read once, outputs
-    written once).  Per head-token with bf16 inputs the path moves 1,536 B
-    forward and 3,072 B backward."""
+    """Algorithmic bytes of each kernel per launch: its share of what the
+    method itself must move (each input read once per pass, y, the gradients,
+    hT and dh0 written once, the checkpoints written once by the forward and
+    read once by the backward, dy read once).  Per head-token with bf16
+    inputs: chunk_prepare 640 (r, w, k, a, b: the forward's read), fwd_scan
+    896 (v, y, checkpoints), bwd_scan 256 (dv), bwd_inputs 2,816 (the six
+    inputs, dy, the checkpoints, five gradients); they add up to the path's
+    1,536 B forward + 3,072 B backward.  Everything else a kernel moves --
+    the chunk operands and inverses, the state gradients at chunk boundaries,
+    the backward scan's read of dy -- is recompute or hand-off traffic of this
+    design, reported separately by `extra_bytes`."""
     ht = wl.B * wl.T * wl.H          # head-tokens
     heads = wl.B * wl.H
     nc = (wl.T + 31) // 32
@@ -58,17 +97,34 @@ def kernel_bytes(wl, in_bytes: int) -> dict:
     tok32 = ht * D * 4
     st = heads * D * D * 4
     ck = heads * nc * D * D * 4
+    h0 = st if wl.with_h0 else 0
+    alg = {
+        "chunk_prepare": 5 * tok_in,
+        "fwd_scan": tok_in + tok32 + ck + h0 + st,
+        "bwd_scan": tok32 + st,
+        "bwd_inputs": 6 * tok_in + tok32 + ck + 5 * tok32,
+    }
+    alg["path"] = sum(alg.values())
+    return alg
+
+
+def extra_bytes(wl) -> dict:
+    """Bytes each kernel moves beyond its algorithmic share: intermediates of
+    the chunked design (written once, read back) and re-reads."""
+    heads = wl.B * wl.H
+    nc = (wl.T + 31) // 32
+    tok32 = wl.B * wl.T * wl.H * D * 4
+    ck = heads * nc * D * D * 4
     inv = heads * nc * 32 * 32 * 4
     ops = heads * nc * OPS_BYTES
-    h0 = st if wl.with_h0 else 0
-    return {
-        "chunk_prepare": 5 * tok_in + inv + ops,
-        "fwd_scan": tok_in + ops + h0 + tok32 + ck + st,
-        "bwd_scan": tok32 + ops + tok32 + ck + st,
-        "bwd_inputs": 6 * tok_in + inv + tok32 + 2 * ck + 5 * tok32,
-        # whole path, algorithmic: fwd 1536 B and bwd 3072 B per head-token (bf16 inputs)
-        "path": (6 * tok_in + tok32 + ck + h0 + st) + (6 * tok_in + tok32 + ck + 6 * tok32 + st),
+    ex = {
+        "chunk_prepare": inv + ops,          # chunk inverses and operands written
+        "fwd_scan": ops,                     # operands read
+        "bwd_scan": tok32 + ops + ck,        # dy read again, operands read, state gradients written
+        "bwd_inputs": inv + ck,              # inverses and state gradients read
     }
+    ex["path"] = sum(ex.values())
+    return ex
 
 
 def kernel_key(name: str):
@@ -128,6 +184,7 @@ def traffic_from(d: str, workload: str) -> dict:
         meas[ctr] = {k: sum(v) / len(v) * 1024 * scale for k, v in vals.items() if k != "copy"}
         meas[ctr + "_copy_scale"] = scale
     kb = kernel_bytes(wl, 2 if str(wl.dtype).endswith("bfloat16") else 4)
+    ex = extra_bytes(wl)
     out = {"copy_scale": {"FETCH_SIZE": meas["FETCH_SIZE_copy_scale"], "WRITE_SIZE": meas["WRITE_SIZE_copy_scale"]},
            "source_digest": source_digest(), "kernels": {}}
     for k in KERNEL_KEYS:
@@ -135,16 +192,64 @@ def traffic_from(d: str, workload: str) -> dict:
         if fb is None or wb is None:
             continue
         out["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
-                             "algorithmic_bytes": kb[k], "ratio": (fb + wb) / kb[k]}
+                             "algorithmic_bytes": kb[k], "extra_bytes": ex[k], "ratio": (fb + wb) / kb[k],
+                             "ratio_to_alg_plus_extra": (fb + wb) / (kb[k] + ex[k])}
+    ks = out["kernels"]
+    if all(k in ks for k in KERNEL_KEYS):
+        tot = sum(ks[k]["bytes_per_launch"] for k in KERNEL_KEYS)
+        out["step"] = {"bytes": tot, "algorithmic_bytes": kb["path"], "extra_bytes": ex["path"],
+                       "ratio": tot / kb["path"]}
     return out
+
+
+# Utilisation counters of every kernel, one rocprofv3 --pmc pass each (at most
+# four SQ counters per pass): the derived metrics' own definitions, averaged
+# over the dispatches of each kernel.
+UTIL_PASSES = (("valu", "VALUBusy MfmaUtil"), ("lds", "LdsUtil LDSBankConflict"))
+
+
+def counters_from(d: str) -> dict:
+    """Utilisation per kernel from rocprofv3 --pmc runs in d/valu, d/lds."""
+    vals = {}
+    for sub, _ in UTIL_PASSES:
+        for r in _pmc_rows(os.path.join(d, sub)):
+            key = kernel_key(r["Kernel_Name"])
+            if key:
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    kern = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    return {"source_digest": source_digest(), "kernels": kern,
+            "definitions": {"VALUBusy": "100 * SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE",
+                            "MfmaUtil": "100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs)",
+                            "LdsUtil": "100 * SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE * CUs)",
+                            "LDSBankConflict": "100 * SQ_LDS_BANK_CONFLICT / GRBM_GUI_ACTIVE / CUs"}}
+
+
+def host_cpu() -> dict:
+    """The host's CPU model and core counts."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": avail, "os_cpu_count": os.cpu_count()}
 
 
 def cpu_baseline(wl, budget_s: float) -> dict:
     """The oracle, as it stands, on the host cores: whole fwd+bwd passes of the
-    workload (a subset of heads if one pass would exceed the budget)."""
+    workload (a subset of heads if one pass would exceed the budget).  One
+    worker thread per available core, at most 16 (this process's share of a
+    shared GPU host)."""
     import oracle
     from linear_rnn_lm_amd.inputs import make_inputs
-    threads = min(oracle.default_threads(), 16)
+    threads = oracle.default_threads()
     # probe with a few heads to size the sample
     probe_heads = min(wl.heads, threads)
     xb = make_inputs(1, wl.T, probe_heads, wl.dtype, seed=wl.seed, with_h0=wl.with_h0)
@@ -168,7 +273,8 @@ def cpu_baseline(wl, budget_s: float) -> dict:
     tokens = B * wl.T * reps * (H / wl.H)    # tokens of the full-width layer
     return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle fwd+bwd on B{B} T{wl.T} H{H} ({B * H} of {wl.heads} heads), "
-                      f"{reps} pass(es) in {el:.1f} s; tokens scaled by {H}/{wl.H} heads"}
+                      f"{reps} pass(es) in {el:.1f} s, {threads} threads; tokens scaled by {H}/{wl.H} heads",
+            **host_cpu()}
 
 
 STEP_METRIC = "WKV7 recurrent step tokens/s and % HBM peak, 32 layers x B256 T1 H64 D64 (1 MI355X)"
@@ -317,7 +423,7 @@ def bench_prologue(args, wl) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": compute_dtype(in_bytes),
         "data": "synthetic",
         "config": {"workload": f"{wl.name} with raw projections w_raw, kappa, alpha: {wl.description}",
                    "B": B, "T": T, "H": H, "D": D,
@@ -381,9 +487,7 @@ def bench_step(args, wl) -> int:
         for c in calls:
             call(c)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(torch, step, args.warmup)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
@@ -470,7 +574,22 @@ def main() -> int:
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="no GPU work: write profiles/traffic.json from rocprofv3 --pmc runs in DIR/fetch, DIR/write")
+    ap.add_argument("--counters-from", metavar="DIR",
+                    help="no GPU work: write profiles/counters.json from rocprofv3 --pmc runs in DIR/valu, DIR/lds")
+    ap.add_argument("--fwd-ab", action="store_true",
+                    help="time the chunked forward against the token-by-token forward on the workload")
     args = ap.parse_args()
+
+    if args.counters_from:
+        cf = {}
+        if os.path.exists(COUNTERS_FILE):
+            with open(COUNTERS_FILE) as f:
+                cf = json.load(f)
+        cf[args.workload] = counters_from(args.counters_from)
+        with open(COUNTERS_FILE, "w") as f:
+            json.dump(cf, f, indent=1, sort_keys=True)
+        print(json.dumps(cf[args.workload], indent=1))
+        return 0
 
     if args.traffic_from:
         tr = {}
@@ -502,6 +621,39 @@ def main() -> int:
         return bench_prologue(args, wl)
     if args.division:
         return bench_division(args, wl)
+    if args.fwd_ab:
+        return bench_fwd_ab(args, wl)
+    return bench_train_step(args, wl)
+
+
+def _digest_entry(path, workload):
+    """The workload's entry of a counters file, if it was taken on the current sources."""
+    try:
+        with open(path) as f:
+            ent = json.load(f).get(workload, {})
+    except (OSError, ValueError):
+        return None
+    return ent if ent.get("source_digest") == source_digest() else None
+
+
+def _stats(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    med = ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+    return {"mean": sum(ys) / n, "median": med, "min": ys[0], "max": ys[-1], "n": n}
+
+
+def bench_train_step(args, wl) -> int:
+    """One step = chunk_prepare, fwd_scan, bwd_scan, bwd_inputs on the current
+    stream.  Timing: before every timed step a 1 GiB buffer is written, which
+    evicts the L2s and the 256 MB MALL, so each step starts from HBM; the step
+    is bracketed by two events (flush outside).  A second flushed pass puts
+    events between the kernels for per-kernel durations.  The same steps back
+    to back without flushes are timed as well (the 'unflushed' figures)."""
+    import torch
+    import linear_rnn_lm_amd as L
+    from linear_rnn_lm_amd.inputs import workload_inputs
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = workload_inputs(wl)
@@ -519,13 +671,13 @@ def main() -> int:
     dv = torch.empty(B, T, H, D, **f32)
     dh0 = torch.empty(B, H, D, D, **f32)
     grads = [torch.empty(B, T, H, D, **f32) for _ in range(5)]
+    flush = Flush(torch, dev)
     lib = L.lib()
     code = 1 if wl.dtype == torch.bfloat16 else 0
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     p = [t.data_ptr() for t in ins]
     ph0 = None if h0 is None else h0.data_ptr()
-
     pops = ops.data_ptr()
 
     def k_prep():
@@ -554,45 +706,57 @@ def main() -> int:
         for _, fn in kernels:
             fn()
 
-    for _ in range(args.warmup):
+    def flushed_step():
+        flush()
         step()
-    torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps between two events on the launch stream
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_warm = warm_up(torch, flushed_step, args.warmup)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # pass 1, the timed region: exactly `steps` steps, each flushed first and
+    # bracketed by two events on the launch stream
+    marks = [(ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    for a, b in marks:
+        flush()
+        a.record(stream)
         step()
-    ev1.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-
-    # per-kernel durations: events between the launches of every step
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in marks]
+    # pass 2: per-kernel durations, events between the launches of every flushed step
+    kev = [[ev() for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
     for s in range(args.steps):
-        evs[s][0].record(stream)
+        flush()
+        kev[s][0].record(stream)
         for i, (_, fn) in enumerate(kernels):
             fn()
-            evs[s][i + 1].record(stream)
+            kev[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    per_kernel_ms = {name: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
-                     for i, (name, _) in enumerate(kernels)}
+    kernel_ms = {name: _stats([kev[s][i].elapsed_time(kev[s][i + 1]) for s in range(args.steps)])
+                 for i, (name, _) in enumerate(kernels)}
+    # pass 3: the same steps back to back, no flushes
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    unflushed_ms = e0.elapsed_time(e1) / args.steps
 
     in_bytes = 2 if wl.dtype == torch.bfloat16 else 4
     kb = kernel_bytes(wl, in_bytes)
-    dom = max(per_kernel_ms, key=per_kernel_ms.get)
-    achieved = kb[dom] / (per_kernel_ms[dom] * 1e-3) / 1e9
+    ex = extra_bytes(wl)
+    st_ms = _stats(step_ms)
+    ms_per_step = st_ms["mean"]
+    dom = max(kernel_ms, key=lambda k: kernel_ms[k]["mean"])
+    dom_ms = kernel_ms[dom]["mean"]
+    achieved = kb[dom] / (dom_ms * 1e-3) / 1e9
     traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        ent = tr.get(args.workload, {})
-        if ent.get("source_digest") == source_digest() and dom in ent.get("kernels", {}):
-            traffic = ent["kernels"][dom]["bytes_per_launch"]
-    except (OSError, ValueError):
-        pass
+    tr = _digest_entry(TRAFFIC_FILE, wl.name)
+    if tr and dom in tr.get("kernels", {}):
+        traffic = tr["kernels"][dom]["bytes_per_launch"]
+    util = _digest_entry(COUNTERS_FILE, wl.name)
 
     tokens = B * T
     out = {
@@ -606,21 +770,112 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": compute_dtype(in_bytes),
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: WKV7 fwd+bwd {wl.description}, chunk 32",
                    "B": B, "T": T, "H": H, "D": D,
                    "in_dtype": "bf16" if in_bytes == 2 else "f32", "state_dtype": "f32"},
-        "fwd_tokens_per_s": tokens / ((per_kernel_ms["fwd_scan"] + per_kernel_ms["chunk_prepare"]) * 1e-3),
-        "kernel_ms": per_kernel_ms,
+        "timing": {"protocol": f"each timed step preceded by a {FLUSH_BYTES >> 30} GiB read (L2 and MALL "
+                               "flushed); ms_per_step = mean of the flushed steps",
+                   "warmup_steps_run": n_warm,
+                   "flushed_ms": st_ms,
+                   "unflushed_ms_per_step": unflushed_ms,
+                   "unflushed_tokens_per_s": tokens / (unflushed_ms * 1e-3)},
+        "fwd_tokens_per_s": tokens / ((kernel_ms["fwd_scan"]["mean"] + kernel_ms["chunk_prepare"]["mean"]) * 1e-3),
+        "kernel_ms": {k: v["mean"] for k, v in kernel_ms.items()},
+        "kernel_ms_stats": kernel_ms,
         "path_hbm": {"algorithmic_bytes": kb["path"],
+                     "extra_bytes": ex["path"],
                      "achieved_GBs": kb["path"] / (ms_per_step * 1e-3) / 1e9,
                      "frac_of_peak": kb["path"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": kb[dom], "extra_bytes": ex[dom],
+                     "traffic_over_algorithmic": None if traffic is None else traffic / kb[dom]},
     }
+    if tr and "step" in tr:
+        out["path_hbm"]["counter_bytes"] = tr["step"]["bytes"]
+        out["path_hbm"]["counter_over_algorithmic"] = tr["step"]["ratio"]
+    if util:
+        out["utilization_pct"] = util["kernels"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def compute_dtype(in_bytes: int) -> str:
+    """What the path computes in: bf16 inputs take bf16 MFMA products of a
+    two-term (hi + lo) split of every fp32 operand, three products per term
+    pair, accumulated in fp32; fp32 inputs take fp32 MFMA products."""
+    return "bf16x3-split-mfma/f32-acc" if in_bytes == 2 else "f32-mfma/f32-acc"
+
+
+FWD_AB_METRIC = "WKV7 forward tokens/s: chunked (matrix cores) vs token-by-token (vector units) (1 MI355X)"
+
+
+def bench_fwd_ab(args, wl) -> int:
+    """The forward two ways on the same inputs and outputs: the chunked form
+    (chunk_prepare + fwd_scan, the matrix-core path wkv7_fwd takes for T > 1)
+    and the token-by-token kernel (wkv7_fwd_sequential, vector units only).
+    Each timed call is preceded by the 1 GiB flush."""
+    import torch
+    import linear_rnn_lm_amd as L
+    from linear_rnn_lm_amd.inputs import workload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = workload_inputs(wl)
+    ins = [t.to(dev) for t in x.tensors()]
+    h0 = None if x.h0 is None else x.h0.to(dev)
+    B, T, H = wl.B, wl.T, wl.H
+    f32 = dict(device=dev, dtype=torch.float32)
+    y = torch.empty(B, T, H, D, **f32)
+    ck = torch.empty(B, H, L.num_chunks(T), D, D, **f32)
+    hT = torch.empty(B, H, D, D, **f32)
+    ws = torch.empty(L.fwd_workspace_bytes(B, T, H) // 4, **f32)
+    flush = Flush(torch, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def chunked():
+        L.fwd(*ins, h0, y=y, ckpt=ck, hT=hT, workspace=ws)
+
+    def sequential():
+        L.fwd_sequential(*ins, h0, y=y, ckpt=ck, hT=hT)
+
+    res = {}
+    for name, fn in (("chunked", chunked), ("sequential", sequential)):
+        warm_up(torch, fn, args.warmup)
+        times = []
+        for _ in range(args.steps):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        res[name] = _stats(times)
+    tokens = B * T
+    out = {
+        "metric": FWD_AB_METRIC,
+        "value": tokens / (res["chunked"]["mean"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["chunked"]["mean"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": compute_dtype(2 if wl.dtype == torch.bfloat16 else 4),
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: forward only, {wl.description}", "B": B, "T": T, "H": H, "D": D},
+        "chunked_ms": res["chunked"],
+        "sequential_ms": res["sequential"],
+        "sequential_tokens_per_s": tokens / (res["sequential"]["mean"] * 1e-3),
+        "speedup_chunked_over_sequential": res["sequential"]["mean"] / res["chunked"]["mean"],
+    }
     print(json.dumps(out), flush=True)
     return 0
 

@@ -32,3 +32,21 @@ def test_path_bytes_per_head_token():
     fwd = ht * 64 * (6 * 4 + 4) + heads * nc * 64 * 64 * 4 + 2 * heads * 64 * 64 * 4
     bwd = ht * 64 * (6 * 4 + 4 + 6 * 4) + heads * nc * 64 * 64 * 4 + heads * 64 * 64 * 4
     assert kb3["path"] == fwd + bwd
+
+
+def test_kernel_shares_add_up_to_the_path():
+    """Each kernel's algorithmic share (per head-token, bf16 inputs):
+    prepare 640, forward scan 896, backward scan 256, input gradients 2,816;
+    the chunk operands, inverses, state gradients and the second read of dy
+    are extra, 4,992 B, so the whole step moves 9,600 B per head-token."""
+    wl = Workload("t", 2, 640, 3, torch.bfloat16, 0, False)
+    ht, heads = 2 * 640 * 3, 6
+    kb, ex = bench.kernel_bytes(wl, 2), bench.extra_bytes(wl)
+    st = heads * 64 * 64 * 4
+    assert kb["chunk_prepare"] == 640 * ht
+    assert kb["fwd_scan"] == 896 * ht + st
+    assert kb["bwd_scan"] == 256 * ht + st
+    assert kb["bwd_inputs"] == 2816 * ht
+    assert kb["path"] == sum(kb[k] for k in bench.KERNEL_KEYS)
+    assert ex["path"] == 4992 * ht
+    assert kb["path"] + ex["path"] == 9600 * ht + 2 * st
