@@ -53,7 +53,7 @@ class Flush:
         self.torch = torch
 
     def __call__(self):
-        self.torch.sum(self.buf, out=self.acc)
+        self.torch.sum(self.buf, dim=0, out=self.acc)
 
 
 def warm_up(torch, fn, steps):

@@ -278,14 +278,13 @@ struct OpsImage {
 // Thread tid of NT moves the 16-byte units tid + NT * u.  F's tile of
 // columns 16-31 in rows 0-15 is zero (F is lower triangular): its units are
 // loaded at an offset past the block, so the buffer load returns 0 without
-// reading memory and the LDS image gets the zeros.
+// reading memory and the LDS image gets the zeros.  OpsMap holds the
+// thread's (constant) offsets, OpsCopy one chunk's data in registers.
 template <bool SPLIT, int NT>
-struct OpsCopy {
+struct OpsMap {
     static constexpr int N16 = kOpsBytes / 16;
     static constexpr int PER = N16 / NT;
     static_assert(N16 % NT == 0, "operand block split");
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 v[PER];
     int off[PER];  // LDS byte offsets inside a buffer
     int src[PER];  // byte offsets inside the operand block (past it for the zero tile)
 
@@ -314,17 +313,38 @@ struct OpsCopy {
             src[u] = zero_tile ? (int)kDropOffset : (tid + NT * u) * 16;
         }
     }
-    __device__ __forceinline__ void load(const char* base, int) {
-        const Rsrc r = make_rsrc(base, kOpsBytes);
+};
+
+// The units u of a thread with (u & 1) == PAR (PAR = -1: every unit; -2:
+// none).  Registers of the other units are never touched.  (A split of each
+// operand block between the two workgroups of a head, one parity fetched
+// early and the partner's parity late as L2 hits, measured no faster.)
+template <bool SPLIT, int NT, int PAR>
+struct OpsCopy {
+    using Map = OpsMap<SPLIT, NT>;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    static constexpr bool has(int u) { return PAR == -1 || (PAR >= 0 && (u & 1) == PAR); }
+    u32x4 v[Map::PER];
+
+    // on == false (a chunk past the last): a size-0 resource, the loads
+    // return 0 and touch no memory
+    __device__ __forceinline__ void load(const char* base, bool on, const Map& m) {
+        const Rsrc r = make_rsrc(base, on ? kOpsBytes : 0u);
 #pragma unroll
-        for (int u = 0; u < PER; ++u)
-            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, src[u], 0, 0));
+        for (int u = 0; u < Map::PER; ++u)
+            if (has(u)) v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, m.src[u], 0, 0));
     }
-    __device__ __forceinline__ void store(char* buf) const {
+    __device__ __forceinline__ void store(char* buf, const Map& m) const {
 #pragma unroll
-        for (int u = 0; u < PER; ++u) *reinterpret_cast<u32x4*>(buf + off[u]) = v[u];
+        for (int u = 0; u < Map::PER; ++u)
+            if (has(u)) *reinterpret_cast<u32x4*>(buf + m.off[u]) = v[u];
     }
 };
+
+// Chunks of operands and token rows in flight per memory thread (register
+// sets).  Two cover the load latency: four measured the same (a CU streams
+// cold operand blocks at about 12 B/cycle either way) with twice the registers.
+constexpr int SCAN_DEPTH = 2;
 
 // LDS plan of the scan: double buffers of one chunk's operands, of its
 // token rows (v exact, or dy split) and of its output rows (y or dv, fp32).
@@ -454,49 +474,57 @@ __global__ __launch_bounds__(64 * (NCW + NMW)) void scan_kernel(ScanArgs p, int 
         const Rsrc rx = make_rsrc(static_cast<const XT*>(p.x) + tok0 + i0, head_span * sizeof(XT));
         const Rsrc ro = make_rsrc(p.out ? p.out + tok0 + i0 : nullptr, p.out ? head_span * 4 : 0);
         const Rsrc rnull = make_rsrc(nullptr, 0);
-        OpsCopy<SPLIT, NTM> oa, ob;
-        XCopy<XT, SPLIT, NWV, NTM> xa, xb;
-        oa.init(ct);
-        ob.init(ct);
-        auto fetch = [&](OpsCopy<SPLIT, NTM>& o, XCopy<XT, SPLIT, NWV, NTM>& x, int it) {
-            o.load(ops_of(it), ct);
-            x.load(rx, chunk_of(min(it, NC - 1)), HD, ct);
-        };
-        auto put = [&](const OpsCopy<SPLIT, NTM>& o, const XCopy<XT, SPLIT, NWV, NTM>& x, int it) {
-            o.store(smem + (it & 1) * L::OPS);
-            x.store(xmat(it), ct);
-        };
-        // outputs of iteration it - 1 (nothing before the first)
+        using Map = OpsMap<SPLIT, NTM>;
+        using XC = XCopy<XT, SPLIT, NWV, NTM>;
+        Map map;
+        map.init(ct);
+        // outputs of iteration it - 1 (nothing before the first or past the last)
         auto out = [&](int it) {
-            store_out<NWV, NTM>(obuf(it - 1), it > 0 ? ro : rnull, chunk_of(max(it - 1, 0)), HD, ct);
+            const bool on = it > 0 && it <= NC;
+            store_out<NWV, NTM>(obuf(it - 1), on ? ro : rnull, chunk_of(min(max(it - 1, 0), NC - 1)), HD, ct);
         };
-        fetch(oa, xa, 0);
-        put(oa, xa, 0);
-        fetch(ob, xb, 1);
-        // Keep chunk 1's loads ahead of chunk 2's: entering the loop with chunk
-        // 1 issued last would make the compiler's count at the loop top (where
-        // chunk 1 is consumed) a full drain in every iteration.
-        __builtin_amdgcn_sched_barrier(0);
-        fetch(oa, xa, 2);
+        // SCAN_DEPTH register sets: chunk j travels in set j % SCAN_DEPTH
+        OpsCopy<SPLIT, NTM, -1> o[SCAN_DEPTH];
+        XC x[SCAN_DEPTH];
+        auto fetch = [&](auto set_c, int it) {
+            constexpr int S = decltype(set_c)::value;
+            const bool on = it < NC;
+            o[S].load(ops_of(it), on, map);
+            x[S].load(on ? rx : rnull, chunk_of(min(it, NC - 1)), HD, ct);
+        };
+        auto put = [&](auto set_c, int it) {
+            constexpr int S = decltype(set_c)::value;
+            o[S].store(smem + (it & 1) * L::OPS, map);
+            x[S].store(xmat(it), ct);
+        };
+        using S0 = std::integral_constant<int, 0>;
+        fetch(S0{}, 0);
+        put(S0{}, 0);
+        // Chunks 1 .. SCAN_DEPTH go out in order, so that the count of
+        // outstanding loads at each put is exact (loads complete in order).
+        static_for<SCAN_DEPTH>([&](auto s_c) {
+            constexpr int S = decltype(s_c)::value;
+            fetch(std::integral_constant<int, (S + 1) % SCAN_DEPTH>{}, S + 1);
+        });
         lds_barrier();
-        // Two iterations per trip, straight-line code (so that every wait is
+        // SCAN_DEPTH iterations per trip, straight-line code (every wait
         // counted exactly).  In iteration it: chunk it + 1 goes into the
         // buffers the compute waves finished reading in iteration it - 1, its
-        // register set is refilled with chunk it + 3 (clamped), and the
-        // outputs of chunk it - 1 go to memory.  Writes past the last chunk
-        // land in buffers nobody reads any more.  An odd NC ends with one
-        // extra barrier, matched by the compute waves.
-        for (int it = 0; it < NC; it += 2) {
-            put(ob, xb, it + 1);
-            fetch(ob, xb, it + 3);
+        // register set is refilled with chunk it + 1 + SCAN_DEPTH, and the
+        // outputs of chunk it - 1 go to memory.  The trip count is rounded up
+        // to a multiple of SCAN_DEPTH; the compute waves match the extra
+        // barriers.  Chunks past the last load nothing (size-0 resources).
+        auto iter = [&](auto u_c, int it) {
+            using S = std::integral_constant<int, (decltype(u_c)::value + 1) % SCAN_DEPTH>;
+            put(S{}, it + 1);
+            fetch(S{}, it + 1 + SCAN_DEPTH);
             out(it);
             lds_barrier();
-            put(oa, xa, it + 2);
-            fetch(oa, xa, it + 4);
-            out(it + 1);
-            lds_barrier();
-        }
-        if (!(NC & 1)) out(NC);
+        };
+        const int trips = (NC + SCAN_DEPTH - 1) / SCAN_DEPTH;
+        for (int tr = 0; tr < trips; ++tr)
+            static_for<SCAN_DEPTH>([&](auto u_c) { iter(u_c, tr * SCAN_DEPTH + decltype(u_c)::value); });
+        if (trips * SCAN_DEPTH == NC) out(NC);
         return;
     }
 
@@ -609,7 +637,8 @@ __global__ __launch_bounds__(64 * (NCW + NMW)) void scan_kernel(ScanArgs p, int 
                 st[2 * (1 - HF) + 1] = x[64 + lane];
             }
         }
-        if (NC & 1) lds_barrier();  // the memory waves' last trip
+        for (int e = NC; e < (NC + SCAN_DEPTH - 1) / SCAN_DEPTH * SCAN_DEPTH; ++e)
+            lds_barrier();   // the memory waves' last trip
         if (p.sT) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)

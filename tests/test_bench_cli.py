@@ -50,3 +50,22 @@ def test_kernel_shares_add_up_to_the_path():
     assert kb["path"] == sum(kb[k] for k in bench.KERNEL_KEYS)
     assert ex["path"] == 4992 * ht
     assert kb["path"] + ex["path"] == 9600 * ht + 2 * st
+
+
+def test_flush_and_warm_up_on_cpu():
+    """The cache flush is one reduction over its buffer; the warm-up runs at
+    least the asked number of calls and at least MIN_WARMUP_S seconds."""
+    f = bench.Flush(torch, torch.device("cpu"))
+    f.buf = torch.ones(1000)
+    f()
+    assert float(f.acc) == 1000.0
+
+    class Sync:
+        class cuda:
+            @staticmethod
+            def synchronize():
+                pass
+
+    calls = []
+    n = bench.warm_up(Sync, lambda: calls.append(1), 3)
+    assert n == len(calls) >= 3
