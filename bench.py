@@ -56,11 +56,13 @@ class Flush:
         self.torch.sum(self.buf, dim=0, out=self.acc)
 
 
-def warm_up(torch, fn, steps):
-    """At least `steps` calls and at least MIN_WARMUP_S seconds of them."""
+def warm_up(torch, fn, steps, min_s=None):
+    """At least `steps` calls and at least `min_s` (default MIN_WARMUP_S)
+    seconds of them."""
+    min_s = MIN_WARMUP_S if min_s is None else min_s
     t0 = time.perf_counter()
     n = 0
-    while n < steps or time.perf_counter() - t0 < MIN_WARMUP_S:
+    while n < steps or time.perf_counter() - t0 < min_s:
         fn()
         n += 1
         if n % 8 == 0:
@@ -200,6 +202,44 @@ def traffic_from(d: str, workload: str) -> dict:
         out["step"] = {"bytes": tot, "algorithmic_bytes": kb["path"], "extra_bytes": ex["path"],
                        "ratio": tot / kb["path"]}
     return out
+
+
+def trace_summary(d: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace of bench.py: per kernel,
+    every launch and the launches of flushed steps (those after the flush's
+    reduction and before the end of their step), in microseconds."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    stats = {}
+    flushed = False
+    for r in rows:
+        name = r["Kernel_Name"]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        key = kernel_key(name) or ("step_kernel" if "step_kernel" in name else
+                                   "fwd_sequential" if "fwd_sequential_kernel" in name else None)
+        if key is None:
+            if "reduce_kernel" in name:
+                flushed = True
+            continue
+        short = name.rsplit("(", 1)[0].split("::")[-1].replace("unsigned short", "bf16")
+        st = stats.setdefault(key, {"all": [], "flushed": [], "name": short})
+        st["all"].append(dur)
+        if flushed:
+            st["flushed"].append(dur)
+        if key == "bwd_inputs":   # the last kernel of a step
+            flushed = False
+    out = ["| kernel | calls | avg us | min us | max us | flushed calls | flushed avg us | flushed max/min |",
+           "|---|---|---|---|---|---|---|---|"]
+    for key, st in sorted(stats.items(), key=lambda kv: -sum(kv[1]["all"])):
+        a, fl = st["all"], st["flushed"]
+        fcol = (f"{len(fl)} | {sum(fl) / len(fl):.1f} | {max(fl) / min(fl):.3f}" if fl else "0 | - | -")
+        out.append(f"| `{st['name']}` ({key}) | {len(a)} | {sum(a) / len(a):.1f} | {min(a):.1f} | {max(a):.1f} | {fcol} |")
+    return "\n".join(out)
 
 
 # Utilisation counters of every kernel, one rocprofv3 --pmc pass each (at most
@@ -487,7 +527,7 @@ def bench_step(args, wl) -> int:
         for c in calls:
             call(c)
 
-    warm_up(torch, step, args.warmup)
+    warm_up(torch, step, args.warmup, args.min_warmup_s)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(args.steps):
@@ -564,6 +604,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="debug_36m")
+    ap.add_argument("--min-warmup-s", type=float, default=MIN_WARMUP_S,
+                    help="warm-up lasts at least this many seconds (short runs under a profiler: 0)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prologue", action="store_true",
@@ -576,9 +618,15 @@ def main() -> int:
                     help="no GPU work: write profiles/traffic.json from rocprofv3 --pmc runs in DIR/fetch, DIR/write")
     ap.add_argument("--counters-from", metavar="DIR",
                     help="no GPU work: write profiles/counters.json from rocprofv3 --pmc runs in DIR/valu, DIR/lds")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="no GPU work: print a markdown table of a rocprofv3 --kernel-trace of bench.py in DIR")
     ap.add_argument("--fwd-ab", action="store_true",
                     help="time the chunked forward against the token-by-token forward on the workload")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
 
     if args.counters_from:
         cf = {}
@@ -710,7 +758,7 @@ def bench_train_step(args, wl) -> int:
         flush()
         step()
 
-    n_warm = warm_up(torch, flushed_step, args.warmup)
+    n_warm = warm_up(torch, flushed_step, args.warmup, args.min_warmup_s)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     # pass 1, the timed region: exactly `steps` steps, each flushed first and
@@ -845,7 +893,7 @@ def bench_fwd_ab(args, wl) -> int:
 
     res = {}
     for name, fn in (("chunked", chunked), ("sequential", sequential)):
-        warm_up(torch, fn, args.warmup)
+        warm_up(torch, fn, args.warmup, args.min_warmup_s)
         times = []
         for _ in range(args.steps):
             flush()
