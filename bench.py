@@ -204,10 +204,12 @@ def traffic_from(d: str, workload: str) -> dict:
     return out
 
 
-def trace_summary(d: str) -> str:
+def trace_summary(d: str, steps: int) -> str:
     """Markdown table of a rocprofv3 --kernel-trace of bench.py: per kernel,
-    every launch and the launches of flushed steps (those after the flush's
-    reduction and before the end of their step), in microseconds."""
+    every launch, and the launches of the two timed flushed passes (the last
+    2 x steps launches that follow the flush's reduction within their step;
+    the warm-up steps before them are flushed too but not timed), in
+    microseconds."""
     import csv
     import glob
     rows = []
@@ -233,10 +235,10 @@ def trace_summary(d: str) -> str:
             st["flushed"].append(dur)
         if key == "bwd_inputs":   # the last kernel of a step
             flushed = False
-    out = ["| kernel | calls | avg us | min us | max us | flushed calls | flushed avg us | flushed max/min |",
+    out = ["| kernel | calls | avg us | min us | max us | timed flushed calls | their avg us | their max/min |",
            "|---|---|---|---|---|---|---|---|"]
     for key, st in sorted(stats.items(), key=lambda kv: -sum(kv[1]["all"])):
-        a, fl = st["all"], st["flushed"]
+        a, fl = st["all"], st["flushed"][-2 * steps:]
         fcol = (f"{len(fl)} | {sum(fl) / len(fl):.1f} | {max(fl) / min(fl):.3f}" if fl else "0 | - | -")
         out.append(f"| `{st['name']}` ({key}) | {len(a)} | {sum(a) / len(a):.1f} | {min(a):.1f} | {max(a):.1f} | {fcol} |")
     return "\n".join(out)
@@ -625,7 +627,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.trace_summary:
-        print(trace_summary(args.trace_summary))
+        print(trace_summary(args.trace_summary, args.steps))
         return 0
 
     if args.counters_from:
