@@ -346,6 +346,10 @@ struct OpsCopy {
 // cold operand blocks at about 12 B/cycle either way) with twice the registers.
 constexpr int SCAN_DEPTH = 2;
 
+// Token tensors (v or dy) of up to this many bytes are read into the caches
+// in one pass at the start of the scan (see the memory waves).
+constexpr uint64_t kTouchBytes = 32ull << 20;
+
 // LDS plan of the scan: double buffers of one chunk's operands, of its
 // token rows (v exact, or dy split) and of its output rows (y or dv, fp32).
 template <bool SPLIT, int NWV, int NCW>
@@ -499,6 +503,33 @@ __global__ __launch_bounds__(64 * (NCW + NMW)) void scan_kernel(ScanArgs p, int 
         };
         using S0 = std::integral_constant<int, 0>;
         fetch(S0{}, 0);
+        // A token tensor that the previous kernel did not touch comes from
+        // HBM, and each chunk's rows (32 lines at a stride of H D elements)
+        // then miss while the operand blocks stream: those misses hold up the
+        // operand loads of the whole CU behind them (11 us of the forward and
+        // 9 us of the backward scan at B12 T1024 H6 after a cache flush).  A
+        // tensor of up to kTouchBytes is therefore read once here, one word
+        // per line of this workgroup's columns of every token, by the last
+        // memory wave, so that its rows come from the caches; a larger one
+        // would not stay cached while the operands stream.  The words go
+        // straight to LDS (no registers), all into one 256-byte slot of the
+        // second output-row buffer: they complete before this wave's chunk-1
+        // rows (a wave's loads complete in order), so before the second
+        // barrier, after which the compute waves first write that buffer.
+        if (wave == NCW + NMW - 1 && (uint64_t)p.B * (uint64_t)p.T * (uint64_t)p.H * D * sizeof(XT) <= kTouchBytes) {
+            constexpr int LPR = (16 * NWV * (int)sizeof(XT) + 127) / 128;   // lines per token row here
+            __attribute__((address_space(3))) void* sink =
+                (__attribute__((address_space(3))) void*)reinterpret_cast<char*>(obuf(1));
+            for (int t0_ = 0; t0_ < p.T; t0_ += 64 * 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int l = 0; l < LPR; ++l)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rx, sink, 4, (int)((uint32_t)(t0_ + 64 * u + lane) * (uint32_t)HD * sizeof(XT) + 128u * l),
+                            0, 0, 0);
+            }
+        }
         put(S0{}, 0);
         // Chunks 1 .. SCAN_DEPTH go out in order, so that the count of
         // outstanding loads at each put is exact (loads complete in order).
