@@ -35,6 +35,9 @@ SMALL = [
     # chunks each (uneven counts), on the XCD-grouped (40 heads) and the
     # plain (300 heads) block order
     (3, 300, 40, BF16, True, True),
+    # more than 128 heads: one scan workgroup per head (64 state rows); fp32 token rows of 256
+    # bytes, so the scans' up-front read of v and dy (token tensors up to 32 MiB) takes two lines
+    # per row (the full-size B8 T4096 H32 case covers scans without that read)
     (1, 200, 300, F32, False, True),
 ]
 
