@@ -8,6 +8,7 @@ CPU fallback; if the library is missing, calls raise.
     y, ckpt, hT = fwd(r, w, k, v, a, b, h0)            # (B,T,H,64) inputs
     dr, dw, dk, dv, da, db, dh0 = bwd(dy, r, w, k, v, a, b, ckpt, dhT)
     WKV7.apply(r, w, k, v, a, b, h0)                   # autograd op -> (y, hT)
+    WKV7.apply(r, w, k, v, a, b, h0, False)            # the same, chunk operands not kept
 
 The recurrence (rwkv-mlx page, section "Metal kernel architecture"): per
 head a 64x64 fp32 state S; per token sa = S a, S = S diag(w) + v k^T + sa b^T,
@@ -440,14 +441,18 @@ def _make_autograd():
     import torch
 
     class WKV7(torch.autograd.Function):
-        """Differentiable op: (r, w, k, v, a, b, h0) -> (y, hT), gradients by wkv7_bwd."""
+        """Differentiable op: (r, w, k, v, a, b, h0, keep_ops) -> (y, hT), gradients by
+        wkv7_bwd.  keep_ops (default True): keep the chunk operands (1,152 B per
+        head-token, plus the chunk inverses) from the forward for the backward; False
+        keeps only the checkpoints (512 B per head-token) and the backward prepares
+        the operands again (one more pass of the prepare kernel)."""
 
         @staticmethod
-        def forward(ctx, r, w, k, v, a, b, h0=None):
+        def forward(ctx, r, w, k, v, a, b, h0=None, keep_ops=True):
             ins = [x.contiguous() for x in (r, w, k, v, a, b)]
             h0c = None if h0 is None else h0.contiguous().float()
             T = ins[0].shape[1]
-            if T > 1:   # chunked path: one set of chunk operands serves forward and backward
+            if T > 1 and keep_ops:   # one set of chunk operands serves forward and backward
                 ops = chunk_prepare(ins[0], ins[1], ins[2], ins[4], ins[5])
                 y, ckpt, hT = fwd_scan(ins[3], ops, h0c)
             else:
@@ -473,7 +478,7 @@ def _make_autograd():
                 dr, dw, dk, da, db = bwd_inputs(dy, r, w, k, v, a, b, ops, ckpt, dh_ck, dhT)
             cast = lambda g, x: g.to(x.dtype)
             grads = [cast(g, x) for g, x in zip((dr, dw, dk, dv, da, db), ins)]
-            return (*grads, dh0 if ctx.has_h0 else None)
+            return (*grads, dh0 if ctx.has_h0 else None, None)
 
     class WKV7Proj(torch.autograd.Function):
         """Differentiable op with the fused time-mix prologue: (r, w_raw, k, v, kappa, alpha, h0)

@@ -101,3 +101,20 @@ def test_device_buffers_rejected_before_launch():
     out = [torch.empty(B, T, H, D, device=DEV) for _ in range(6)]
     assert lib.wkv7_bwd(B, T, H, D, 1, dy.data_ptr(), None, *p, ck.data_ptr(), *[o.data_ptr() for o in out], None,
                         ws.data_ptr(), 64, s) == 7
+
+
+def test_autograd_op_without_kept_operands():
+    """keep_ops=False (the forward keeps only the checkpoints; the backward prepares
+    the chunk operands again) gives the same outputs and gradients, bit for bit."""
+    ins, h0, dy = _inputs(T=100, seed=11)
+    dhT = torch.randn(h0.shape, device=DEV)
+    res = []
+    for keep in (True, False):
+        leaves = [t.clone().requires_grad_(True) for t in ins] + [h0.clone().requires_grad_(True)]
+        note(f"autograd op keep_ops={keep}")
+        y, hT = L.WKV7.apply(*leaves, keep)
+        ((y * dy).sum() + (hT * dhT).sum()).backward()
+        res.append([y.detach(), hT.detach()] + [leaf.grad for leaf in leaves])
+    torch.cuda.synchronize()
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
