@@ -232,7 +232,7 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
 
   for (;;) {
     const ChunkPos cw(p, idx, xcd != 0);
-    const int head = cw.head, c = cw.c, bb = cw.bb, hh = cw.hh;
+    const int c = cw.c, bb = cw.bb, hh = cw.hh;
     const int nidx = idx + (int)gridDim.x;
     const bool more = nidx < total;
     const ChunkSrc nsrc(p, ChunkPos(p, more ? nidx : idx, xcd != 0), more);
