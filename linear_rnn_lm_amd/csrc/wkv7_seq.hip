@@ -112,9 +112,11 @@ __device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
 
 // One token (T = 1), the recurrent step: the same update as above, with the
 // state accessed as one contiguous 16 KiB block per head.  Thread tid holds
-// the four 4-column pieces at flat offsets 1024 q + 4 tid of the head's state:
-// rows tid / 16 + 16 q, columns 4 (tid % 16) .. + 3.  The 16 threads of a row
-// are one DPP row, so the row dot products need no LDS.
+// rows 4 (tid / 16) + q, q = 0..3, columns 4 (tid % 16) .. + 3: each access of
+// a wave covers four whole 256-byte rows, and a thread's four rows are
+// consecutive, so their v values arrive in one load and their y values leave
+// in one store.  The 16 threads of a row are one DPP row, so the row dot
+// products need no LDS.
 // PROJ: the w, a, b pointers hold the raw projections w_raw, kappa, alpha and
 // the time-mix prologue runs on the loaded values (the 16 lanes of a DPP row
 // hold one token's 64 channels, so |kappa| is a row sum).
@@ -124,15 +126,15 @@ __global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
     const int head = blockIdx.x;
     const int bb = head / p.H, hh = head % p.H;
     const int64_t base = ((int64_t)bb * p.H + hh) * D;      // this head's token row (T = 1)
-    const int c0 = 4 * (tid & 15), r0 = tid >> 4;
-    const int64_t hoff = (int64_t)head * D * D + 4 * tid;
+    const int c0 = 4 * (tid & 15), r0 = 4 * (tid >> 4);
+    const int64_t hoff = (int64_t)head * D * D + r0 * D + c0;
     f32x4 st[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)   // streamed once: non-temporal
-        st[q] = p.h0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.h0 + hoff + 1024 * q)) : zero4();
+        st[q] = p.h0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.h0 + hoff + D * q)) : zero4();
     if (p.ckpt) {   // checkpoint 0: the state entering the (only) chunk
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(p.ckpt + hoff + 1024 * q) = st[q];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(p.ckpt + hoff + D * q) = st[q];
     }
     f32x4 w = load4(static_cast<const InT*>(p.w) + base + c0);
     const f32x4 k = load4(static_cast<const InT*>(p.k) + base + c0);
@@ -152,9 +154,11 @@ __global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
         }
     }
     const f32x4 r = load4(static_cast<const InT*>(p.r) + base + c0);
+    const f32x4 vr = load4(static_cast<const InT*>(p.v) + base + r0);   // v of rows r0 .. r0 + 3
+    f32x4 yr;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const float vi = load1(static_cast<const InT*>(p.v) + base + r0 + 16 * q);
+        const float vi = vr[q];
         float sa = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) sa = fmaf(st[q][c], a[c], sa);
@@ -165,12 +169,12 @@ __global__ __launch_bounds__(SEQ_NT) void step_kernel(FwdArgs p) {
             st[q][c] = fmaf(w[c], st[q][c], fmaf(vi, k[c], sa * b[c]));
             y = fmaf(st[q][c], r[c], y);
         }
-        y = row16_allsum(y);
-        if (p.y && (tid & 15) == 0) p.y[base + r0 + 16 * q] = y;
+        yr[q] = row16_allsum(y);
     }
+    if (p.y && (tid & 15) == 0) *reinterpret_cast<f32x4*>(p.y + base + r0) = yr;
     if (p.hT) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) __builtin_nontemporal_store(st[q], reinterpret_cast<f32x4*>(p.hT + hoff + 1024 * q));
+        for (int q = 0; q < 4; ++q) __builtin_nontemporal_store(st[q], reinterpret_cast<f32x4*>(p.hT + hoff + D * q));
     }
 }
 
