@@ -653,7 +653,7 @@ def main() -> int:
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported. "
+        print(f"bench.py: measures exactly one GPU; --gpus {args.gpus} is not supported. "
               "The WKV7 op shards over heads with no exchange, so N GPUs each run this same "
               "single-GPU step on their share.", file=sys.stderr)
         return 2
