@@ -38,8 +38,8 @@ namespace {
 constexpr int GNT = 512;  // threads per workgroup (8 waves)
 constexpr int GNW = GNT / 64;
 
-// LDS plan (byte offsets).  Region Q holds T, Lak, Mrb, RHS_U, RHS_D until U
-// and DSA exist, then P1..P4 and the dw ingredients.
+// LDS plan (byte offsets).  Region Q holds T, Lak, Mrb until U and DSA exist,
+// then P1..P4 and the dw ingredients.
 template <bool SPLIT>
 struct GradSmem {
     using F = Fmt<SPLIT>;
@@ -61,9 +61,7 @@ struct GradSmem {
     static constexpr int Tm = Q;                     // T rows (t, s)
     static constexpr int Lak = Tm + CM;              // Lak rows (t, s)
     static constexpr int Mrb = Lak + CM;             // Mrb rows (t, s)
-    static constexpr int RU = Mrb + CM;              // RHS_U rows (s, i)
-    static constexpr int RD = RU + RM;               // RHS_D rows (s, i)
-    static constexpr int QEND1 = RD + RM;
+    static constexpr int QEND1 = Mrb + CM;
     // region Q, phases 4-6
     static constexpr int P1 = Q;                     // P1..P4 rows (t, s)
     static constexpr int HH = P1 + 4 * CM;           // fp32 [t][j]: k dk + b db - r dr - a da
@@ -129,7 +127,7 @@ struct ChunkSrc {
 
 // Everything one chunk reads from global memory, held in registers so that
 // the next chunk's loads are in flight while the current chunk computes.  The
-// loads are issued in five parts, one per compute phase, so that no wave
+// loads are issued in five parts spread over the compute phases, so that no wave
 // stalls on a full memory queue; buffer loads without branches keep the
 // wave's count of outstanding loads exact.
 template <typename InT, bool PROJ>
@@ -251,7 +249,6 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     const M S0m = make_mat<SPLIT>(smem, L::S0, D, D), Gem = make_mat<SPLIT>(smem, L::Ge, D, D);
     const M Tm = make_mat<SPLIT>(smem, L::Tm, C, C), Lak = make_mat<SPLIT>(smem, L::Lak, C, C);
     const M Mrb = make_mat<SPLIT>(smem, L::Mrb, C, C);
-    const M RU = make_mat<SPLIT>(smem, L::RU, C, D), RD = make_mat<SPLIT>(smem, L::RD, C, D);
     const M Um = make_mat<SPLIT>(smem, L::U, C, D), DSAm = make_mat<SPLIT>(smem, L::DSA, C, D);
     auto Pm = [&](int m) { return make_mat<SPLIT>(smem, L::P1 + m * L::CM, C, C); };
     float* gam = reinterpret_cast<float*>(smem + L::Gam);
@@ -314,48 +311,50 @@ __global__ __launch_bounds__(GNT) void grad_kernel(BwdArgs p, int xcd, int total
     lds_barrier();
 
     nxt.template issue<2>(p, nsrc, tid);
-    // ---- phase 2: RHS_U[s][i] = sum_j S0[i][j] Ahat[s][j] + sum_u V[u][i] Lak[s][u]
-    //               RHS_D[s][i] = sum_j Ge'[i][j] Btil[s][j] + sum_u DY[u][i] Mrb[u][s]
-    // (accumulator element (i, s); rows s stored with four consecutive i per lane)
-    {   // waves 0-3: RU, waves 4-7: RD; wave: column block ib, both row blocks s (the i-side
-        // fragments are read once for both)
+    // ---- phases 2 and 3 (no barrier between them):
+    // phase 2: RHS_U[s][i] = sum_j S0[i][j] Ahat[s][j] + sum_u V[u][i] Lak[s][u]
+    //          RHS_D[s][i] = sum_j Ge'[i][j] Btil[s][j] + sum_u DY[u][i] Mrb[u][s]
+    // phase 3: U[t][i] = sum_s T[t][s] RHS_U[s][i], DSA[t][i] = sum_s T[s][t] RHS_D[s][i].
+    // Waves 0-3: RHS_U and U, waves 4-7: RHS_D and DSA; wave: column block ib, both blocks of s
+    // (the i-side fragments are read once for both) and then both blocks of t.  The RHS tiles are
+    // formed as accumulator elements (s, i), which in the fragment order are the operand rows i
+    // over k = s of the U / DSA products: they never leave the registers.
+    {
         using Fr = Frag<SPLIT>;
         const int ib = wave & 3;
         f32x4 a0, a1;
         if (wave < 4) {
             const Fr x0 = frag_n(S0m, 16 * ib, 0, lane), x1 = frag_n(S0m, 16 * ib, 32, lane);
-            a0 = fmma(zero4(), x0, frag_n(A, 0, 0, lane));
-            a1 = fmma(zero4(), x0, frag_n(A, 16, 0, lane));
-            a0 = fmma(a0, x1, frag_n(A, 0, 32, lane));
-            a1 = fmma(a1, x1, frag_n(A, 16, 32, lane));
+            a0 = fmma(zero4(), frag_n(A, 0, 0, lane), x0);
+            a1 = fmma(zero4(), frag_n(A, 16, 0, lane), x0);
+            a0 = fmma(a0, frag_n(A, 0, 32, lane), x1);
+            a1 = fmma(a1, frag_n(A, 16, 32, lane), x1);
             const Fr xv = frag_t_exact(Vm, 16 * ib, 0, lane);
-            a0 = fmma<true, false>(a0, xv, frag_n(Lak, 0, 0, lane));
-            a1 = fmma<true, false>(a1, xv, frag_n(Lak, 16, 0, lane));
-            put4_pair(RU, r16, 16 * ib + 8 * (g4 >> 1), a0, g4);
-            put4_pair(RU, 16 + r16, 16 * ib + 8 * (g4 >> 1), a1, g4);
+            a0 = fmma<false, true>(a0, frag_n(Lak, 0, 0, lane), xv);
+            a1 = fmma<false, true>(a1, frag_n(Lak, 16, 0, lane), xv);
         } else {
             const Fr x0 = frag_n(Gem, 16 * ib, 0, lane), x1 = frag_n(Gem, 16 * ib, 32, lane);
-            a0 = fmma(zero4(), x0, frag_n(Bm, 0, 0, lane));
-            a1 = fmma(zero4(), x0, frag_n(Bm, 16, 0, lane));
-            a0 = fmma(a0, x1, frag_n(Bm, 0, 32, lane));
-            a1 = fmma(a1, x1, frag_n(Bm, 16, 32, lane));
+            a0 = fmma(zero4(), frag_n(Bm, 0, 0, lane), x0);
+            a1 = fmma(zero4(), frag_n(Bm, 16, 0, lane), x0);
+            a0 = fmma(a0, frag_n(Bm, 0, 32, lane), x1);
+            a1 = fmma(a1, frag_n(Bm, 16, 32, lane), x1);
             const Fr xd = frag_t(DYm, 16 * ib, 0, lane);
-            a0 = fmma(a0, xd, frag_t(Mrb, 0, 0, lane));
-            a1 = fmma(a1, xd, frag_t(Mrb, 16, 0, lane));
-            put4_pair(RD, r16, 16 * ib + 8 * (g4 >> 1), a0, g4);
-            put4_pair(RD, 16 + r16, 16 * ib + 8 * (g4 >> 1), a1, g4);
+            a0 = fmma(a0, frag_t(Mrb, 0, 0, lane), xd);
+            a1 = fmma(a1, frag_t(Mrb, 16, 0, lane), xd);
         }
-    }
-    lds_barrier();
-
-    nxt.template issue<3>(p, nsrc, tid);
-    // ---- phase 3: U[t][i] = sum_s T[t][s] RHS_U[s][i], DSA[t][i] = sum_s T[s][t] RHS_D[s][i]
-    {
-        const int ib = wave & 3, tb = wave >> 2;
-        const f32x4 au = fmma(zero4(), frag_t(RU, 16 * ib, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
-        const f32x4 ad = fmma(zero4(), frag_t(RD, 16 * ib, 0, lane), frag_t(Tm, 16 * tb, 0, lane));
-        put4_pair(Um, 16 * tb + r16, 16 * ib + 8 * (g4 >> 1), au, g4);
-        put4_pair(DSAm, 16 * tb + r16, 16 * ib + 8 * (g4 >> 1), ad, g4);
+        nxt.template issue<3>(p, nsrc, tid);
+        const Fr rhs = frag_acc<SPLIT>(a0, a1);   // rows i = 16 ib + r, k = s
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            // accumulator element (i, t)
+            if (wave < 4) {
+                const f32x4 au = fmma(zero4(), rhs, frag_n(Tm, 16 * tb, 0, lane));
+                put4_pair(Um, 16 * tb + r16, 16 * ib + 8 * (g4 >> 1), au, g4);
+            } else {
+                const f32x4 ad = fmma(zero4(), rhs, frag_t(Tm, 16 * tb, 0, lane));
+                put4_pair(DSAm, 16 * tb + r16, 16 * ib + 8 * (g4 >> 1), ad, g4);
+            }
+        }
     }
     lds_barrier();
 
