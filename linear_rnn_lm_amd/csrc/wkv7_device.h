@@ -801,6 +801,16 @@ __device__ __forceinline__ Frag<SPLIT> frag_acc(f32x4 a0, f32x4 a1) {
     return f;
 }
 
+// Rows of an fp32 LDS matrix (row stride ld floats) as an operand fragment,
+// split in registers for the bf16 format: lane (g, r) gets
+// X[row0 + r][c0 + 16h + 4g + q] (the order of frag_n).
+template <bool SPLIT>
+__device__ __forceinline__ Frag<SPLIT> frag_n_f32(const float* X, int ld, int row0, int c0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const float* p = X + (row0 + r) * ld + c0 + 4 * g;
+    return frag_acc<SPLIT>(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 16));
+}
+
 // Fragment of values exact in bf16 (SPLIT: the lo part is never read).
 template <bool SPLIT>
 __device__ __forceinline__ Frag<SPLIT> frag_exact(f32x4 a0, f32x4 a1) {

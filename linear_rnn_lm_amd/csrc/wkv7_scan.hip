@@ -60,8 +60,7 @@ struct PrepSmem {
     static constexpr int R = A + F::bytes(C, D);       // Rhat rows
     static constexpr int Bm = R + F::bytes(C, D);      // Btil rows
     static constexpr int Km = Bm + F::bytes(C, D);     // Ktil rows
-    static constexpr int Tm = Km + F::bytes(C, D);     // T rows (t, s)
-    static constexpr int Lak = Tm + F::bytes(C, C);    // Lak rows (t, s)
+    static constexpr int Lak = Km + F::bytes(C, D);    // Lak rows (t, s)
     static constexpr int Mrb = Lak + F::bytes(C, C);   // Mrb rows (t, s)
     static constexpr int W1 = Mrb + F::bytes(C, C);    // W1 rows (t, j)
     static constexpr int Zm = W1 + F::bytes(C, D);     // Z rows (t, u)
@@ -107,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p, int i
 
     const M A = make_mat<SPLIT>(smem, L::A, C, D), R = make_mat<SPLIT>(smem, L::R, C, D);
     const M Bm = make_mat<SPLIT>(smem, L::Bm, C, D), Km = make_mat<SPLIT>(smem, L::Km, C, D);
-    const M Tm = make_mat<SPLIT>(smem, L::Tm, C, C), Lak = make_mat<SPLIT>(smem, L::Lak, C, C);
+    const M Lak = make_mat<SPLIT>(smem, L::Lak, C, C);
     const M Mrb = make_mat<SPLIT>(smem, L::Mrb, C, C), W1 = make_mat<SPLIT>(smem, L::W1, C, D);
     const M Zm = make_mat<SPLIT>(smem, L::Zm, C, C);
     float* glast = reinterpret_cast<float*>(smem + L::glast);
@@ -168,27 +167,26 @@ __global__ __launch_bounds__(256, 2) void chunk_prepare_kernel(PrepArgs p, int i
     }
     lds_barrier();
 
-    // ---- T to its operand rows and to memory: wave w rows 8w .. 8w + 7, four columns per lane
+    // ---- T to memory: wave w rows 8w .. 8w + 7, four columns per lane
     {
         const int t = 8 * wave + (lane >> 3), s4 = 4 * (lane & 7);
         const f32x4 v = *reinterpret_cast<const f32x4*>(tf + t * LDF + s4);
-        put4(Tm, t, s4, v);
         *reinterpret_cast<f32x4*>(p.inv + (int64_t)item * C * C + t * C + s4) = v;
     }
-    lds_barrier();
 
     // ---- W1 = T Ahat (rows t, columns j) and Z = T Lak (rows t, columns u).  Wave w: W1 tiles
     // (t blocks 0, 1; j block w) and Z tile w of (u block, t block) = (0, 0), (0, 1), (1, 1); wave 3
-    // the zero Z tile (t < 16 <= u).
+    // the zero Z tile (t < 16 <= u).  T's rows come from its fp32 copy, split in registers.
     {
         const Frag<SPLIT> aw = frag_t(A, 16 * wave, 0, lane);
+        const Frag<SPLIT> t0f = frag_n_f32<SPLIT>(tf, LDF, 0, 0, lane), t1f = frag_n_f32<SPLIT>(tf, LDF, 16, 0, lane);
         // element (j, t) = sum_s Ahat[s][j] T[t][s]
-        const f32x4 w0 = fmma(zero4(), aw, frag_n(Tm, 0, 0, lane));
-        const f32x4 w1 = fmma(zero4(), aw, frag_n(Tm, 16, 0, lane));
+        const f32x4 w0 = fmma(zero4(), aw, t0f);
+        const f32x4 w1 = fmma(zero4(), aw, t1f);
         if (wave < 3) {
             const int ub = wave == 2 ? 1 : 0, tb = wave == 0 ? 0 : 1;
             // element (u, t) = sum_s Lak[s][u] T[t][s]
-            const f32x4 z = fmma(zero4(), frag_t(Lak, 16 * ub, 0, lane), frag_n(Tm, 16 * tb, 0, lane));
+            const f32x4 z = fmma(zero4(), frag_t(Lak, 16 * ub, 0, lane), tb == 0 ? t0f : t1f);
             put4(Zm, 16 * tb + r16, 16 * ub + 4 * g4, z);
         } else {
             put4(Zm, r16, 16 + 4 * g4, zero4());
