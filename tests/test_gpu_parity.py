@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 F32, BF16 = torch.float32, torch.bfloat16
 
 # (B, T, H, dtype, with_h0, with_dhT): several chunks, ragged tails, one token,
-# head counts on every launch shape (row blocks of 16, 32 and 64 rows).
+# head counts on every scan launch shape (on 256 CUs: workgroups of 16 state
+# rows up to 64 heads, of 32 rows up to 128 heads, of 64 rows beyond).
 SMALL = [
     (1, 64, 1, F32, False, False),
     (2, 1, 3, F32, True, True),
