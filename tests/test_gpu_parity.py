@@ -29,6 +29,9 @@ SMALL = [
     (2, 95, 3, BF16, True, True),
     (3, 200, 5, BF16, True, True),
     (4, 130, 4, F32, True, False),
+    # the scan launch boundaries on 256 CUs: 64 heads (four workgroups per head) and 65 (two)
+    (4, 70, 16, BF16, True, True),
+    (5, 70, 13, F32, True, True),
     (8, 40, 16, BF16, True, True),
     (16, 40, 16, BF16, False, True),
     (1, 257, 8, F32, True, True),
